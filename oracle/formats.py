@@ -1,0 +1,33 @@
+"""Decoding of the storage formats the GDPA inputs arrive in, to fp64.
+
+Test infrastructure (see the package docstring).
+
+* bf16: the upper 16 bits of an IEEE-754 binary32 value.
+* FP8 E4M3: the OCP 8-bit floating point format ("OCP 8-bit Floating Point
+  Specification (OFP8)", E4M3 encoding): 1 sign bit, 4 exponent bits with bias
+  7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is
+  NaN; there are no infinities; the largest finite magnitude is 448.
+  The GDPA README ("Features": "FP8 (E4M3) forward") names the format; it does
+  not state the scaling.  Reading: one fp32 scale per tensor, so the value a
+  code stands for is decode(code) * scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_bf16(bits) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes, scale: float = 1.0) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
+    return sign * mag * float(scale)
