@@ -1,0 +1,212 @@
+"""Python binding of the MI355X GDPA library (libgdpa.so, C ABI in include/gdpa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C entry points.  PyTorch provides device memory and the
+current stream.  The functions keep the C names (gdpa_fwd, gdpa_varlen_fwd,
+gdpa_bwd, gdpa_varlen_bwd); outputs are caller-allocated tensors, as in C.
+Small helpers (`varlen_forward`, `varlen_backward`, ...) allocate the outputs
+with torch and call the same entry points.
+
+The library must have been built (`python generalized_attention_amd/build.py`);
+importing this module fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdpa.so")
+
+ACT = {
+    "identity": 0, "gelu": 1, "gelu_tanh": 2, "gelu_approx": 2, "fast_gelu": 3, "fast_gelu_bf16": 4,
+    "relu": 5, "relu2": 6, "relu_squared": 6, "leaky_relu": 7, "silu": 8, "fast_silu": 9,
+    "hardswish": 10,
+}
+MASK = {"none": 0, "causal": 1, "window": 2, "sliding_window": 2}
+DTYPE_BF16, DTYPE_FP16, DTYPE_FP8_E4M3, DTYPE_FP32 = 0, 1, 2, 3
+STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_UNSUPPORTED",
+          3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP"}
+
+EXPORTED = (
+    "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd",
+    "gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
+    "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size",
+    "gdpa_status_string", "gdpa_abi_version",
+)
+
+
+class GDPAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python generalized_attention_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.gdpa_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
+                             I32, I32, I32, F32, F32, P, SZ, P]
+    lib.gdpa_varlen_fwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32, I32,
+                                    I32, I32, F32, I32, I32, I32, F32, F32, P, SZ, P]
+    lib.gdpa_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
+                             I32, I32, P, SZ, P]
+    lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32,
+                                    I32, I32, I32, F32, I32, I32, P, SZ, P]
+    for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
+        getattr(lib, n).restype = ctypes.c_int
+    for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
+              "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
+        getattr(lib, n).argtypes = [I32] * 6
+        getattr(lib, n).restype = SZ
+    lib.gdpa_status_string.argtypes = [ctypes.c_int]
+    lib.gdpa_status_string.restype = ctypes.c_char_p
+    lib.gdpa_abi_version.restype = I32
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(st, where):
+    if st != 0:
+        raise GDPAError(st, where)
+
+
+def _act(a):
+    return ACT[a] if isinstance(a, str) else int(a)
+
+
+def _mask(m):
+    return MASK[m] if isinstance(m, str) else int(m)
+
+
+def _qk_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DTYPE_FP8_E4M3
+    if t.dtype == torch.float16:
+        return DTYPE_FP16
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _out_dtype(t):
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported output dtype {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ---------------------------------------------------------------- C-name calls
+def gdpa_fwd(q, k, v, o, scale, act="fast_gelu", act_param=0.01, mask="none", window_left=-1,
+             window_right=-1, q_descale=1.0, k_descale=1.0):
+    """Fixed-length forward: q/o [B, Lq, Hq, D], k/v [B, Lk, Hkv, D]; writes o."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    ws, nws = _workspace(_lib.gdpa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
+    st = _lib.gdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Lq, Lk, Hq, Hkv, D, float(scale), _mask(mask),
+                       window_left, window_right, _act(act), float(act_param), _qk_dtype(q), _qk_dtype(v),
+                       _out_dtype(o), float(q_descale), float(k_descale), _ptr(ws), nws, _stream(q.device))
+    _check(st, "gdpa_fwd")
+    return o
+
+
+def gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                    act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1,
+                    q_descale=1.0, k_descale=1.0):
+    """Jagged forward: q/o [total_q, Hq, D], k/v [total_k, Hkv, D], cu_seqlens int32 [B+1]."""
+    B = cu_seqlens_q.numel() - 1
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    ws, nws = _workspace(_lib.gdpa_varlen_fwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
+    st = _lib.gdpa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
+                              int(max_seqlen_q), int(max_seqlen_k), q.shape[0], k.shape[0], Hq, Hkv, D,
+                              float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
+                              _qk_dtype(q), _qk_dtype(v), _out_dtype(o), float(q_descale), float(k_descale),
+                              _ptr(ws), nws, _stream(q.device))
+    _check(st, "gdpa_varlen_fwd")
+    return o
+
+
+def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, mask="none",
+             window_left=-1, window_right=-1):
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
+    st = _lib.gdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, Lq, Lk, Hq, Hkv,
+                       D, float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
+                       _qk_dtype(q), _out_dtype(dq), _ptr(ws), nws, _stream(q.device))
+    _check(st, "gdpa_bwd")
+    return dq, dk, dv
+
+
+def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                    act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1):
+    B = cu_seqlens_q.numel() - 1
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    ws, nws = _workspace(_lib.gdpa_varlen_bwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
+    st = _lib.gdpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k),
+                              q.shape[0], k.shape[0], Hq, Hkv, D, float(scale), _mask(mask), window_left,
+                              window_right, _act(act), float(act_param), _qk_dtype(q), _out_dtype(dq), _ptr(ws),
+                              nws, _stream(q.device))
+    _check(st, "gdpa_varlen_bwd")
+    return dq, dk, dv
+
+
+# ------------------------------------------------------ allocating conveniences
+def varlen_forward(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                   activation="fast_gelu", out_dtype=torch.float32, **kw):
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    o = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=out_dtype, device=q.device)
+    return gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                           act=activation, **kw)
+
+
+def varlen_backward(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                    activation="fast_gelu", grad_dtype=torch.float32, **kw):
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    return gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                           scale, act=activation, **kw)
+
+
+def forward(q, k, v, scale=None, activation="fast_gelu", out_dtype=torch.float32, **kw):
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    o = torch.empty(q.shape[0], q.shape[1], q.shape[2], v.shape[3], dtype=out_dtype, device=q.device)
+    return gdpa_fwd(q, k, v, o, scale, act=activation, **kw)
+
+
+def backward(q, k, v, dout, scale=None, activation="fast_gelu", grad_dtype=torch.float32, **kw):
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    return gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act=activation, **kw)

@@ -1,0 +1,286 @@
+// Host side of the GDPA C ABI: argument validation, variant selection and
+// kernel launches on the caller's stream.  Every check runs before the first
+// HIP call, so invalid arguments are reported without touching a device.
+#include "../../include/gdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+#include <algorithm>
+
+#include "gdpa_kernels.hpp"
+
+namespace {
+
+using gdpa::BwdArgs;
+using gdpa::FwdArgs;
+
+constexpr int64_t kMaxGrid = 2147483647LL;
+
+bool debug_log() {
+  static const bool on = [] {
+    const char* e = std::getenv("GDPA_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+// Folds the enum aliases onto the kernel's activation kinds; -1 if invalid.
+int act_kind_of(int32_t act) {
+  switch (act) {
+    case GDPA_ACT_IDENTITY: return gdpa::ACT_IDENTITY;
+    case GDPA_ACT_GELU: return gdpa::ACT_GELU;
+    case GDPA_ACT_GELU_TANH:
+    case GDPA_ACT_FAST_GELU:
+    case GDPA_ACT_FAST_GELU_BF16: return gdpa::ACT_GELU_TANH;
+    case GDPA_ACT_RELU: return gdpa::ACT_RELU;
+    case GDPA_ACT_RELU2: return gdpa::ACT_RELU2;
+    case GDPA_ACT_LEAKY_RELU: return gdpa::ACT_LEAKY;
+    case GDPA_ACT_SILU:
+    case GDPA_ACT_FAST_SILU: return gdpa::ACT_SILU;
+    case GDPA_ACT_HARDSWISH: return gdpa::ACT_HARDSWISH;
+    default: return -1;
+  }
+}
+
+struct Common {
+  int32_t batch, max_lq, max_lk, hq, hkv, d;
+  int64_t total_q, total_k;
+  int act_kind;
+  int32_t wl, wr;
+};
+
+// Shape/enum checks shared by all four entry points.
+gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_t total_q,
+                           int64_t total_k, int32_t hq, int32_t hkv, int32_t d, float scale,
+                           int32_t mask, int32_t window_left, int32_t window_right, int32_t act,
+                           float act_param, Common* c) {
+  if (batch < 0 || max_lq < 0 || max_lk < 0 || total_q < 0 || total_k < 0) return GDPA_ERR_INVALID_ARG;
+  if (total_q > INT32_MAX || total_k > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return GDPA_ERR_INVALID_ARG;
+  if (d <= 0) return GDPA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return GDPA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !std::isfinite(act_param)) return GDPA_ERR_INVALID_ARG;
+  const int kind = act_kind_of(act);
+  if (kind < 0) return GDPA_ERR_INVALID_ARG;
+  int32_t wl = -1, wr = -1;
+  switch (mask) {
+    case GDPA_MASK_NONE: break;
+    case GDPA_MASK_CAUSAL: wr = 0; break;
+    case GDPA_MASK_SLIDING_WINDOW:
+      if (window_left < -1 || window_right < -1) return GDPA_ERR_INVALID_ARG;
+      wl = window_left;
+      wr = window_right;
+      break;
+    default: return GDPA_ERR_INVALID_ARG;
+  }
+  // Row offsets inside the kernels are 32-bit; tensor offsets are 64-bit.
+  if ((int64_t)total_q * hq * d > (int64_t)1 << 40 || (int64_t)total_k * hkv * d > (int64_t)1 << 40)
+    return GDPA_ERR_UNSUPPORTED;
+  *c = Common{batch, max_lq, max_lk, hq, hkv, d, total_q, total_k, kind, wl, wr};
+  return GDPA_OK;
+}
+
+// Upper bound on the number of products summed into one output row: `len`
+// rows of the other operand times `heads` query heads, with `len` capped by the
+// window width when both window sides are bounded.
+constexpr int64_t kFewTerms = 128;
+bool few_terms(int64_t len, int64_t heads, const Common& c) {
+  if (c.wl >= 0 && c.wr >= 0) len = std::min<int64_t>(len, (int64_t)c.wl + c.wr + 1);
+  return len * heads <= kFewTerms;
+}
+
+gdpa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GDPA_OK;
+  if (debug_log()) std::fprintf(stderr, "[gdpa] %s failed: %s\n", what, hipGetErrorString(e));
+  return GDPA_ERR_HIP;
+}
+
+gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_q,
+                      const int32_t* cu_k, const Common& c, float scale, float act_param,
+                      int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale,
+                      float k_descale, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (qk_dtype == GDPA_DTYPE_FP16 || v_dtype == GDPA_DTYPE_FP16 || out_dtype == GDPA_DTYPE_FP16)
+    return GDPA_ERR_UNSUPPORTED;
+  if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_INVALID_ARG;
+  if (v_dtype != GDPA_DTYPE_BF16) return v_dtype == GDPA_DTYPE_FP8_E4M3 ? GDPA_ERR_UNSUPPORTED : GDPA_ERR_INVALID_ARG;
+  if (out_dtype != GDPA_DTYPE_FP32 && out_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  const bool fp8 = qk_dtype == GDPA_DTYPE_FP8_E4M3;
+  if (fp8 && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
+  if (c.batch == 0 || c.total_q == 0) return GDPA_OK;
+  if (q == nullptr || o == nullptr) return GDPA_ERR_INVALID_ARG;
+  if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
+  const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kFwdBM - 1) / gdpa::kFwdBM;
+  if (mblocks == 0) return GDPA_OK;
+  if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
+
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.batch = c.batch;
+  a.lq_fixed = c.max_lq;
+  a.lk_fixed = c.max_lk;
+  a.hq = c.hq;
+  a.hkv = c.hkv;
+  a.group = c.hq / c.hkv;
+  a.mblocks = (int32_t)mblocks;
+  a.s_scale = fp8 ? scale * q_descale * k_descale : scale;
+  a.act_param = act_param;
+  a.wl = c.wl;
+  a.wr = c.wr;
+  a.out_f32 = out_dtype == GDPA_DTYPE_FP32;
+  // When an output row sums at most kFewTerms products, the bf16 rounding of P
+  // no longer averages out; P is then carried as hi + lo (such short rows are
+  // bandwidth-bound, so the second MFMA is free).
+  a.psplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
+  if (debug_log())
+    std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
+                 c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, (int)fp8, c.wl, c.wr,
+                 a.psplit, (long long)(c.batch * c.hq * mblocks));
+  return hip_status(gdpa::launch_fwd(a, c.d, c.act_kind, fp8, static_cast<hipStream_t>(stream)),
+                    "forward launch");
+}
+
+gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                      void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
+                      float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (in_dtype == GDPA_DTYPE_FP8_E4M3 || in_dtype == GDPA_DTYPE_FP16 || grad_dtype == GDPA_DTYPE_FP16)
+    return GDPA_ERR_UNSUPPORTED;
+  if (in_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  if (grad_dtype != GDPA_DTYPE_FP32 && grad_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  if (c.batch == 0 || (c.total_q == 0 && c.total_k == 0)) return GDPA_OK;
+  if (c.total_q > 0 && (q == nullptr || dout == nullptr || dq == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (c.total_k > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return GDPA_ERR_INVALID_ARG;
+  const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kBwdBM - 1) / gdpa::kBwdBM;
+  const int64_t nblocks = ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN;
+  if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid || (int64_t)c.batch * c.hkv * nblocks > kMaxGrid)
+    return GDPA_ERR_UNSUPPORTED;
+
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.batch = c.batch;
+  a.lq_fixed = c.max_lq;
+  a.lk_fixed = c.max_lk;
+  a.hq = c.hq;
+  a.hkv = c.hkv;
+  a.group = c.hq / c.hkv;
+  a.mblocks = (int32_t)mblocks;
+  a.nblocks = (int32_t)nblocks;
+  a.scale = scale;
+  a.act_param = act_param;
+  a.wl = c.wl;
+  a.wr = c.wr;
+  a.out_f32 = grad_dtype == GDPA_DTYPE_FP32;
+  a.dsplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
+  a.kvsplit = few_terms(c.max_lq, a.group, c) ? 1 : 0;
+  if (debug_log())
+    std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,
+                 c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr);
+  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t seqlen_q,
+                       int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float scale,
+                       int32_t mask, int32_t window_left, int32_t window_right, int32_t act, float act_param,
+                       int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale, float k_descale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Common c;
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return GDPA_ERR_INVALID_ARG;
+  gdpa_status_t st = check_common(batch, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, (int64_t)batch * seqlen_k,
+                                  num_heads_q, num_heads_kv, head_dim, scale, mask, window_left, window_right, act,
+                                  act_param, &c);
+  if (st != GDPA_OK) return st;
+  return run_fwd(q, k, v, o, nullptr, nullptr, c, scale, act_param, qk_dtype, v_dtype, out_dtype, q_descale,
+                 k_descale, workspace, workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int64_t total_q, int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv,
+                              int32_t head_dim, float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                              int32_t act, float act_param, int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
+                              float q_descale, float k_descale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Common c;
+  gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                  head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+  if (st != GDPA_OK) return st;
+  if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
+  return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, qk_dtype, v_dtype, out_dtype,
+                 q_descale, k_descale, workspace, workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                       int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_kv,
+                       int32_t head_dim, float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                       int32_t act, float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Common c;
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return GDPA_ERR_INVALID_ARG;
+  gdpa_status_t st = check_common(batch, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, (int64_t)batch * seqlen_k,
+                                  num_heads_q, num_heads_kv, head_dim, scale, mask, window_left, window_right, act,
+                                  act_param, &c);
+  if (st != GDPA_OK) return st;
+  return run_bwd(q, k, v, dout, dq, dk, dv, nullptr, nullptr, c, scale, act_param, in_dtype, grad_dtype, workspace,
+                 workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                              void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q, int64_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float scale, int32_t mask,
+                              int32_t window_left, int32_t window_right, int32_t act, float act_param,
+                              int32_t in_dtype, int32_t grad_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Common c;
+  gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                  head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+  if (st != GDPA_OK) return st;
+  if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
+  return run_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, in_dtype, grad_dtype,
+                 workspace, workspace_bytes, stream);
+}
+
+size_t gdpa_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdpa_varlen_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdpa_bwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdpa_varlen_bwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+const char* gdpa_status_string(gdpa_status_t s) {
+  switch (s) {
+    case GDPA_OK: return "GDPA_OK";
+    case GDPA_ERR_INVALID_ARG: return "GDPA_ERR_INVALID_ARG";
+    case GDPA_ERR_UNSUPPORTED: return "GDPA_ERR_UNSUPPORTED";
+    case GDPA_ERR_WORKSPACE_TOO_SMALL: return "GDPA_ERR_WORKSPACE_TOO_SMALL";
+    case GDPA_ERR_HIP: return "GDPA_ERR_HIP";
+    default: return "GDPA_ERR_UNKNOWN";
+  }
+}
+
+int32_t gdpa_abi_version(void) { return GDPA_ABI_VERSION; }
+
+}  // extern "C"

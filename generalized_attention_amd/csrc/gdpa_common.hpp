@@ -1,0 +1,310 @@
+// Device-side building blocks shared by the GDPA kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_{bf16,fp8}):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l holds column l%32, the same k range
+//   C (32 x 32): lane l holds column l%32, rows 4*(l/32) + 8*(r/4) + r%4 in
+//                accumulator register r (0..15)
+// A C tile therefore feeds the next product directly as a B operand that
+// contracts over the C tile's rows: with S^T = K Q^T (keys x queries) in
+// registers, O^T = V^T P^T takes P^T straight from the accumulators, provided
+// the key order of the V^T operand follows the accumulator's row order.  The
+// transposed LDS tiles below store their columns in exactly that order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdpa_kernels.hpp"
+
+namespace gdpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(const u32x2& a, const u32x2& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a),
+                                                    __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ----------------------------------------------------------------- activations
+// act(x) and act'(x) in fp32.  Exponentials use v_exp_f32 (2^x) and v_rcp_f32;
+// both are accurate to about 1 ulp, far below the bf16 rounding applied to P.
+// tanh-GELU uses 0.5 x (1 + tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSqrt2OverPi = 0.7978845608028654f;
+constexpr float kGeluC = 0.044715f;
+constexpr float kInvSqrt2 = 0.7071067811865476f;
+constexpr float kInvSqrt2Pi = 0.3989422804014327f;
+
+template <int ACT>
+struct Act;
+
+template <>
+struct Act<ACT_IDENTITY> {
+  static __device__ __forceinline__ float f(float x, float) { return x; }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) { df = 1.0f; return x; }
+};
+
+template <>
+struct Act<ACT_RELU> {
+  static __device__ __forceinline__ float f(float x, float) { return fmaxf(x, 0.0f); }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    df = x > 0.0f ? 1.0f : 0.0f;
+    return fmaxf(x, 0.0f);
+  }
+};
+
+template <>
+struct Act<ACT_RELU2> {
+  static __device__ __forceinline__ float f(float x, float) { float r = fmaxf(x, 0.0f); return r * r; }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    float r = fmaxf(x, 0.0f);
+    df = 2.0f * r;
+    return r * r;
+  }
+};
+
+template <>
+struct Act<ACT_LEAKY> {
+  static __device__ __forceinline__ float f(float x, float a) { return x >= 0.0f ? x : a * x; }
+  static __device__ __forceinline__ float f_df(float x, float a, float& df) {
+    df = x > 0.0f ? 1.0f : a;
+    return x >= 0.0f ? x : a * x;
+  }
+};
+
+template <>
+struct Act<ACT_SILU> {
+  static __device__ __forceinline__ float f(float x, float) {
+    return x * fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+  }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    float s = fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+    df = s * (1.0f + x * (1.0f - s));
+    return x * s;
+  }
+};
+
+template <>
+struct Act<ACT_GELU_TANH> {
+  // sigmoid(2u) = 1 / (1 + 2^(x * (c0 + c1 x^2)))
+  static constexpr float c0 = -2.0f * kSqrt2OverPi * kLog2e;
+  static constexpr float c1 = c0 * kGeluC;
+  static __device__ __forceinline__ float f(float x, float) {
+    float t = x * __builtin_fmaf(c1, x * x, c0);
+    return x * fast_rcp(1.0f + fast_exp2(t));
+  }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    float x2 = x * x;
+    float s = fast_rcp(1.0f + fast_exp2(x * __builtin_fmaf(c1, x2, c0)));
+    // d/dx x s(2u) = s + x s (1 - s) 2 u',  2u' = 2 sqrt(2/pi) (1 + 3 c x^2)
+    float du2 = 2.0f * kSqrt2OverPi * __builtin_fmaf(3.0f * kGeluC, x2, 1.0f);
+    df = __builtin_fmaf(x * s * (1.0f - s), du2, s);
+    return x * s;
+  }
+};
+
+template <>
+struct Act<ACT_GELU> {
+  static __device__ __forceinline__ float f(float x, float) { return 0.5f * x * (1.0f + erff(x * kInvSqrt2)); }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    float cdf = 0.5f * (1.0f + erff(x * kInvSqrt2));
+    df = __builtin_fmaf(x * kInvSqrt2Pi, fast_exp2(-0.5f * kLog2e * x * x), cdf);
+    return x * cdf;
+  }
+};
+
+template <>
+struct Act<ACT_HARDSWISH> {
+  static __device__ __forceinline__ float f(float x, float) {
+    return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+  }
+  static __device__ __forceinline__ float f_df(float x, float, float& df) {
+    df = x < -3.0f ? 0.0f : (x > 3.0f ? 1.0f : __builtin_fmaf(x, 1.0f / 3.0f, 0.5f));
+    return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+  }
+};
+
+// ------------------------------------------------------------- LDS tile layouts
+// Row tile: [rows][D] bf16 (row = key or query), 16-byte chunks XOR-swizzled by
+// (row & 7) so that 8 consecutive rows read at one chunk hit distinct banks.
+template <int D>
+__device__ __forceinline__ int row_tile_off(int row, int chunk) {  // in bf16 elements
+  return row * D + ((chunk ^ (row & 7)) << 3);
+}
+
+// FP8 row tile: [rows][D] bytes, 8-byte units swizzled for conflict-free
+// ds_read_b64 of 16 consecutive rows.
+template <int D>
+__device__ __forceinline__ int row_tile8_off(int row, int unit) {  // in bytes
+  constexpr int kShift = (D == 64) ? 1 : 0;
+  return row * D + ((unit ^ ((row >> kShift) & (D / 8 - 1))) << 3);
+}
+
+// Transposed tile: [D][NCOL] bf16, row = head-dim index d, columns = NCOL keys
+// (or queries) in "accumulator order": within every 32-column block, logical
+// 16-byte chunk 2*t + hf holds columns 16 t + 8 (p/4) + 4 hf + p%4, p = 0..7.
+// Chunks are XOR-swizzled within their 128-byte bank sweep: by
+// ((d ^ (d >> 3)) & 7) for rows of >= 64 columns, by (((d >> 1) ^ (d >> 3)) & 3)
+// for 32-column rows (two rows per sweep).  Reads of 8 consecutive rows at one
+// chunk are conflict-free; the transposing writes (rows 8c + e) are <= 4-way.
+__device__ __forceinline__ int tr_chunk_of(int col) {  // logical chunk of column col
+  int kk = col & 31;
+  return ((col >> 5) << 2) + ((kk >> 4) << 1) + ((kk >> 2) & 1);
+}
+__device__ __forceinline__ int tr_pos_of(int col) {  // element position inside the chunk
+  int kk = col & 31;
+  return (((kk >> 3) & 1) << 2) + (kk & 3);
+}
+template <int NCOL>
+__device__ __forceinline__ int tr_tile_off(int d, int chunk) {  // in bf16 elements
+  static_assert(NCOL == 32 || NCOL == 64 || NCOL == 128, "transposed tile width");
+  const int swz = (NCOL == 32) ? (((d >> 1) ^ (d >> 3)) & 3) : ((d ^ (d >> 3)) & 7);
+  return d * NCOL + ((chunk ^ swz) << 3);
+}
+
+// Stage a [NROW x D] bf16 tile from global memory (row stride `ld` elements,
+// rows at or beyond `nvalid` read as zero) into registers: thread t owns the
+// 16-byte chunks t, t+256, ...
+template <int NROW, int D>
+struct RowTileRegs {
+  static constexpr int CPR = D / 8;                    // chunks per row
+  static constexpr int PER_THREAD = NROW * CPR / 256;
+  u32x4 r[PER_THREAD];
+  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int c = tid + 256 * i;
+      int row = c / CPR, col = c % CPR;
+      if (row < nvalid)
+        r[i] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + col * 8);
+      else
+        r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int c = tid + 256 * i;
+      int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(row, col)) = r[i];
+    }
+  }
+};
+
+// Same for an FP8 tile ([NROW x D] bytes).
+template <int NROW, int D>
+struct RowTile8Regs {
+  static constexpr int CPR = D / 16;
+  static constexpr int PER_THREAD = NROW * CPR / 256;
+  u32x4 r[PER_THREAD];
+  __device__ __forceinline__ void load(const uint8_t* base, long ld, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int c = tid + 256 * i;
+      int row = c / CPR, col = c % CPR;
+      if (row < nvalid)
+        r[i] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + col * 16);
+      else
+        r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int c = tid + 256 * i;
+      int row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col)) = u32x2{r[i][0], r[i][1]};
+      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col + 1)) = u32x2{r[i][2], r[i][3]};
+    }
+  }
+};
+
+// Stage a [NROW x D] bf16 tile and store it transposed ([D][NROW], accumulator
+// column order).  Thread t owns 4 consecutive rows (4a..4a+3) of one 8-wide
+// column chunk cd; lanes with consecutive cd read one row contiguously.
+template <int NROW, int D>
+struct TrTileRegs {
+  static constexpr int CPR = D / 8;
+  static constexpr int GROUPS = (NROW / 4) * CPR;      // (4-row group, chunk) pairs
+  static constexpr int PER_THREAD = (GROUPS + 255) / 256;
+  u32x4 r[PER_THREAD][4];
+  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int g = tid + 256 * i;
+      int a = g / CPR, cd = g % CPR;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int row = 4 * a + rr;
+        if (g < GROUPS && row < nvalid)
+          r[i][rr] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + cd * 8);
+        else
+          r[i][rr] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  // The same registers written as a row tile (row_tile_off layout).
+  __device__ __forceinline__ void store_rows(__bf16* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int g = tid + 256 * i;
+      if (GROUPS % 256 != 0 && g >= GROUPS) continue;
+      int a = g / CPR, cd = g % CPR;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(4 * a + rr, cd)) = r[i][rr];
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      int g = tid + 256 * i;
+      if (GROUPS % 256 != 0 && g >= GROUPS) continue;
+      int a = g / CPR, cd = g % CPR;
+      int col = 4 * a;
+      int chunk = tr_chunk_of(col);
+      int pos = tr_pos_of(col);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int d = cd * 8 + e;
+        int w = e >> 1;
+        uint32_t x0 = r[i][0][w], x1 = r[i][1][w], x2 = r[i][2][w], x3 = r[i][3][w];
+        uint32_t lo, hi;
+        if (e & 1) {
+          lo = (x0 >> 16) | (x1 & 0xffff0000u);
+          hi = (x2 >> 16) | (x3 & 0xffff0000u);
+        } else {
+          lo = (x0 & 0xffffu) | (x1 << 16);
+          hi = (x2 & 0xffffu) | (x3 << 16);
+        }
+        *reinterpret_cast<u32x2*>(lds + tr_tile_off<NROW>(d, chunk) + pos) = u32x2{lo, hi};
+      }
+    }
+  }
+};
+
+}  // namespace gdpa

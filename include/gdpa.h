@@ -1,0 +1,184 @@
+/*
+ * gdpa.h - C ABI of the MI355X (gfx950) Generalized Dot Product Attention library.
+ *
+ * GDPA is dot-product attention whose softmax is replaced by a pointwise
+ * activation (GDPA README, page "gdpa/README.md", intro).  There is no row
+ * normaliser, so for every sequence b, query head h and its KV head
+ * g = h / (Hq / Hkv):
+ *
+ *     S = scale * Q_bh K_bg^T        P = M .* act(S)        O_bh = P V_bg
+ *
+ * and, given dO, the backward products
+ *
+ *     dP = dO V^T   dS = M .* act'(S) .* dP   dQ = scale dS K
+ *     dK = scale sum_{h in g} dS^T Q          dV = sum_{h in g} P^T dO.
+ *
+ * M is the attention mask (README "Features": causal, non-causal, sliding
+ * window); masked pairs contribute exactly zero.  Jagged batches follow the
+ * cu_seqlens/max_seqlen convention of the README's "CUTE-DSL" usage example
+ * (flash_attn_varlen_func).  Head configurations MHA/GQA/MQA and the
+ * activation list come from "Features"; FP8 (E4M3) is forward-only there.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains them; they must stay valid until the
+ *    work queued on `stream` completes.
+ *  - Layouts are row-major with the head dimension fastest:
+ *      fixed length:  q/o/dO [B, Lq, Hq, D],  k/v [B, Lk, Hkv, D]
+ *      jagged:        q/o/dO [total_q, Hq, D], k/v [total_k, Hkv, D]
+ *    cu_seqlens_{q,k}: device int32 [B+1], cu[0] = 0, non-decreasing,
+ *    cu[B] = total.  Zero-length sequences are allowed.
+ *  - Element types: inputs bf16 (or FP8 E4M3 codes for q/k in the forward,
+ *    with fp32 per-tensor descales); outputs fp32 or bf16.
+ *  - Outputs are overwritten, never accumulated into.  Query rows with no
+ *    allowed key get O = 0 and dQ = 0; keys no query attends get dK = dV = 0.
+ *    dK/dV are summed over the query heads of each KV group.
+ *  - All work is queued on `stream` (a hipStream_t; NULL = default stream) and
+ *    the call returns without synchronising.
+ *  - Errors are returned as gdpa_status_t, never thrown.  Argument checks run
+ *    on the host before any HIP call.  Invalid device data (e.g. a
+ *    non-monotone cu_seqlens or a length above max_seqlen) is undefined
+ *    behaviour.
+ *  - Results are bitwise deterministic for a given input and launch.
+ */
+#ifndef GDPA_H_
+#define GDPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDPA_ABI_VERSION 1
+
+typedef enum {
+  GDPA_OK = 0,
+  GDPA_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0, bad enum */
+  GDPA_ERR_UNSUPPORTED = 2,          /* valid but not implemented (head dim, dtype combination) */
+  GDPA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the *_workspace_size() query */
+  GDPA_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
+} gdpa_status_t;
+
+/* Activation replacing softmax (README "Features": custom activations).
+ * GELU_TANH, FAST_GELU and FAST_GELU_BF16 all compute the tanh approximation
+ * of GELU; SILU and FAST_SILU both compute x*sigmoid(x).  act_param is the
+ * LeakyReLU negative slope and is ignored otherwise. */
+typedef enum {
+  GDPA_ACT_IDENTITY = 0,
+  GDPA_ACT_GELU = 1,
+  GDPA_ACT_GELU_TANH = 2,
+  GDPA_ACT_FAST_GELU = 3,
+  GDPA_ACT_FAST_GELU_BF16 = 4,
+  GDPA_ACT_RELU = 5,
+  GDPA_ACT_RELU2 = 6,
+  GDPA_ACT_LEAKY_RELU = 7,
+  GDPA_ACT_SILU = 8,
+  GDPA_ACT_FAST_SILU = 9,
+  GDPA_ACT_HARDSWISH = 10
+} gdpa_act_t;
+
+/* Mask (README "Features": causal, non-causal, sliding window).  Causal masks
+ * align bottom-right: query i of a sequence with Lq queries and Lk keys may
+ * see key j iff j <= i + Lk - Lq.  SLIDING_WINDOW allows
+ * i' - window_left <= j <= i' + window_right with i' = i + Lk - Lq, where a
+ * negative window side is unbounded.  For NONE and CAUSAL the window
+ * arguments are ignored. */
+typedef enum {
+  GDPA_MASK_NONE = 0,
+  GDPA_MASK_CAUSAL = 1,
+  GDPA_MASK_SLIDING_WINDOW = 2
+} gdpa_mask_t;
+
+typedef enum {
+  GDPA_DTYPE_BF16 = 0,
+  GDPA_DTYPE_FP16 = 1,      /* reserved: not implemented (GDPA_ERR_UNSUPPORTED) */
+  GDPA_DTYPE_FP8_E4M3 = 2,  /* OCP E4M3 codes, forward q/k only */
+  GDPA_DTYPE_FP32 = 3       /* outputs only */
+} gdpa_dtype_t;
+
+/* ------------------------------------------------------------------ forward
+ * O = M .* act(scale * q_descale * k_descale * Q K^T) V per (sequence, head).
+ *   q, k, v, o     : device tensors in the layouts above.
+ *   head_dim       : 64 or 128.
+ *   scale          : multiplies Q K^T inside the activation (FA softmax_scale).
+ *   qk_dtype       : GDPA_DTYPE_BF16 or GDPA_DTYPE_FP8_E4M3 (q and k codes).
+ *   v_dtype        : GDPA_DTYPE_BF16.
+ *   out_dtype      : GDPA_DTYPE_FP32 or GDPA_DTYPE_BF16.
+ *   q_descale, k_descale : per-tensor fp32 factors of FP8 codes (ignored for bf16).
+ *   workspace      : device scratch of at least gdpa_*_workspace_size() bytes
+ *                    (may be NULL when that size is 0); contents are clobbered.
+ */
+gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o,
+                       int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                       int32_t act, float act_param,
+                       int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
+                       float q_descale, float k_descale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Jagged forward.  max_seqlen_q/k are host upper bounds of the per-sequence
+ * lengths (used to size the launch; no device->host copy is made);
+ * total_q/total_k are the packed token counts (cu[B]). */
+gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void* o,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int64_t total_q, int64_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                              int32_t act, float act_param,
+                              int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
+                              float q_descale, float k_descale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------- backward
+ * Gradients of L = sum(O .* dO) for the forward above (bf16 inputs only; the
+ * README lists FP8 as forward-only, so an FP8 in_dtype returns
+ * GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout; all three
+ * are written in grad_dtype (GDPA_DTYPE_FP32 or GDPA_DTYPE_BF16).  The dQ
+ * reduction over key blocks runs in a fixed order (deterministic). */
+gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout,
+                       void* dq, void* dk, void* dv,
+                       int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                       int32_t act, float act_param,
+                       int32_t in_dtype, int32_t grad_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const void* dout,
+                              void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int64_t total_q, int64_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                              int32_t act, float act_param,
+                              int32_t in_dtype, int32_t grad_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace each call needs, in bytes (0 = none; pass NULL then).  Arguments
+ * mirror the shape arguments of the matching entry point. */
+size_t gdpa_fwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* gdpa_status_string(gdpa_status_t status);
+
+/* Returns GDPA_ABI_VERSION of the loaded library. */
+int32_t gdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDPA_H_ */

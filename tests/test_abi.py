@@ -1,0 +1,165 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+include/gdpa.h declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdpa.h")
+LIB = os.path.join(ROOT, "generalized_attention_amd", "libgdpa.so")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        subprocess.run([sys.executable, os.path.join(ROOT, "generalized_attention_amd", "build.py")], check=True)
+    import generalized_attention_amd as g
+    return g.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdpa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (gdpa_\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define GDPA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.gdpa_abi_version() == ver
+    for code, name in [(0, b"GDPA_OK"), (1, b"GDPA_ERR_INVALID_ARG"), (2, b"GDPA_ERR_UNSUPPORTED"),
+                       (3, b"GDPA_ERR_WORKSPACE_TOO_SMALL"), (4, b"GDPA_ERR_HIP"), (99, b"GDPA_ERR_UNKNOWN")]:
+        assert lib.gdpa_status_string(code) == name
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def fwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128, scale=0.1, mask=0,
+             wl=-1, wr=-1, act=3, ap=0.01, qk=0, vd=0, od=3, qd=1.0, kd=1.0, ws=None, nws=0, stream=None)
+    a.update(over)
+    return lib.gdpa_fwd(*a.values())
+
+
+def varlen_fwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, cq=FAKE, ck=FAKE, B=2, mq=128, mk=128, tq=200, tk=200, Hq=4, Hkv=4,
+             D=64, scale=0.1, mask=0, wl=-1, wr=-1, act=3, ap=0.01, qk=0, vd=0, od=3, qd=1.0, kd=1.0, ws=None,
+             nws=0, stream=None)
+    a.update(over)
+    return lib.gdpa_varlen_fwd(*a.values())
+
+
+def bwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128,
+             scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3, ws=None, nws=0, stream=None)
+    a.update(over)
+    return lib.gdpa_bwd(*a.values())
+
+
+def varlen_bwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cq=FAKE, ck=FAKE, B=2, mq=128, mk=128,
+             tq=200, tk=200, Hq=4, Hkv=2, D=128, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3,
+             ws=None, nws=0, stream=None)
+    a.update(over)
+    return lib.gdpa_varlen_bwd(*a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(Hq=3, Hkv=2), INVALID),            # Hq % Hkv != 0
+    (dict(Hkv=0), INVALID),
+    (dict(D=96), UNSUPPORTED),               # listed by the README, not built here
+    (dict(D=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(Lq=-5), INVALID),
+    (dict(act=11), INVALID),
+    (dict(act=-1), INVALID),
+    (dict(mask=3), INVALID),
+    (dict(mask=2, wl=-2), INVALID),
+    (dict(qk=1), UNSUPPORTED),               # fp16 reserved
+    (dict(vd=2), UNSUPPORTED),               # fp8 V
+    (dict(od=2), INVALID),                   # fp8 output
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(qk=2, qd=float("inf")), INVALID),
+    (dict(B=0), OK),                         # empty problem: no launch
+    (dict(Lq=0), OK),
+])
+def test_fwd_validation(lib, over, expect):
+    assert fwd(lib, **over) == expect
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(cq=None), INVALID),
+    (dict(tq=-1), INVALID),
+    (dict(tq=2 ** 31), UNSUPPORTED),
+    (dict(B=0), OK),
+    (dict(tq=0), OK),
+    (dict(D=256), UNSUPPORTED),
+])
+def test_varlen_fwd_validation(lib, over, expect):
+    assert varlen_fwd(lib, **over) == expect
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(ind=2), UNSUPPORTED),              # FP8 is forward-only (README "Features")
+    (dict(ind=1), UNSUPPORTED),
+    (dict(gd=2), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(dk=None), INVALID),
+    (dict(Hq=5), INVALID),
+    (dict(B=0), OK),
+])
+def test_bwd_validation(lib, over, expect):
+    assert bwd(lib, **over) == expect
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(ck=None), INVALID),
+    (dict(dv=None), INVALID),
+    (dict(tq=0, tk=0), OK),
+    (dict(act=42), INVALID),
+])
+def test_varlen_bwd_validation(lib, over, expect):
+    assert varlen_bwd(lib, **over) == expect
+
+
+def test_workspace_queries(lib):
+    for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
+              "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
+        assert getattr(lib, n)(64, 1024, 1024, 4, 4, 128) >= 0
+
+
+def test_python_binding_names_match_c_names():
+    import generalized_attention_amd as g
+    for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
+        assert callable(getattr(g, n))
+    assert set(g.EXPORTED) == set(declared_functions())
+
+
+def test_binding_modules_do_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "generalized_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.sub(r"(#|//).*", "", text), f

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Inputs are seeded (gdpa_inputs); the oracle consumes exactly the values the
+kernels consume (decoded bf16, E4M3 code x scale).  Bar: max|err| <= tol *
+rms(ref) with tol = 2e-2 (bf16 forward), 3e-2 (dQ/dK/dV), 6e-2 (FP8 forward).
+Outputs are NaN-poisoned before each call, so an unwritten element fails.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import gdpa_inputs as gi
+import oracle
+from helpers import (TOL_BWD, TOL_FWD_BF16, TOL_FWD_FP8, device_batch, err_ratio, mask_kw, oracle_inputs,
+                     run_backward, run_forward)
+
+pytestmark = pytest.mark.gpu
+
+ALL_ACTS = gi.ACTIVATIONS
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import generalized_attention_amd
+    return generalized_attention_amd
+
+
+def _wl(**kw):
+    base = dict(name="t", batch=4, heads_q=4, heads_kv=2, head_dim=128, lq_range=(1, 300), lk_range=None,
+                act="silu", backward=True, seed=11)
+    base.update(kw)
+    return gi.Workload(**base)
+
+
+def check_forward(g, bt, tol=None):
+    wl = bt.wl
+    tol = tol or (TOL_FWD_FP8 if wl.fp8_qk else TOL_FWD_BF16)
+    o = run_forward(g, bt).cpu().double().numpy()
+    q, k, v, _ = oracle_inputs(bt)
+    ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **mask_kw(wl))
+    r = err_ratio(o, ref)
+    assert r <= tol, f"{wl} forward err/rms {r:.4g} > {tol}"
+    return r
+
+
+def check_backward(g, bt, tol=TOL_BWD):
+    wl = bt.wl
+    dq, dk, dv = [t.cpu().double().numpy() for t in run_backward(g, bt)]
+    q, k, v, do = oracle_inputs(bt)
+    rq, rk, rv = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act,
+                                      **mask_kw(wl))
+    errs = dict(dq=err_ratio(dq, rq), dk=err_ratio(dk, rk), dv=err_ratio(dv, rv))
+    assert max(errs.values()) <= tol, f"{wl} backward {errs}"
+    return errs
+
+
+# ------------------------------------------------------------- reference workload 1
+def test_tiny_fixed_length_forward(g):
+    bt = gi.make_batch(gi.WORKLOADS["tiny"])
+    check_forward(g, bt)
+
+
+# ------------------------------------------------------------ activation x head dim
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ALL_ACTS)
+def test_forward_every_activation(g, act, D):
+    # jagged lengths incl. 0, 1 and ragged tails across several 128-row / KV tiles; GQA 4:2
+    bt = gi.make_batch(_wl(act=act, head_dim=D, act_param=0.05), seqlens_q=[37, 0, 300, 1, 129],
+                       seqlens_k=[37, 0, 300, 1, 129])
+    check_forward(g, bt)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ALL_ACTS)
+def test_backward_every_activation(g, act, D):
+    bt = gi.make_batch(_wl(act=act, head_dim=D, act_param=0.05), seqlens_q=[37, 0, 300, 1, 129],
+                       seqlens_k=[37, 0, 300, 1, 129])
+    check_backward(g, bt)
+
+
+# ---------------------------------------------------------------------- masks
+MASK_CASES = [
+    ("causal", -1, -1, [200, 77, 256], [200, 77, 256]),
+    ("causal", -1, -1, [50, 130, 1], [300, 140, 64]),      # Lq < Lk: bottom-right alignment
+    ("causal", -1, -1, [300, 20], [100, 3]),               # Lq > Lk: leading rows fully masked
+    ("window", 63, 0, [400, 129], [400, 129]),
+    ("window", 17, 5, [333, 64], [333, 80]),
+    ("window", 0, 0, [150], [150]),
+    ("window", -1, 40, [260], [260]),
+    ("window", 100, -1, [260], [300]),
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(MASK_CASES)))
+def test_masks_forward_backward(g, case, D):
+    mask, wl_, wr_, lq, lk = MASK_CASES[case]
+    wl = _wl(act="gelu_tanh", head_dim=D, mask=mask, window_left=wl_, window_right=wr_, batch=len(lq))
+    bt = gi.make_batch(wl, seqlens_q=lq, seqlens_k=lk)
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (6, 3), (2, 2)])
+def test_head_configs(g, hq, hkv):
+    # MQA (Hkv = 1), GQA 2:1, MHA
+    bt = gi.make_batch(_wl(heads_q=hq, heads_kv=hkv, act="relu2"), seqlens_q=[90, 257], seqlens_k=[90, 257])
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
+def test_cross_attention_short_kv(g):
+    wl = dataclasses.replace(gi.WORKLOADS["short_kv_cross"], batch=6)
+    bt = gi.make_batch(wl)
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_forward(g, D):
+    wl = _wl(head_dim=D, fp8_qk=True, act="leaky_relu", mask="window", window_left=127, window_right=0,
+             heads_q=8, heads_kv=2, backward=False)
+    bt = gi.make_batch(wl, seqlens_q=[300, 45, 513], seqlens_k=[300, 45, 513])
+    check_forward(g, bt)
+
+
+def test_empty_kv_gives_zero_output(g):
+    import torch
+    bt = gi.make_batch(_wl(act="identity"), seqlens_q=[5, 70], seqlens_k=[0, 0])
+    o = run_forward(g, bt).cpu()
+    assert torch.all(o == 0)
+    dq, dk, dv = run_backward(g, bt)
+    assert torch.all(dq.cpu() == 0) and dk.numel() == 0
+
+
+def test_bf16_outputs(g):
+    import torch
+    bt = gi.make_batch(_wl(act="silu"), seqlens_q=[300, 65], seqlens_k=[300, 65])
+    o = run_forward(g, bt, out_dtype=torch.bfloat16).float().cpu().double().numpy()
+    q, k, v, do = oracle_inputs(bt)
+    wl = bt.wl
+    ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act)
+    assert err_ratio(o, ref) <= TOL_FWD_BF16
+    grads = [t.float().cpu().double().numpy() for t in run_backward(g, bt, grad_dtype=torch.bfloat16)]
+    refs = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act)
+    for a, b in zip(grads, refs):
+        assert err_ratio(a, b) <= TOL_BWD
+
+
+def test_deterministic(g):
+    import torch
+    bt = gi.make_batch(_wl(act="fast_gelu", mask="causal"), seqlens_q=[300, 129, 5], seqlens_k=[300, 129, 5])
+    dev = device_batch(bt)
+    o1 = run_forward(g, bt, dev)
+    o2 = run_forward(g, bt, dev)
+    assert torch.equal(o1, o2)
+    g1 = run_backward(g, bt, dev)
+    g2 = run_backward(g, bt, dev)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_fixed_length_equals_varlen(g):
+    import torch
+    wl = _wl(act="hardswish", varlen=False, lq_range=(200, 200), batch=3)
+    bt = gi.make_batch(wl)
+    o_fixed = run_forward(g, bt)
+    bt_var = dataclasses.replace(bt, wl=dataclasses.replace(wl, varlen=True))
+    o_var = run_forward(g, bt_var)
+    assert torch.equal(o_fixed, o_var)
+    for a, b in zip(run_backward(g, bt), run_backward(g, bt_var)):
+        assert torch.equal(a, b)
