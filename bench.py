@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""GDPA throughput on one MI355X: forward + backward TFLOP/s on the jagged
+self-attention workload (64 sequences, lengths uniform in [1, 1024], 4 heads,
+head dim 128, FastGELU (tanh GELU), bf16 inputs, fp32 outputs).
+
+One step = the whole hot path over one batch: gdpa_varlen_fwd (O) followed by
+gdpa_varlen_bwd (dQ, dK, dV), all launched through the C ABI on one stream,
+with every input already resident in HBM.  Prints ONE JSON line.
+
+Flops are algorithmic: only allowed (query, key) pairs count, 4*D per pair and
+query head for the forward (Q K^T and P V) and 10*D for the backward (the five
+products S, dP, dV, dK, dQ); activation math is not counted.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --calibrate-copy 1024     # plain 1 GiB device copy, for PMC scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdpa_inputs as gi  # noqa: E402
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def allowed_pairs(lq, lk, wl, wr):
+    """Number of allowed (query, key) pairs of one sequence (bottom-right aligned window)."""
+    lq, lk = int(lq), int(lk)
+    if lq == 0 or lk == 0:
+        return 0
+    i = np.arange(lq, dtype=np.int64) + (lk - lq)
+    lo = np.zeros(lq, np.int64) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full(lq, lk - 1, np.int64) if wr < 0 else np.minimum(lk - 1, i + wr)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def workload_pairs(bt: gi.Batch):
+    wl = bt.wl
+    left, right = {"none": (-1, -1), "causal": (-1, 0), "window": (wl.window_left, wl.window_right)}[wl.mask]
+    per_seq = [allowed_pairs(a, b, left, right) for a, b in zip(bt.seqlens_q, bt.seqlens_k)]
+    return np.array(per_seq, np.int64) * wl.heads_q
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "generalized_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(bt: gi.Batch, budget_s: float):
+    """Time the fp64 oracle (forward + backward) on leading sequences of the same
+    batch until about `budget_s` seconds of CPU work; report TFLOP/s on the
+    algorithmic flops of the sequences processed."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    wl = bt.wl
+    pairs = workload_pairs(bt)
+    q, k, v, do = (oracle.decode_bf16(bt.q), oracle.decode_bf16(bt.k), oracle.decode_bf16(bt.v),
+                   oracle.decode_bf16(bt.do))
+    cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
+    t_total, flops, nseq = 0.0, 0, 0
+    for b in range(wl.batch):
+        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        lcq, lck = [0, cq[b + 1] - cq[b]], [0, ck[b + 1] - ck[b]]
+        kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
+        t0 = time.perf_counter()
+        oracle.gdpa_forward(q[sq], k[sk], v[sk], lcq, lck, wl.scale, wl.act, **kw)
+        oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck, wl.scale, wl.act, **kw)
+        t_total += time.perf_counter() - t0
+        flops += 14 * wl.head_dim * int(pairs[b])
+        nseq += 1
+        if t_total >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, forward+backward of the first {nseq} of {wl.batch} sequences "
+                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {t_total:.1f} s"}
+
+
+def calibrate_copy(mib: int, reps: int):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"calibrate_copy_bytes_read": n, "bytes_written": n, "reps": reps, "ms": ms,
+                      "GBps_read_plus_write": 2 * n / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="jagged_self", choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for per-kernel timing")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "GDPA work units are independent per (sequence, head), so more GPUs would each run this "
+              "kernel on their own share with no collective.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 20)
+        return
+
+    import generalized_attention_amd as g
+
+    wl = gi.WORKLOADS[args.workload]
+    if not wl.backward:
+        wl = gi.dataclasses.replace(wl, backward=True)
+    print(f"[bench] drawing {wl.name} (seed {wl.seed})", file=sys.stderr, flush=True)
+    bt = gi.make_batch(wl)
+    pairs = workload_pairs(bt)
+    P = int(pairs.sum())
+    D = wl.head_dim
+    fwd_flops, bwd_flops = 4 * D * P, 10 * D * P
+
+    def dev(a, kind):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        t = t.view(torch.int16).view(torch.bfloat16) if kind == "bf16" else t.view(torch.float8_e4m3fn)
+        return t.cuda()
+
+    qk = "fp8" if wl.fp8_qk else "bf16"
+    q, k, v, do = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, "bf16"), dev(bt.do, "bf16")
+    cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
+    o = torch.empty(q.shape[0], wl.heads_q, D, dtype=torch.float32, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    mq, mk = bt.max_seqlen_q, bt.max_seqlen_k
+    kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
+              window_right=wl.window_right)
+
+    def fwd():
+        g.gdpa_varlen_fwd(q, k, v, o, cu_q, cu_k, mq, mk, wl.scale, q_descale=bt.q_scale, k_descale=bt.k_scale,
+                          **kw)
+
+    def bwd(want_dq=True, want_dkv=True):
+        g.gdpa_varlen_bwd(q, k, v, do, dq if want_dq else None, dk if want_dkv else None,
+                          dv if want_dkv else None, cu_q, cu_k, mq, mk, wl.scale, **kw)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel average launch durations (HIP events on the stream the kernels run on)
+    def avg_ms(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    kern = {
+        "gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 4 * D * P),
+        "gdpa_bwd_dkdv_kernel": (avg_ms(lambda: bwd(False, True), args.kernel_reps), 8 * D * P),
+        "gdpa_bwd_dq_kernel": (avg_ms(lambda: bwd(True, False), args.kernel_reps), 2 * D * P),
+    }
+    dom = max(kern, key=lambda n: kern[n][0])
+    dom_ms, dom_flops = kern[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        ent = rec.get("kernels", {}).get(dom)
+        if ent and rec.get("source_hash") == kernel_source_hash() and rec.get("workload") == wl.name:
+            traffic = ent["hbm_bytes_per_launch"]
+
+    total_flops = fwd_flops + bwd_flops
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": "GDPA fwd/bwd TFLOP/s and % of bf16 MFMA peak on one MI355X (jagged)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f8" if wl.fp8_qk else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.batch} sequences, lengths U[{wl.lq_range[0]},{wl.lq_range[1]}] "
+                               f"(drawn total {int(bt.seqlens_q.sum())} tokens), Hq={wl.heads_q}, "
+                               f"Hkv={wl.heads_kv}, D={D}, act={wl.act}, mask={wl.mask}, fwd+bwd, fp32 outputs",
+                   "global_batch": wl.batch, "seq_len": int(bt.max_seqlen_q), "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (kern["gdpa_fwd_kernel"][0] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / ((kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]) * 1e-3)
+                            / 1e12, 2),
+        "kernel_ms": {n: round(t, 4) for n, (t, _) in kern.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(bt, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,8 +76,13 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bf16 (round to nearest even) and return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 encoding expects finite values")
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1          # finite patterns are <= 0xff7fffff, so the sum below cannot wrap
+    r += u
+    r += 0x7FFF
+    r >>= 16
     return r.astype(np.uint16)
 
 

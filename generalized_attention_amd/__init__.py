@@ -115,6 +115,13 @@ def _out_dtype(t):
     raise TypeError(f"unsupported output dtype {t.dtype}")
 
 
+def _grad_dtype(dq, dk, dv):
+    for t in (dq, dk, dv):
+        if t is not None:
+            return _out_dtype(t)
+    return DTYPE_FP32
+
+
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None, 0
@@ -154,18 +161,20 @@ def gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_se
 
 def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, mask="none",
              window_left=-1, window_right=-1):
+    """Fixed-length backward; writes dq (may be None) and dk/dv (both may be None)."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
     st = _lib.gdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, Lq, Lk, Hq, Hkv,
                        D, float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
-                       _qk_dtype(q), _out_dtype(dq), _ptr(ws), nws, _stream(q.device))
+                       _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws), nws, _stream(q.device))
     _check(st, "gdpa_bwd")
     return dq, dk, dv
 
 
 def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
                     act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1):
+    """Jagged backward; writes dq (may be None) and dk/dv (both may be None)."""
     B = cu_seqlens_q.numel() - 1
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
@@ -173,7 +182,7 @@ def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_s
     st = _lib.gdpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k),
                               q.shape[0], k.shape[0], Hq, Hkv, D, float(scale), _mask(mask), window_left,
-                              window_right, _act(act), float(act_param), _qk_dtype(q), _out_dtype(dq), _ptr(ws),
+                              window_right, _act(act), float(act_param), _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws),
                               nws, _stream(q.device))
     _check(st, "gdpa_varlen_bwd")
     return dq, dk, dv

@@ -160,9 +160,13 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
     return GDPA_ERR_UNSUPPORTED;
   if (in_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
   if (grad_dtype != GDPA_DTYPE_FP32 && grad_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  // dq == NULL skips dQ; dk == dv == NULL skips dK and dV; at least one is wanted.
+  const bool want_dq = dq != nullptr;
+  const bool want_dkv = dk != nullptr;
+  if ((dk == nullptr) != (dv == nullptr) || (!want_dq && !want_dkv)) return GDPA_ERR_INVALID_ARG;
   if (c.batch == 0 || (c.total_q == 0 && c.total_k == 0)) return GDPA_OK;
-  if (c.total_q > 0 && (q == nullptr || dout == nullptr || dq == nullptr)) return GDPA_ERR_INVALID_ARG;
-  if (c.total_k > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (c.total_q > 0 && (q == nullptr || dout == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kBwdBM - 1) / gdpa::kBwdBM;
   const int64_t nblocks = ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN;
   if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid || (int64_t)c.batch * c.hkv * nblocks > kMaxGrid)
@@ -196,7 +200,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   if (debug_log())
     std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,
                  c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr);
-  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, static_cast<hipStream_t>(stream)), "backward launch");
+  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, want_dq, want_dkv, static_cast<hipStream_t>(stream)),
+                    "backward launch");
 }
 
 }  // namespace

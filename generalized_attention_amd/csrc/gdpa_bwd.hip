@@ -87,12 +87,13 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
   const long kv_ld = (long)a.hkv * D;
   u32x4 kreg[KS], vreg[KS];
   {
-    const __bf16* kp = static_cast<const __bf16*>(a.k) + (long)(ks + kj) * kv_ld + g * D + hf * 8;
-    const __bf16* vp = static_cast<const __bf16*>(a.v) + (long)(ks + kj) * kv_ld + g * D + hf * 8;
+    const long krow = (long)(ks + min(kj, lk - 1)) * kv_ld + g * D + hf * 8;
+    const __bf16* kp = static_cast<const __bf16*>(a.k) + krow;
+    const __bf16* vp = static_cast<const __bf16*>(a.v) + krow;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kreg[s] = (kj < lk) ? *reinterpret_cast<const u32x4*>(kp + s * 16) : u32x4{0u, 0u, 0u, 0u};
-      vreg[s] = (kj < lk) ? *reinterpret_cast<const u32x4*>(vp + s * 16) : u32x4{0u, 0u, 0u, 0u};
+      kreg[s] = load16_or_zero(kp + s * 16, kj < lk);
+      vreg[s] = load16_or_zero(vp + s * 16, kj < lk);
     }
   }
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -271,12 +272,13 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   const long q_ld = (long)a.hq * D;
   u32x4 qreg[KS], doreg[KS];
   {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + (long)(qs + qi) * q_ld + h * D + hf * 8;
-    const __bf16* dp = static_cast<const __bf16*>(a.dout) + (long)(qs + qi) * q_ld + h * D + hf * 8;
+    const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
+    const __bf16* dp = static_cast<const __bf16*>(a.dout) + qrow;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qreg[s] = (qi < lq) ? *reinterpret_cast<const u32x4*>(qp + s * 16) : u32x4{0u, 0u, 0u, 0u};
-      doreg[s] = (qi < lq) ? *reinterpret_cast<const u32x4*>(dp + s * 16) : u32x4{0u, 0u, 0u, 0u};
+      qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
+      doreg[s] = load16_or_zero(dp + s * 16, qi < lq);
     }
   }
   f32x16 dqacc[NDB];
@@ -402,9 +404,9 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dq_kernel(const BwdArgs a) {
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, hipStream_t stream) {
-  const long grid_kv = (long)a.batch * a.hkv * a.nblocks;
-  const long grid_q = (long)a.batch * a.hq * a.mblocks;
+static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
+  const long grid_kv = want_dkv ? (long)a.batch * a.hkv * a.nblocks : 0;
+  const long grid_q = want_dq ? (long)a.batch * a.hq * a.mblocks : 0;
   dim3 blk(256);
   switch (act_kind) {
 #define GDPA_BWD_CASE(K)                                                                             \
@@ -427,9 +429,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, hipStream_t strea
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, hipStream_t stream) {
-  if (head_dim == 64) return launch_bwd_d<64>(a, act_kind, stream);
-  if (head_dim == 128) return launch_bwd_d<128>(a, act_kind, stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
+                      hipStream_t stream) {
+  if (head_dim == 64) return launch_bwd_d<64>(a, act_kind, want_dq, want_dkv, stream);
+  if (head_dim == 128) return launch_bwd_d<128>(a, act_kind, want_dq, want_dkv, stream);
   return hipErrorInvalidValue;
 }
 

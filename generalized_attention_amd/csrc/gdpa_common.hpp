@@ -186,23 +186,38 @@ __device__ __forceinline__ int tr_tile_off(int d, int chunk) {  // in bf16 eleme
   return d * NCOL + ((chunk ^ swz) << 3);
 }
 
+// Loads below are branch-free: an out-of-range row is redirected to row
+// nvalid-1 (callers guarantee nvalid >= 1) and its value replaced by zero with
+// a select.  Keeping every load unconditional lets the compiler count
+// outstanding loads exactly, so the prefetch of the next tile is not drained
+// (s_waitcnt vmcnt(0)) before the current tile's MFMAs.  The tile stagers
+// apply the select only when they write LDS, after the current tile's math,
+// so no instruction consumes the prefetched registers early.
+__device__ __forceinline__ u32x4 load16_or_zero(const void* p, bool valid) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return valid ? v : u32x4{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ u32x2 load8_or_zero(const void* p, bool valid) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  return valid ? v : u32x2{0u, 0u};
+}
+
 // Stage a [NROW x D] bf16 tile from global memory (row stride `ld` elements,
-// rows at or beyond `nvalid` read as zero) into registers: thread t owns the
-// 16-byte chunks t, t+256, ...
+// rows at or beyond `nvalid` >= 1 read as zero) into registers: thread t owns
+// the 16-byte chunks t, t+256, ...
 template <int NROW, int D>
 struct RowTileRegs {
   static constexpr int CPR = D / 8;                    // chunks per row
   static constexpr int PER_THREAD = NROW * CPR / 256;
   u32x4 r[PER_THREAD];
-  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid, int tid) {
+  int nvalid;
+  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid_, int tid) {
+    nvalid = nvalid_;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       int c = tid + 256 * i;
       int row = c / CPR, col = c % CPR;
-      if (row < nvalid)
-        r[i] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + col * 8);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
+      r[i] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + col * 8);
     }
   }
   __device__ __forceinline__ void store(__bf16* lds, int tid) const {
@@ -210,7 +225,7 @@ struct RowTileRegs {
     for (int i = 0; i < PER_THREAD; ++i) {
       int c = tid + 256 * i;
       int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(row, col)) = r[i];
+      *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(row, col)) = row < nvalid ? r[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
 };
@@ -221,15 +236,14 @@ struct RowTile8Regs {
   static constexpr int CPR = D / 16;
   static constexpr int PER_THREAD = NROW * CPR / 256;
   u32x4 r[PER_THREAD];
-  __device__ __forceinline__ void load(const uint8_t* base, long ld, int nvalid, int tid) {
+  int nvalid;
+  __device__ __forceinline__ void load(const uint8_t* base, long ld, int nvalid_, int tid) {
+    nvalid = nvalid_;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       int c = tid + 256 * i;
       int row = c / CPR, col = c % CPR;
-      if (row < nvalid)
-        r[i] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + col * 16);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
+      r[i] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + col * 16);
     }
   }
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
@@ -237,8 +251,9 @@ struct RowTile8Regs {
     for (int i = 0; i < PER_THREAD; ++i) {
       int c = tid + 256 * i;
       int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col)) = u32x2{r[i][0], r[i][1]};
-      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col + 1)) = u32x2{r[i][2], r[i][3]};
+      const u32x4 v = row < nvalid ? r[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col)) = u32x2{v[0], v[1]};
+      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col + 1)) = u32x2{v[2], v[3]};
     }
   }
 };
@@ -252,7 +267,9 @@ struct TrTileRegs {
   static constexpr int GROUPS = (NROW / 4) * CPR;      // (4-row group, chunk) pairs
   static constexpr int PER_THREAD = (GROUPS + 255) / 256;
   u32x4 r[PER_THREAD][4];
-  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid, int tid) {
+  int nvalid;
+  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid_, int tid) {
+    nvalid = nvalid_;
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       int g = tid + 256 * i;
@@ -260,12 +277,14 @@ struct TrTileRegs {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         int row = 4 * a + rr;
-        if (g < GROUPS && row < nvalid)
-          r[i][rr] = *reinterpret_cast<const u32x4*>(base + (long)row * ld + cd * 8);
-        else
-          r[i][rr] = u32x4{0u, 0u, 0u, 0u};
+        r[i][rr] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + cd * 8);
       }
     }
+  }
+  // zero the rows at or beyond nvalid (applied when writing LDS)
+  __device__ __forceinline__ u32x4 val(int i, int rr, int tid) const {
+    const int row = 4 * ((tid + 256 * i) / CPR) + rr;
+    return row < nvalid ? r[i][rr] : u32x4{0u, 0u, 0u, 0u};
   }
   // The same registers written as a row tile (row_tile_off layout).
   __device__ __forceinline__ void store_rows(__bf16* lds, int tid) const {
@@ -276,7 +295,7 @@ struct TrTileRegs {
       int a = g / CPR, cd = g % CPR;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(4 * a + rr, cd)) = r[i][rr];
+        *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(4 * a + rr, cd)) = val(i, rr, tid);
     }
   }
   __device__ __forceinline__ void store(__bf16* lds, int tid) const {
@@ -288,11 +307,12 @@ struct TrTileRegs {
       int col = 4 * a;
       int chunk = tr_chunk_of(col);
       int pos = tr_pos_of(col);
+      const u32x4 v0 = val(i, 0, tid), v1 = val(i, 1, tid), v2 = val(i, 2, tid), v3 = val(i, 3, tid);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         int d = cd * 8 + e;
         int w = e >> 1;
-        uint32_t x0 = r[i][0][w], x1 = r[i][1][w], x2 = r[i][2][w], x3 = r[i][3][w];
+        uint32_t x0 = v0[w], x1 = v1[w], x2 = v2[w], x3 = v3[w];
         uint32_t lo, hi;
         if (e & 1) {
           lo = (x0 >> 16) | (x1 & 0xffff0000u);

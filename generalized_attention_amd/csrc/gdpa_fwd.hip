@@ -6,16 +6,21 @@
 // partial sum to O: there is no running maximum, no rescaling and no final
 // division, unlike softmax flash attention.
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, query head,
-// 128-row query block); wave w owns query rows 32w..32w+31 of the block.
-// Per KV tile of BN = 8192/D keys:
-//   * K (row-major) and V^T (transposed, accumulator column order) are staged
-//     in LDS, double-buffered: the next tile's global loads are issued before
-//     the current tile's MFMAs and written to the other buffer afterwards;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16 (Q^T held in registers as the B
-//     operand for the whole loop), scaled, masked and activated in registers;
-//   * P^T is packed to bf16 straight from the accumulators and used as the B
-//     operand of O^T += V^T P^T (fp32 accumulation in registers).
+// Work decomposition: one workgroup (4 waves, two workgroups per CU) per
+// (sequence, query head, 128-row query block); wave w owns query rows
+// 32w..32w+31.  Per KV tile of BN = 8192/D keys:
+//   * K and V are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//     staging), row-major with 16-byte chunks XOR-swizzled by the row index;
+//     tiles are double-buffered, the next tile's copy is in flight while the
+//     current tile is computed;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (Q^T stays in registers as the B
+//     operand for the whole loop), then scale, mask and activation in
+//     registers;
+//   * P^T is packed to bf16 straight from the accumulators and is the B
+//     operand of O^T += V^T P^T.  The V^T operand comes from the row-major V
+//     tile through ds_read_b64_tr_b16, whose 16-lane transpose hands each lane
+//     4 consecutive keys of one head-dim column, in exactly the key order of
+//     the accumulator rows.
 // Query blocks are dispatched last-block-first: for self-attention the late
 // blocks exist only in long sequences and carry the most KV tiles, so the
 // hardware dispatcher sees roughly longest-processing-time-first order (the
@@ -25,16 +30,133 @@
 
 namespace gdpa {
 
-template <int D, int ACT, bool FP8>
-__global__ __launch_bounds__(256) void gdpa_fwd_kernel(const FwdArgs a) {
-  constexpr int BM = kFwdBM;
-  constexpr int BN = 8192 / D;          // keys per KV tile
-  constexpr int NKB = BN / 32;          // 32-key blocks per tile
-  constexpr int KS = D / 16;            // k-steps of Q K^T
-  constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int KBYTES = FP8 ? BN * D : BN * D * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][KBYTES];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * BN];
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzle of a row-major LDS row tile.
+template <int ROWB>
+__device__ __forceinline__ int chunk_swz(int row) {
+  return (ROWB >= 128) ? (row & 7) : ((row >> 1) & 3);  // 64-byte rows: two rows per bank sweep
+}
+template <int ROWB>
+__device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk
+  return row * ROWB + ((chunk ^ chunk_swz<ROWB>(row)) << 4);
+}
+
+// Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile.  Rows at or
+// beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks the
+// matching keys, so the duplicated rows never contribute.
+template <int NROW, int ROWB>
+__device__ __forceinline__ void stage_tile(const uint8_t* g, long ld_bytes, int nvalid, uint8_t* lds, int wave,
+                                           int lane) {
+  constexpr int U = ROWB / 16;                // 16-byte units per row
+  constexpr int NI = NROW * U / 256;          // instructions per wave
+  static_assert(NROW * U % 256 == 0, "tile must be a multiple of 4 KiB");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = i * 4 + wave;             // 1 KiB block of LDS written by this instruction
+    const int p = blk * 64 + lane;            // destination unit
+    const int row = p / U, pc = p % U;
+    const int c = pc ^ chunk_swz<ROWB>(row);  // logical chunk stored at physical chunk pc
+    const uint8_t* src = g + (long)min(row, nvalid - 1) * ld_bytes + c * 16;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <int D, int ACT, bool FP8, bool PSPLIT>
+struct FwdKernel {
+  static constexpr int BM = kFwdBM;
+  static constexpr int BN = 8192 / D;     // keys per KV tile
+  static constexpr int NKB = BN / 32;     // 32-key blocks per tile
+  static constexpr int KS = D / 16;       // k-steps of Q K^T
+  static constexpr int NDB = D / 32;      // 32-row blocks of O^T
+  static constexpr int KROWB = FP8 ? D : 2 * D;
+  static constexpr int VROWB = 2 * D;
+
+  // S^T for one tile, activation, and O^T += V^T P^T.  MASK: apply the
+  // window / key-tail mask element-wise.
+  template <bool MASK>
+  static __device__ __forceinline__ void tile(const uint8_t* kl, const uint8_t* vl, const u32x4* qreg,
+                                              const u32x2* qreg8, f32x16* oacc, int lane, int n0, int ip,
+                                              int lk, const FwdArgs& a) {
+    const int hf = lane >> 5;
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + (lane & 31);
+        if constexpr (FP8) {
+          const u32x2 aop = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(row, s) + hf * 8);
+          sacc[kb] = mfma_fp8(aop, qreg8[s], sacc[kb]);
+        } else {
+          const u32x4 aop = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, 2 * s + hf));
+          sacc[kb] = mfma_bf16(aop, qreg[s], sacc[kb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      u32x4 phi[2], plo[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float y[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * t + 2 * w + u;
+            float v = Act<ACT>::f(sacc[kb][r] * a.s_scale, a.act_param);
+            if constexpr (MASK) {
+              const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
+              bool ok = j < lk;
+              if (a.wl >= 0) ok = ok && j >= ip - a.wl;
+              if (a.wr >= 0) ok = ok && j <= ip + a.wr;
+              v = ok ? v : 0.0f;
+            }
+            y[u] = v;
+          }
+          const uint32_t hi = pack_bf16x2(y[0], y[1]);
+          phi[t][w] = hi;
+          if constexpr (PSPLIT) plo[t][w] = pack_bf16x2(y[0] - bf16_lo_to_f32(hi), y[1] - bf16_hi_to_f32(hi));
+        }
+      }
+      // V^T operand: lane (group g = lane/16, r = lane%16) addresses V[key0 + r/4][d0 + 4 (r%4)];
+      // the transpose read returns V[key0 + e][d0 + r], e = 0..3.
+      const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          bf16x4 part[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int key = kb * 32 + 16 * t + 8 * c + 4 * (g >> 1) + (r >> 2);
+            const int d = db * 32 + 16 * (g & 1) + 4 * (r & 3);
+            const uint8_t* p = vl + lds_off<VROWB>(key, d >> 3) + ((d & 4) << 1);
+            part[c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(p));
+          }
+          const bf16x8 aop = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, phi[t]), oacc[db], 0, 0, 0);
+          if constexpr (PSPLIT)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, plo[t]), oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+template <int D, int ACT, bool FP8, bool PSPLIT>
+__global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
+  using K = FwdKernel<D, ACT, FP8, PSPLIT>;
+  constexpr int BM = K::BM, BN = K::BN, KS = K::KS, NDB = K::NDB;
+  constexpr int KBYTES = BN * K::KROWB, VBYTES = BN * K::VROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,60 +201,34 @@ __global__ __launch_bounds__(256) void gdpa_fwd_kernel(const FwdArgs a) {
   u32x4 qreg[FP8 ? 1 : KS];
   u32x2 qreg8[FP8 ? KS : 1];
   if constexpr (FP8) {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (long)(qs + qi) * q_ld + h * D + hf * 8;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qreg8[s] = (qi < lq) ? *reinterpret_cast<const u32x2*>(qp + s * 16) : u32x2{0u, 0u};
+    for (int s = 0; s < KS; ++s) qreg8[s] = load8_or_zero(qp + s * 16, qi < lq);
   } else {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + (long)(qs + qi) * q_ld + h * D + hf * 8;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qreg[s] = (qi < lq) ? *reinterpret_cast<const u32x4*>(qp + s * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < KS; ++s) qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
   }
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
 
+  const int esz = FP8 ? 1 : 2;
   const long kv_ld = (long)a.hkv * D;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (long)ks * kv_ld + g * D;
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (long)ks * kv_ld + g * D;
-  const uint8_t* kbase8 = static_cast<const uint8_t*>(a.k) + (long)ks * kv_ld + g * D;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)ks * kv_ld + g * D) * esz;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)ks * kv_ld + g * D) * 2;
 
-  RowTileRegs<BN, D> kregs;
-  RowTile8Regs<BN, D> kregs8;
-  TrTileRegs<BN, D> vregs;
-
-  auto load_tile = [&](int nb) {
+  auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    if constexpr (FP8)
-      kregs8.load(kbase8 + (long)n0 * kv_ld, kv_ld, lk - n0, tid);
-    else
-      kregs.load(kbase + (long)n0 * kv_ld, kv_ld, lk - n0, tid);
-    vregs.load(vbase + (long)n0 * kv_ld, kv_ld, lk - n0, tid);
+    stage_tile<BN, K::KROWB>(kbase + (long)n0 * kv_ld * esz, kv_ld * esz, lk - n0, kl, wave, lane);
+    stage_tile<BN, K::VROWB>(vbase + (long)n0 * kv_ld * 2, kv_ld * 2, lk - n0, vl, wave, lane);
   };
-  auto store_tile = [&](int buf) {
-    if constexpr (FP8)
-      kregs8.store(k_lds[buf], tid);
-    else
-      kregs.store(reinterpret_cast<__bf16*>(k_lds[buf]), tid);
-    vregs.store(vt_lds[buf], tid);
-  };
-
-  if (nb_begin < nb_end) {
-    load_tile(nb_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int nb = nb_begin; nb < nb_end; ++nb) {
-    const int buf = (nb - nb_begin) & 1;
-    const bool has_next = nb + 1 < nb_end;
-    if (has_next) load_tile(nb + 1);
-
+  // One tile of math for this wave; the mask is applied only where the
+  // window cuts the tile or the tile runs past the last key.
+  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) {
     const int n0 = nb * BN;
-    // wave-level mask classification of this tile
-    bool empty = false, full = true;
+    bool empty = false, full = n0 + BN <= lk;
     if (a.wr >= 0) {
       empty |= n0 > qmax_w + off + a.wr;
       full &= n0 + BN - 1 <= q0w + off + a.wr;
@@ -141,73 +237,25 @@ __global__ __launch_bounds__(256) void gdpa_fwd_kernel(const FwdArgs a) {
       empty |= n0 + BN - 1 < q0w + off - a.wl;
       full &= n0 >= qmax_w + off - a.wl;
     }
-    if (wave_active && !empty) {
-      // ---- S^T = K Q^T
-      f32x16 sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int row = kb * 32 + (lane & 31);
-          if constexpr (FP8) {
-            u32x2 aop = *reinterpret_cast<const u32x2*>(k_lds[buf] + row_tile8_off<D>(row, 2 * s + hf));
-            sacc[kb] = mfma_fp8(aop, qreg8[s], sacc[kb]);
-          } else {
-            const __bf16* kl = reinterpret_cast<const __bf16*>(k_lds[buf]);
-            u32x4 aop = *reinterpret_cast<const u32x4*>(kl + row_tile_off<D>(row, 2 * s + hf));
-            sacc[kb] = mfma_bf16(aop, qreg[s], sacc[kb]);
-          }
-        }
-      }
-      // ---- P = M .* act(scale S), packed to bf16 (hi, and lo = remainder if split)
-      u32x4 phi[NKB][2], plo[NKB][2];
-      const int ip = qi + off;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kb][r] * a.s_scale;
-          float y = Act<ACT>::f(x, a.act_param);
-          if (!full) {
-            const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
-            bool ok = true;
-            if (a.wl >= 0) ok &= j >= ip - a.wl;
-            if (a.wr >= 0) ok &= j <= ip + a.wr;
-            y = ok ? y : 0.0f;
-          }
-          p[r] = y;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float x0 = p[8 * t + 2 * w], x1 = p[8 * t + 2 * w + 1];
-            const uint32_t hi = pack_bf16x2(x0, x1);
-            phi[kb][t][w] = hi;
-            if (a.psplit) plo[kb][t][w] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
-          }
-        }
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int chunk = kb * 4 + 2 * t + hf;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + (lane & 31);
-            u32x4 aop = *reinterpret_cast<const u32x4*>(vt_lds[buf] + tr_tile_off<BN>(d, chunk));
-            oacc[db] = mfma_bf16(aop, phi[kb][t], oacc[db]);
-            if (a.psplit) oacc[db] = mfma_bf16(aop, plo[kb][t], oacc[db]);
-          }
-        }
-      }
-    }
-    if (has_next) store_tile(buf ^ 1);
+    if (!wave_active || empty) return;
+    if (full)
+      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, qi + off, lk, a);
+    else
+      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, qi + off, lk, a);
+  };
+
+  if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): tile copy landed
+  __syncthreads();
+  for (int nb = nb_begin; nb < nb_end; nb += 2) {
+    if (nb + 1 < nb_end) stage(nb + 1, k_lds1, v_lds1);
+    compute(nb, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nb + 1 >= nb_end) break;
+    if (nb + 2 < nb_end) stage(nb + 2, k_lds0, v_lds0);
+    compute(nb + 1, k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -237,8 +285,13 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
   const long grid = (long)a.batch * a.hq * a.mblocks;
   dim3 g((unsigned)grid), blk(256);
   switch (act_kind) {
-#define GDPA_FWD_CASE(K) \
-  case K: hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8>), g, blk, 0, stream, a); break;
+#define GDPA_FWD_CASE(K)                                                                   \
+  case K:                                                                                  \
+    if (a.psplit)                                                                          \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, true>), g, blk, 0, stream, a);        \
+    else                                                                                   \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, false>), g, blk, 0, stream, a);       \
+    break;
     GDPA_FWD_CASE(ACT_IDENTITY)
     GDPA_FWD_CASE(ACT_GELU)
     GDPA_FWD_CASE(ACT_GELU_TANH)

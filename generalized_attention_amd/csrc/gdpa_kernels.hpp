@@ -80,6 +80,7 @@ constexpr int kBwdBN = 128;
 constexpr int kBwdBM = 128;
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int act_kind, bool fp8, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
+                      hipStream_t stream);
 
 }  // namespace gdpa

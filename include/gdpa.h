@@ -139,7 +139,10 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
  * README lists FP8 as forward-only, so an FP8 in_dtype returns
  * GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout; all three
  * are written in grad_dtype (GDPA_DTYPE_FP32 or GDPA_DTYPE_BF16).  The dQ
- * reduction over key blocks runs in a fixed order (deterministic). */
+ * reduction over key blocks runs in a fixed order (deterministic).
+ * Partial gradients: dq == NULL skips dQ; dk == dv == NULL skips dK and dV
+ * (e.g. frozen keys/values).  dk and dv must be both NULL or both non-NULL,
+ * and at least one gradient must be requested (else GDPA_ERR_INVALID_ARG). */
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout,
                        void* dq, void* dk, void* dv,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k,

@@ -124,8 +124,8 @@ def test_varlen_fwd_validation(lib, over, expect):
     (dict(ind=2), UNSUPPORTED),              # FP8 is forward-only (README "Features")
     (dict(ind=1), UNSUPPORTED),
     (dict(gd=2), INVALID),
-    (dict(dq=None), INVALID),
-    (dict(dk=None), INVALID),
+    (dict(dk=None), INVALID),                # dk and dv must be requested together
+    (dict(dq=None, dk=None, dv=None), INVALID),
     (dict(Hq=5), INVALID),
     (dict(B=0), OK),
 ])

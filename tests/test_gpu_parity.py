@@ -173,3 +173,18 @@ def test_fixed_length_equals_varlen(g):
     assert torch.equal(o_fixed, o_var)
     for a, b in zip(run_backward(g, bt), run_backward(g, bt_var)):
         assert torch.equal(a, b)
+
+
+def test_partial_gradients(g):
+    import torch
+    bt = gi.make_batch(_wl(act="silu", mask="causal"), seqlens_q=[200, 70], seqlens_k=[200, 70])
+    dev = device_batch(bt)
+    dq, dk, dv = run_backward(g, bt, dev)
+    wl = bt.wl
+    common = (dev["cu_q"], dev["cu_k"], bt.max_seqlen_q, bt.max_seqlen_k, wl.scale)
+    kw = dict(act=wl.act, mask=wl.mask)
+    dq2 = torch.full_like(dq, float("nan"))
+    g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], dq2, None, None, *common, **kw)
+    dk2, dv2 = torch.full_like(dk, float("nan")), torch.full_like(dv, float("nan"))
+    g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, dk2, dv2, *common, **kw)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
