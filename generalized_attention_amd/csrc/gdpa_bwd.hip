@@ -11,16 +11,17 @@
 // Two kernels, each writing its outputs exactly once (no atomics, so results
 // are bitwise reproducible):
 //  * dK/dV kernel (KV-outer): one workgroup per (sequence, KV head, 128-key
-//    block), wave w owns keys 32w..32w+31 with K and V held in registers.  It
-//    loops over the group's query heads and 32-row query blocks; Q and dO
-//    tiles are staged in LDS both row-major (A operands of S = Q K^T and
-//    dP = dO V^T) and transposed (A operands of dK^T += Q^T dS and
-//    dV^T += dO^T P).  S and dP come out of the MFMAs with the query index on
-//    the accumulator rows, so P and dS feed the next products straight from
-//    registers.
+//    block), wave w owns keys 32w..32w+31 with K and V held in registers as B
+//    operands.  It loops over the group's query heads and 64-row query
+//    blocks; each Q and dO tile is copied HBM -> LDS once (row-major) and read
+//    both row-wise (A operands of S = Q K^T and dP = dO V^T) and through the
+//    transposing LDS read (A operands of dK^T += Q^T dS and dV^T += dO^T P).
+//    S and dP come out of the MFMAs with the query index on the accumulator
+//    rows, so P and dS feed the next products straight from registers.
 //  * dQ kernel (Q-outer): one workgroup per (sequence, query head, 128-row
-//    block) recomputes S^T = K Q^T and dP^T = V dO^T per KV tile and
-//    accumulates dQ^T += K^T dS^T in a fixed key order.
+//    block), Q and dO in registers; per KV tile it recomputes S^T = K Q^T and
+//    dP^T = V dO^T and accumulates dQ^T += K^T dS^T in a fixed key order, the
+//    K^T operand again read transposed from the row-major K tile.
 // This costs 7 matrix products per (query, key) pair instead of the 5 the
 // gradient needs, in exchange for a deterministic dQ without a reduction
 // buffer.
@@ -43,17 +44,93 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
   }
 }
 
+// bf16 hi/lo pair of (x0, x1): hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ uint32_t split_lo(float x0, float x1, uint32_t hi) {
+  return pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+}
+
 // ------------------------------------------------------------------ dK / dV
-template <int D, int ACT>
-__global__ __launch_bounds__(256) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
+template <int D, int ACT, bool SPLIT>
+struct DkdvKernel {
+  static constexpr int BQ = 64;        // query rows per step (two 32-row blocks)
+  static constexpr int KS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int ROWB = 2 * D;
+
+  // One 32-query block against this wave's 32 keys.
+  template <bool MASK>
+  static __device__ __forceinline__ void block(const uint8_t* ql, const uint8_t* dl, int qb, const u32x4* kreg,
+                                               const u32x4* vreg, f32x16* dkacc, f32x16* dvacc, int lane,
+                                               int m0, int kj, int lq, int off, const BwdArgs& a) {
+    const int hf = lane >> 5;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sacc = mfma_bf16(row_operand<ROWB>(ql, qb * 32, 2 * s, lane), kreg[s], sacc);
+      dpacc = mfma_bf16(row_operand<ROWB>(dl, qb * 32, 2 * s, lane), vreg[s], dpacc);
+    }
+    // accumulator element r: query m0 + qb*32 + 4hf + 8(r/4) + r%4, key kj
+    u32x4 pb[2], dsb[2], pbl[2], dsbl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float pv[2], dsv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * t + 2 * w + u;
+          float dy;
+          float y = Act<ACT>::f_df(sacc[r] * a.scale, a.act_param, dy);
+          float ds = dpacc[r] * dy;
+          if constexpr (MASK) {
+            const int i = m0 + qb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
+            const int ip = i + off;
+            bool ok = i < lq;
+            if (a.wl >= 0) ok = ok && kj >= ip - a.wl;
+            if (a.wr >= 0) ok = ok && kj <= ip + a.wr;
+            y = ok ? y : 0.0f;
+            ds = ok ? ds : 0.0f;
+          }
+          pv[u] = y;
+          dsv[u] = ds;
+        }
+        pb[t][w] = pack_bf16x2(pv[0], pv[1]);
+        dsb[t][w] = pack_bf16x2(dsv[0], dsv[1]);
+        if constexpr (SPLIT) {
+          pbl[t][w] = split_lo(pv[0], pv[1], pb[t][w]);
+          dsbl[t][w] = split_lo(dsv[0], dsv[1], dsb[t][w]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 doa = tr_operand<ROWB>(dl, qb * 32 + 16 * t, db * 32, lane);
+        const bf16x8 qta = tr_operand<ROWB>(ql, qb * 32 + 16 * t, db * 32, lane);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, __builtin_bit_cast(bf16x8, pb[t]), dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, __builtin_bit_cast(bf16x8, dsb[t]), dkacc[db], 0, 0, 0);
+        if constexpr (SPLIT) {
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, __builtin_bit_cast(bf16x8, pbl[t]), dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, __builtin_bit_cast(bf16x8, dsbl[t]), dkacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+// D = 128 keeps dK, dV, K and V (256 registers) live across the loop: one
+// wave per SIMD there; D = 64 fits two.
+template <int D, int ACT, bool SPLIT>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
+  using K = DkdvKernel<D, ACT, SPLIT>;
   constexpr int BNB = kBwdBN;  // keys per workgroup (32 per wave)
-  constexpr int BQ = 32;       // query rows per step
-  constexpr int KS = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 qt_lds[2][D * BQ];
-  __shared__ __attribute__((aligned(16))) __bf16 do_lds[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 dot_lds[2][D * BQ];
+  constexpr int BQ = K::BQ, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;
+  constexpr int TB = BQ * ROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,106 +180,51 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
     dvacc[i] = f32x16{};
   }
 
-  const long q_ld = (long)a.hq * D;
-  TrTileRegs<BQ, D> qregs, doregs;
-  auto load_step = [&](int step) {
+  const long q_ld_b = (long)a.hq * D * 2;  // bytes per token row of q / dO
+  auto stage = [&](int step, uint8_t* ql, uint8_t* dl) {
     const int h = g * a.group + step % a.group;
     const int m0 = (mb_begin + step / a.group) * BQ;
-    const __bf16* qb = static_cast<const __bf16*>(a.q) + (long)(qs + m0) * q_ld + h * D;
-    const __bf16* db = static_cast<const __bf16*>(a.dout) + (long)(qs + m0) * q_ld + h * D;
-    qregs.load(qb, q_ld, lq - m0, tid);
-    doregs.load(db, q_ld, lq - m0, tid);
+    const long base = (long)(qs + m0) * q_ld_b + (long)h * D * 2;
+    stage_tile<BQ, ROWB>(static_cast<const uint8_t*>(a.q) + base, q_ld_b, lq - m0, ql, wave, lane);
+    stage_tile<BQ, ROWB>(static_cast<const uint8_t*>(a.dout) + base, q_ld_b, lq - m0, dl, wave, lane);
   };
-  auto store_step = [&](int buf) {
-    qregs.store_rows(q_lds[buf], tid);
-    qregs.store(qt_lds[buf], tid);
-    doregs.store_rows(do_lds[buf], tid);
-    doregs.store(dot_lds[buf], tid);
-  };
-
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-  }
-  __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool has_next = step + 1 < nsteps;
-    if (has_next) load_step(step + 1);
+  auto compute = [&](int step, const uint8_t* ql, const uint8_t* dl) {
+    if (!wave_active) return;
     const int m0 = (mb_begin + step / a.group) * BQ;
-    const int mmax = min(m0 + BQ - 1, lq - 1);
-    // wave-level mask classification of (queries m0.., keys k0w..)
-    bool empty = false, full = true;
-    if (a.wr >= 0) {
-      empty |= k0w > mmax + off + a.wr;
-      full &= kmax_w <= m0 + off + a.wr;
-    }
-    if (a.wl >= 0) {
-      empty |= kmax_w < m0 + off - a.wl;
-      full &= k0w >= mmax + off - a.wl;
-    }
-    if (wave_active && !empty) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int row = lane & 31;
-        u32x4 qa = *reinterpret_cast<const u32x4*>(q_lds[buf] + row_tile_off<D>(row, 2 * s + hf));
-        u32x4 da = *reinterpret_cast<const u32x4*>(do_lds[buf] + row_tile_off<D>(row, 2 * s + hf));
-        sacc = mfma_bf16(qa, kreg[s], sacc);
-        dpacc = mfma_bf16(da, vreg[s], dpacc);
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int mlo = m0 + qb * 32, mhi = mlo + 31;
+      if (mlo >= lq) break;
+      // wave-level classification of (queries mlo..mhi, keys k0w..kmax_w)
+      bool empty = false, full = mhi < lq;
+      if (a.wr >= 0) {
+        empty |= k0w > min(mhi, lq - 1) + off + a.wr;
+        full &= kmax_w <= mlo + off + a.wr;
       }
-      // accumulator element r: query m0 + 4hf + 8(r/4) + r%4, key kj
-      u32x4 pb[2], dsb[2], pbl[2], dsbl[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float pv[2], dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * t + 2 * w + u;
-            float dy;
-            float y = Act<ACT>::f_df(sacc[r] * a.scale, a.act_param, dy);
-            float ds = dpacc[r] * dy;
-            if (!full) {
-              const int ip = m0 + hf * 4 + 8 * (r >> 2) + (r & 3) + off;
-              bool ok = true;
-              if (a.wl >= 0) ok &= kj >= ip - a.wl;
-              if (a.wr >= 0) ok &= kj <= ip + a.wr;
-              y = ok ? y : 0.0f;
-              ds = ok ? ds : 0.0f;
-            }
-            pv[u] = y;
-            dsv[u] = ds;
-          }
-          const uint32_t ph = pack_bf16x2(pv[0], pv[1]);
-          const uint32_t dh = pack_bf16x2(dsv[0], dsv[1]);
-          pb[t][w] = ph;
-          dsb[t][w] = dh;
-          if (a.kvsplit) {
-            pbl[t][w] = pack_bf16x2(pv[0] - bf16_lo_to_f32(ph), pv[1] - bf16_hi_to_f32(ph));
-            dsbl[t][w] = pack_bf16x2(dsv[0] - bf16_lo_to_f32(dh), dsv[1] - bf16_hi_to_f32(dh));
-          }
-        }
+      if (a.wl >= 0) {
+        empty |= kmax_w < mlo + off - a.wl;
+        full &= k0w >= mhi + off - a.wl;
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + (lane & 31);
-          u32x4 doa = *reinterpret_cast<const u32x4*>(dot_lds[buf] + tr_tile_off<BQ>(d, 2 * t + hf));
-          u32x4 qta = *reinterpret_cast<const u32x4*>(qt_lds[buf] + tr_tile_off<BQ>(d, 2 * t + hf));
-          dvacc[db] = mfma_bf16(doa, pb[t], dvacc[db]);
-          dkacc[db] = mfma_bf16(qta, dsb[t], dkacc[db]);
-          if (a.kvsplit) {
-            dvacc[db] = mfma_bf16(doa, pbl[t], dvacc[db]);
-            dkacc[db] = mfma_bf16(qta, dsbl[t], dkacc[db]);
-          }
-        }
-      }
+      if (empty) continue;
+      if (full)
+        K::template block<false>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, kj, lq, off, a);
+      else
+        K::template block<true>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, kj, lq, off, a);
     }
-    if (has_next) store_step(buf ^ 1);
+  };
+
+  if (nsteps > 0) stage(0, q_lds0, do_lds0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    if (step + 1 < nsteps) stage(step + 1, q_lds1, do_lds1);
+    compute(step, q_lds0, do_lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (step + 1 >= nsteps) break;
+    if (step + 2 < nsteps) stage(step + 2, q_lds0, do_lds0);
+    compute(step + 1, q_lds1, do_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -231,16 +253,75 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------- dQ
-template <int D, int ACT>
-__global__ __launch_bounds__(256) void gdpa_bwd_dq_kernel(const BwdArgs a) {
+template <int D, int ACT, bool SPLIT>
+struct DqKernel {
+  static constexpr int BN = 8192 / D;  // keys per KV tile
+  static constexpr int NKB = BN / 32;
+  static constexpr int KS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int ROWB = 2 * D;
+
+  // One 32-key block of the tile against this wave's 32 queries.
+  template <bool MASK>
+  static __device__ __forceinline__ void block(const uint8_t* kl, const uint8_t* vl, int kb, const u32x4* qreg,
+                                               const u32x4* doreg, f32x16* dqacc, int lane, int n0, int ip,
+                                               int lk, const BwdArgs& a) {
+    const int hf = lane >> 5;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sacc = mfma_bf16(row_operand<ROWB>(kl, kb * 32, 2 * s, lane), qreg[s], sacc);
+      dpacc = mfma_bf16(row_operand<ROWB>(vl, kb * 32, 2 * s, lane), doreg[s], dpacc);
+    }
+    // accumulator element r: key n0 + kb*32 + 4hf + 8(r/4) + r%4, query ip - off
+    u32x4 dsh[2], dsl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float dsv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * t + 2 * w + u;
+          float dy;
+          (void)Act<ACT>::f_df(sacc[r] * a.scale, a.act_param, dy);
+          float ds = dpacc[r] * dy;
+          if constexpr (MASK) {
+            const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
+            bool ok = j < lk;
+            if (a.wl >= 0) ok = ok && j >= ip - a.wl;
+            if (a.wr >= 0) ok = ok && j <= ip + a.wr;
+            ds = ok ? ds : 0.0f;
+          }
+          dsv[u] = ds;
+        }
+        dsh[t][w] = pack_bf16x2(dsv[0], dsv[1]);
+        if constexpr (SPLIT) dsl[t][w] = split_lo(dsv[0], dsv[1], dsh[t][w]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 kta = tr_operand<ROWB>(kl, kb * 32 + 16 * t, db * 32, lane);
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, __builtin_bit_cast(bf16x8, dsh[t]), dqacc[db], 0, 0, 0);
+        if constexpr (SPLIT)
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, __builtin_bit_cast(bf16x8, dsl[t]), dqacc[db], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int D, int ACT, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
+  using K = DqKernel<D, ACT, SPLIT>;
   constexpr int BM = kBwdBM;
-  constexpr int BN = 4096 / D;  // keys per KV tile
-  constexpr int NKB = BN / 32;
-  constexpr int KS = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[2][D * BN];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][BN * D];
+  constexpr int BN = K::BN, NKB = K::NKB, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;
+  constexpr int TB = BN * ROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,103 +366,50 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
 
-  const long kv_ld = (long)a.hkv * D;
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (long)ks * kv_ld + g * D;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (long)ks * kv_ld + g * D;
-  TrTileRegs<BN, D> kregs;
-  RowTileRegs<BN, D> vregs;
-  auto load_tile = [&](int nb) {
+  const long kv_ld_b = (long)a.hkv * D * 2;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (long)ks * kv_ld_b + (long)g * D * 2;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (long)ks * kv_ld_b + (long)g * D * 2;
+  auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    kregs.load(kbase + (long)n0 * kv_ld, kv_ld, lk - n0, tid);
-    vregs.load(vbase + (long)n0 * kv_ld, kv_ld, lk - n0, tid);
+    stage_tile<BN, ROWB>(kbase + (long)n0 * kv_ld_b, kv_ld_b, lk - n0, kl, wave, lane);
+    stage_tile<BN, ROWB>(vbase + (long)n0 * kv_ld_b, kv_ld_b, lk - n0, vl, wave, lane);
   };
-  auto store_tile = [&](int buf) {
-    kregs.store_rows(k_lds[buf], tid);
-    kregs.store(kt_lds[buf], tid);
-    vregs.store(v_lds[buf], tid);
+  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) {
+    if (!wave_active) return;
+    const int n0 = nb * BN;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int jlo = n0 + kb * 32, jhi = jlo + 31;
+      if (jlo >= lk) break;
+      bool empty = false, full = jhi < lk;
+      if (a.wr >= 0) {
+        empty |= jlo > qmax_w + off + a.wr;
+        full &= jhi <= q0w + off + a.wr;
+      }
+      if (a.wl >= 0) {
+        empty |= jhi < q0w + off - a.wl;
+        full &= jlo >= qmax_w + off - a.wl;
+      }
+      if (empty) continue;
+      if (full)
+        K::template block<false>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, qi + off, lk, a);
+      else
+        K::template block<true>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, qi + off, lk, a);
+    }
   };
 
-  if (nb_begin < nb_end) {
-    load_tile(nb_begin);
-    store_tile(0);
-  }
+  if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  for (int nb = nb_begin; nb < nb_end; ++nb) {
-    const int buf = (nb - nb_begin) & 1;
-    const bool has_next = nb + 1 < nb_end;
-    if (has_next) load_tile(nb + 1);
-    const int n0 = nb * BN;
-    bool empty = false, full = true;
-    if (a.wr >= 0) {
-      empty |= n0 > qmax_w + off + a.wr;
-      full &= n0 + BN - 1 <= q0w + off + a.wr;
-    }
-    if (a.wl >= 0) {
-      empty |= n0 + BN - 1 < q0w + off - a.wl;
-      full &= n0 >= qmax_w + off - a.wl;
-    }
-    if (wave_active && !empty) {
-      f32x16 sacc[NKB], dpacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = f32x16{};
-        dpacc[kb] = f32x16{};
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int row = kb * 32 + (lane & 31);
-          u32x4 ka = *reinterpret_cast<const u32x4*>(k_lds[buf] + row_tile_off<D>(row, 2 * s + hf));
-          u32x4 va = *reinterpret_cast<const u32x4*>(v_lds[buf] + row_tile_off<D>(row, 2 * s + hf));
-          sacc[kb] = mfma_bf16(ka, qreg[s], sacc[kb]);
-          dpacc[kb] = mfma_bf16(va, doreg[s], dpacc[kb]);
-        }
-      }
-      const int ip = qi + off;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        u32x4 dsh[2], dsl[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            float dsv[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int r = 8 * t + 2 * w + u;
-              float dy;
-              (void)Act<ACT>::f_df(sacc[kb][r] * a.scale, a.act_param, dy);
-              float ds = dpacc[kb][r] * dy;
-              if (!full) {
-                const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
-                bool ok = true;
-                if (a.wl >= 0) ok &= j >= ip - a.wl;
-                if (a.wr >= 0) ok &= j <= ip + a.wr;
-                ds = ok ? ds : 0.0f;
-              }
-              dsv[u] = ds;
-            }
-            const uint32_t hi = pack_bf16x2(dsv[0], dsv[1]);
-            dsh[t][w] = hi;
-            if (a.dsplit) dsl[t][w] = pack_bf16x2(dsv[0] - bf16_lo_to_f32(hi), dsv[1] - bf16_hi_to_f32(hi));
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int chunk = kb * 4 + 2 * t + hf;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + (lane & 31);
-            u32x4 kta = *reinterpret_cast<const u32x4*>(kt_lds[buf] + tr_tile_off<BN>(d, chunk));
-            dqacc[db] = mfma_bf16(kta, dsh[t], dqacc[db]);
-            if (a.dsplit) dqacc[db] = mfma_bf16(kta, dsl[t], dqacc[db]);
-          }
-        }
-      }
-    }
-    if (has_next) store_tile(buf ^ 1);
+  for (int nb = nb_begin; nb < nb_end; nb += 2) {
+    if (nb + 1 < nb_end) stage(nb + 1, k_lds1, v_lds1);
+    compute(nb, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nb + 1 >= nb_end) break;
+    if (nb + 2 < nb_end) stage(nb + 2, k_lds0, v_lds0);
+    compute(nb + 1, k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -403,16 +431,18 @@ __global__ __launch_bounds__(256) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   }
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
+template <int D, bool SPLIT_KV, bool SPLIT_Q>
+static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
   const long grid_kv = want_dkv ? (long)a.batch * a.hkv * a.nblocks : 0;
   const long grid_q = want_dq ? (long)a.batch * a.hq * a.mblocks : 0;
   dim3 blk(256);
   switch (act_kind) {
-#define GDPA_BWD_CASE(K)                                                                             \
-  case K:                                                                                            \
-    if (grid_kv > 0) hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K>), dim3((unsigned)grid_kv), blk, 0, stream, a); \
-    if (grid_q > 0) hipLaunchKernelGGL((gdpa_bwd_dq_kernel<D, K>), dim3((unsigned)grid_q), blk, 0, stream, a);     \
+#define GDPA_BWD_CASE(K)                                                                                       \
+  case K:                                                                                                      \
+    if (grid_kv > 0)                                                                                           \
+      hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K, SPLIT_KV>), dim3((unsigned)grid_kv), blk, 0, stream, a); \
+    if (grid_q > 0)                                                                                            \
+      hipLaunchKernelGGL((gdpa_bwd_dq_kernel<D, K, SPLIT_Q>), dim3((unsigned)grid_q), blk, 0, stream, a);     \
     break;
     GDPA_BWD_CASE(ACT_IDENTITY)
     GDPA_BWD_CASE(ACT_GELU)
@@ -427,6 +457,15 @@ static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, bool want_dq, boo
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
+  if (a.kvsplit)
+    return a.dsplit ? launch_bwd_ds<D, true, true>(a, act_kind, want_dq, want_dkv, stream)
+                    : launch_bwd_ds<D, true, false>(a, act_kind, want_dq, want_dkv, stream);
+  return a.dsplit ? launch_bwd_ds<D, false, true>(a, act_kind, want_dq, want_dkv, stream)
+                  : launch_bwd_ds<D, false, false>(a, act_kind, want_dq, want_dkv, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,

@@ -327,4 +327,71 @@ struct TrTileRegs {
   }
 };
 
+
+// ------------------------------------------------- direct HBM -> LDS row tiles
+// Row-major [rows][ROWB bytes] tiles written by global_load_lds_dwordx4: each
+// lane's 16 bytes land at (LDS base of the instruction) + 16 * lane, so the
+// chunk swizzle is chosen by picking which source chunk each lane fetches.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzle of a row-major LDS row tile.
+template <int ROWB>
+__device__ __forceinline__ int chunk_swz(int row) {
+  return (ROWB >= 128) ? (row & 7) : ((row >> 1) & 3);  // 64-byte rows: two rows per bank sweep
+}
+template <int ROWB>
+__device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk
+  return row * ROWB + ((chunk ^ chunk_swz<ROWB>(row)) << 4);
+}
+
+// Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile.  Rows at or
+// beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks the
+// matching keys, so the duplicated rows never contribute.
+template <int NROW, int ROWB>
+__device__ __forceinline__ void stage_tile(const uint8_t* g, long ld_bytes, int nvalid, uint8_t* lds, int wave,
+                                           int lane) {
+  constexpr int U = ROWB / 16;                // 16-byte units per row
+  constexpr int NI = NROW * U / 256;          // instructions per wave
+  static_assert(NROW * U % 256 == 0, "tile must be a multiple of 4 KiB");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = i * 4 + wave;             // 1 KiB block of LDS written by this instruction
+    const int p = blk * 64 + lane;            // destination unit
+    const int row = p / U, pc = p % U;
+    const int c = pc ^ chunk_swz<ROWB>(row);  // logical chunk stored at physical chunk pc
+    const uint8_t* src = g + (long)min(row, nvalid - 1) * ld_bytes + c * 16;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+
+// Transposed MFMA A operand from a row-major bf16 row tile via
+// ds_read_b64_tr_b16.  Within each 16-lane group the instruction hands lane j
+// element e of the 8-byte row that lane 4e + j/4 addressed, column j % 4.  So
+// if lane r of group g addresses row (r0 + r/4), columns c0 + 4 (r%4) .. +3,
+// lane j receives rows r0..r0+3 of column c0 + j.  Lane l thus obtains the A
+// operand (row = column index c of the tile, l % 32 within a 32-block; k =
+// 8 tile rows) whose k order matches the accumulator row order of a C tile:
+// k position 4c' + e  <->  tile row 16 t + 8 c' + 4 (l / 32) + e.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, int row_base, int col_base, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  bf16x4 part[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = row_base + 8 * c + 4 * (g >> 1) + (r >> 2);
+    const int col = col_base + 16 * (g & 1) + 4 * (r & 3);
+    const uint8_t* p = tile + lds_off<ROWB>(row, col >> 3) + ((col & 4) << 1);
+    part[c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row-major MFMA A operand (row = tile row l % 32 of the 32-row block at
+// row_base; k = 8 consecutive bf16 columns at chunk `chunk` + l / 32).
+template <int ROWB>
+__device__ __forceinline__ u32x4 row_operand(const uint8_t* tile, int row_base, int chunk, int lane) {
+  return *reinterpret_cast<const u32x4*>(tile + lds_off<ROWB>(row_base + (lane & 31), chunk + (lane >> 5)));
+}
+
 }  // namespace gdpa

@@ -30,38 +30,6 @@
 
 namespace gdpa {
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte chunk swizzle of a row-major LDS row tile.
-template <int ROWB>
-__device__ __forceinline__ int chunk_swz(int row) {
-  return (ROWB >= 128) ? (row & 7) : ((row >> 1) & 3);  // 64-byte rows: two rows per bank sweep
-}
-template <int ROWB>
-__device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk
-  return row * ROWB + ((chunk ^ chunk_swz<ROWB>(row)) << 4);
-}
-
-// Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile.  Rows at or
-// beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks the
-// matching keys, so the duplicated rows never contribute.
-template <int NROW, int ROWB>
-__device__ __forceinline__ void stage_tile(const uint8_t* g, long ld_bytes, int nvalid, uint8_t* lds, int wave,
-                                           int lane) {
-  constexpr int U = ROWB / 16;                // 16-byte units per row
-  constexpr int NI = NROW * U / 256;          // instructions per wave
-  static_assert(NROW * U % 256 == 0, "tile must be a multiple of 4 KiB");
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int blk = i * 4 + wave;             // 1 KiB block of LDS written by this instruction
-    const int p = blk * 64 + lane;            // destination unit
-    const int row = p / U, pc = p % U;
-    const int c = pc ^ chunk_swz<ROWB>(row);  // logical chunk stored at physical chunk pc
-    const uint8_t* src = g + (long)min(row, nvalid - 1) * ld_bytes + c * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
-  }
-}
-
 template <int D, int ACT, bool FP8, bool PSPLIT>
 struct FwdKernel {
   static constexpr int BM = kFwdBM;
@@ -122,23 +90,12 @@ struct FwdKernel {
           if constexpr (PSPLIT) plo[t][w] = pack_bf16x2(y[0] - bf16_lo_to_f32(hi), y[1] - bf16_hi_to_f32(hi));
         }
       }
-      // V^T operand: lane (group g = lane/16, r = lane%16) addresses V[key0 + r/4][d0 + 4 (r%4)];
-      // the transpose read returns V[key0 + e][d0 + r], e = 0..3.
-      const int g = lane >> 4, r = lane & 15;
+      // V^T operand straight from the row-major V tile (transpose read).
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          bf16x4 part[2];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int key = kb * 32 + 16 * t + 8 * c + 4 * (g >> 1) + (r >> 2);
-            const int d = db * 32 + 16 * (g & 1) + 4 * (r & 3);
-            const uint8_t* p = vl + lds_off<VROWB>(key, d >> 3) + ((d & 4) << 1);
-            part[c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(p));
-          }
-          const bf16x8 aop = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 aop = tr_operand<VROWB>(vl, kb * 32 + 16 * t, db * 32, lane);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, phi[t]), oacc[db], 0, 0, 0);
           if constexpr (PSPLIT)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, plo[t]), oacc[db], 0, 0, 0);
