@@ -30,7 +30,7 @@ def _flags():
     # Packed fp32 VALU ops are disabled: the kernels use plain fp32 math only.
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+            "-I", os.path.join(ROOT, "include"), "-Wall", "-Wshadow", "-Wno-unused-function"]
 
 
 def _compile(src: str) -> str:

@@ -93,6 +93,49 @@ bool few_terms(int64_t len, int64_t heads, const Common& c) {
   return len * heads <= kFewTerms;
 }
 
+// Activation constants for the kernels: act(c s) = pscale * y(s), the score
+// scale c folded into the constants (the formulas are listed in
+// gdpa_common.hpp next to the device code that uses them).
+gdpa::ActConsts make_act(int kind, double c, double alpha) {
+  const double log2e = 1.4426950408889634, sqrt2opi = 0.7978845608028654, cubic = 0.044715;
+  gdpa::ActConsts k{};
+  k.alpha = (float)alpha;
+  k.gscale = (float)c;
+  k.pscale = 1.0f;
+  switch (kind) {
+    case gdpa::ACT_IDENTITY: k.pscale = (float)c; break;
+    case gdpa::ACT_GELU:
+      k.k0 = (float)(c / std::sqrt(2.0));
+      k.a0 = (float)(c / std::sqrt(2.0 * M_PI));
+      k.a1 = (float)(-0.5 * c * c * log2e);
+      k.pscale = (float)(0.5 * c);
+      break;
+    case gdpa::ACT_GELU_TANH: {
+      const double c0 = -2.0 * sqrt2opi * log2e;  // sigmoid(2u) = 1 / (1 + 2^(x (c0 + c1 x^2)))
+      k.k0 = (float)(c * c0);
+      k.k1 = (float)(c * c * c * c0 * cubic);
+      k.a0 = (float)(2.0 * sqrt2opi * c);            // x 2u'(x) = s (a0 + a1 s^2)
+      k.a1 = (float)(2.0 * sqrt2opi * 3.0 * cubic * c * c * c);
+      k.pscale = (float)c;
+      break;
+    }
+    case gdpa::ACT_RELU:
+    case gdpa::ACT_RELU2:
+    case gdpa::ACT_LEAKY: k.k0 = (float)c; break;
+    case gdpa::ACT_SILU:
+      k.k0 = (float)(-log2e * c);
+      k.a0 = (float)c;
+      k.pscale = (float)c;
+      break;
+    case gdpa::ACT_HARDSWISH:
+      k.k0 = (float)c;
+      k.pscale = (float)(c / 6.0);
+      break;
+    default: break;
+  }
+  return k;
+}
+
 gdpa_status_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return GDPA_OK;
   if (debug_log()) std::fprintf(stderr, "[gdpa] %s failed: %s\n", what, hipGetErrorString(e));
@@ -133,8 +176,7 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   a.hkv = c.hkv;
   a.group = c.hq / c.hkv;
   a.mblocks = (int32_t)mblocks;
-  a.s_scale = fp8 ? scale * q_descale * k_descale : scale;
-  a.act_param = act_param;
+  a.act = make_act(c.act_kind, fp8 ? (double)scale * q_descale * k_descale : (double)scale, act_param);
   a.wl = c.wl;
   a.wr = c.wr;
   a.out_f32 = out_dtype == GDPA_DTYPE_FP32;
@@ -190,8 +232,7 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.group = c.hq / c.hkv;
   a.mblocks = (int32_t)mblocks;
   a.nblocks = (int32_t)nblocks;
-  a.scale = scale;
-  a.act_param = act_param;
+  a.act = make_act(c.act_kind, scale, act_param);
   a.wl = c.wl;
   a.wr = c.wr;
   a.out_f32 = grad_dtype == GDPA_DTYPE_FP32;

@@ -44,11 +44,6 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
   }
 }
 
-// bf16 hi/lo pair of (x0, x1): hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ uint32_t split_lo(float x0, float x1, uint32_t hi) {
-  return pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
-}
-
 // ------------------------------------------------------------------ dK / dV
 template <int D, int ACT, bool SPLIT>
 struct DkdvKernel {
@@ -57,11 +52,12 @@ struct DkdvKernel {
   static constexpr int NDB = D / 32;
   static constexpr int ROWB = 2 * D;
 
-  // One 32-query block against this wave's 32 keys.
+  // One 32-query block against this wave's 32 keys.  [ilo, ihi]: queries
+  // allowed to see this lane's key.
   template <bool MASK>
   static __device__ __forceinline__ void block(const uint8_t* ql, const uint8_t* dl, int qb, const u32x4* kreg,
                                                const u32x4* vreg, f32x16* dkacc, f32x16* dvacc, int lane,
-                                               int m0, int kj, int lq, int off, const BwdArgs& a) {
+                                               int m0, int ilo, int ihi, const BwdArgs& a) {
     const int hf = lane >> 5;
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -69,7 +65,9 @@ struct DkdvKernel {
       sacc = mfma_bf16(row_operand<ROWB>(ql, qb * 32, 2 * s, lane), kreg[s], sacc);
       dpacc = mfma_bf16(row_operand<ROWB>(dl, qb * 32, 2 * s, lane), vreg[s], dpacc);
     }
-    // accumulator element r: query m0 + qb*32 + 4hf + 8(r/4) + r%4, key kj
+    // accumulator element r: query m0 + qb*32 + 4hf + 8(r/4) + r%4, this lane's key
+    const int base = m0 + qb * 32 + hf * 4;
+    const int lo = ilo - base, hi = ihi - base;
     u32x4 pb[2], dsb[2], pbl[2], dsbl[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -80,14 +78,10 @@ struct DkdvKernel {
         for (int u = 0; u < 2; ++u) {
           const int r = 8 * t + 2 * w + u;
           float dy;
-          float y = Act<ACT>::f_df(sacc[r] * a.scale, a.act_param, dy);
+          float y = Act<ACT>::f_df(sacc[r], a.act, dy);
           float ds = dpacc[r] * dy;
           if constexpr (MASK) {
-            const int i = m0 + qb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
-            const int ip = i + off;
-            bool ok = i < lq;
-            if (a.wl >= 0) ok = ok && kj >= ip - a.wl;
-            if (a.wr >= 0) ok = ok && kj <= ip + a.wr;
+            const bool ok = in_range(r, lo, hi);
             y = ok ? y : 0.0f;
             ds = ok ? ds : 0.0f;
           }
@@ -151,6 +145,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
   const int kj = k0w + (lane & 31);  // this lane's key
   const int kmax_w = min(k0w + 31, lk - 1);
   const int klast = min(n0 + BNB, lk) - 1;
+  // queries that may see this lane's key: [ilo_l, ihi_l]
+  const int ilo_l = a.wr >= 0 ? kj - a.wr - off : 0;
+  const int ihi_l = min(lq - 1, a.wl >= 0 ? kj + a.wl - off : lq - 1);
 
   // query rows that can see any key of this block
   int i_lo = 0, i_hi = lq;
@@ -207,9 +204,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
       }
       if (empty) continue;
       if (full)
-        K::template block<false>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, kj, lq, off, a);
+        K::template block<false>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, 0, 0, a);
       else
-        K::template block<true>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, kj, lq, off, a);
+        K::template block<true>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, ilo_l, ihi_l, a);
     }
   };
 
@@ -235,17 +232,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
-        const float k0 = dkacc[db][4 * i4] * a.scale, k1 = dkacc[db][4 * i4 + 1] * a.scale;
-        const float k2 = dkacc[db][4 * i4 + 2] * a.scale, k3 = dkacc[db][4 * i4 + 3] * a.scale;
+        const float gs = a.act.gscale, ps = a.act.pscale;
+        const float k0 = dkacc[db][4 * i4] * gs, k1 = dkacc[db][4 * i4 + 1] * gs;
+        const float k2 = dkacc[db][4 * i4 + 2] * gs, k3 = dkacc[db][4 * i4 + 3] * gs;
+        const float v0 = dvacc[db][4 * i4] * ps, v1 = dvacc[db][4 * i4 + 1] * ps;
+        const float v2 = dvacc[db][4 * i4 + 2] * ps, v3 = dvacc[db][4 * i4 + 3] * ps;
         if (a.out_f32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.dk) + orow + d) = f32x4{k0, k1, k2, k3};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + orow + d) =
-              f32x4{dvacc[db][4 * i4], dvacc[db][4 * i4 + 1], dvacc[db][4 * i4 + 2], dvacc[db][4 * i4 + 3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + orow + d) = f32x4{v0, v1, v2, v3};
         } else {
           *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.dk) + orow + d) = u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)};
-          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.dv) + orow + d) =
-              u32x2{pack_bf16x2(dvacc[db][4 * i4], dvacc[db][4 * i4 + 1]),
-                    pack_bf16x2(dvacc[db][4 * i4 + 2], dvacc[db][4 * i4 + 3])};
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.dv) + orow + d) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
       }
     }
@@ -261,11 +258,12 @@ struct DqKernel {
   static constexpr int NDB = D / 32;
   static constexpr int ROWB = 2 * D;
 
-  // One 32-key block of the tile against this wave's 32 queries.
+  // One 32-key block of the tile against this wave's 32 queries.  [jlo, jhi]:
+  // keys this lane's query may see.
   template <bool MASK>
   static __device__ __forceinline__ void block(const uint8_t* kl, const uint8_t* vl, int kb, const u32x4* qreg,
-                                               const u32x4* doreg, f32x16* dqacc, int lane, int n0, int ip,
-                                               int lk, const BwdArgs& a) {
+                                               const u32x4* doreg, f32x16* dqacc, int lane, int n0, int jlo,
+                                               int jhi, const BwdArgs& a) {
     const int hf = lane >> 5;
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -273,7 +271,9 @@ struct DqKernel {
       sacc = mfma_bf16(row_operand<ROWB>(kl, kb * 32, 2 * s, lane), qreg[s], sacc);
       dpacc = mfma_bf16(row_operand<ROWB>(vl, kb * 32, 2 * s, lane), doreg[s], dpacc);
     }
-    // accumulator element r: key n0 + kb*32 + 4hf + 8(r/4) + r%4, query ip - off
+    // accumulator element r: key n0 + kb*32 + 4hf + 8(r/4) + r%4, this lane's query
+    const int base = n0 + kb * 32 + hf * 4;
+    const int lo = jlo - base, hi = jhi - base;
     u32x4 dsh[2], dsl[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -284,15 +284,9 @@ struct DqKernel {
         for (int u = 0; u < 2; ++u) {
           const int r = 8 * t + 2 * w + u;
           float dy;
-          (void)Act<ACT>::f_df(sacc[r] * a.scale, a.act_param, dy);
+          (void)Act<ACT>::f_df(sacc[r], a.act, dy);
           float ds = dpacc[r] * dy;
-          if constexpr (MASK) {
-            const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
-            bool ok = j < lk;
-            if (a.wl >= 0) ok = ok && j >= ip - a.wl;
-            if (a.wr >= 0) ok = ok && j <= ip + a.wr;
-            ds = ok ? ds : 0.0f;
-          }
+          if constexpr (MASK) ds = in_range(r, lo, hi) ? ds : 0.0f;
           dsv[u] = ds;
         }
         dsh[t][w] = pack_bf16x2(dsv[0], dsv[1]);
@@ -349,6 +343,9 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   const bool wave_active = q0w < lq;
   const int qmax_w = min(q0w + 31, lq - 1);
   const int qi = q0w + (lane & 31);
+  // keys this lane's query may see: [jlo, jhi]
+  const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
+  const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
   const long q_ld = (long)a.hq * D;
   u32x4 qreg[KS], doreg[KS];
@@ -379,22 +376,22 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
     const int n0 = nb * BN;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int jlo = n0 + kb * 32, jhi = jlo + 31;
-      if (jlo >= lk) break;
-      bool empty = false, full = jhi < lk;
+      const int b_lo = n0 + kb * 32, b_hi = b_lo + 31;  // keys of this 32-key block
+      if (b_lo >= lk) break;
+      bool empty = false, full = b_hi < lk;
       if (a.wr >= 0) {
-        empty |= jlo > qmax_w + off + a.wr;
-        full &= jhi <= q0w + off + a.wr;
+        empty |= b_lo > qmax_w + off + a.wr;
+        full &= b_hi <= q0w + off + a.wr;
       }
       if (a.wl >= 0) {
-        empty |= jhi < q0w + off - a.wl;
-        full &= jlo >= qmax_w + off - a.wl;
+        empty |= b_hi < q0w + off - a.wl;
+        full &= b_lo >= qmax_w + off - a.wl;
       }
       if (empty) continue;
       if (full)
-        K::template block<false>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, qi + off, lk, a);
+        K::template block<false>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, 0, 0, a);
       else
-        K::template block<true>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, qi + off, lk, a);
+        K::template block<true>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, jlo, jhi, a);
     }
   };
 
@@ -420,8 +417,9 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
-        const float x0 = dqacc[db][4 * i4] * a.scale, x1 = dqacc[db][4 * i4 + 1] * a.scale;
-        const float x2 = dqacc[db][4 * i4 + 2] * a.scale, x3 = dqacc[db][4 * i4 + 3] * a.scale;
+        const float gs = a.act.gscale;
+        const float x0 = dqacc[db][4 * i4] * gs, x1 = dqacc[db][4 * i4 + 1] * gs;
+        const float x2 = dqacc[db][4 * i4 + 2] * gs, x3 = dqacc[db][4 * i4 + 3] * gs;
         if (a.out_f32)
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.dq) + orow + d) = f32x4{x0, x1, x2, x3};
         else

@@ -36,163 +36,151 @@ __device__ __forceinline__ f32x16 mfma_fp8(const u32x2& a, const u32x2& b, const
                                                     __builtin_bit_cast(long, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// bf16 remainder of a packed pair: lo = bf16(x - float(hi)).
+__device__ __forceinline__ uint32_t split_lo(float x0, float x1, uint32_t hi) {
+  return pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ----------------------------------------------------------------- activations
-// act(x) and act'(x) in fp32.  Exponentials use v_exp_f32 (2^x) and v_rcp_f32;
-// both are accurate to about 1 ulp, far below the bf16 rounding applied to P.
-// tanh-GELU uses 0.5 x (1 + tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3).
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSqrt2OverPi = 0.7978845608028654f;
-constexpr float kGeluC = 0.044715f;
-constexpr float kInvSqrt2 = 0.7071067811865476f;
-constexpr float kInvSqrt2Pi = 0.3989422804014327f;
-
+// With c the score scale and s the raw dot product, y(s) satisfies
+// act(c s) = pscale * y(s) and d(s) = act'(c s) (constants in ActConsts, set
+// on the host from c).  Folding c into the constants removes the per-score
+// multiply; pscale and the chain-rule c are applied once per output element.
+// Exponentials use v_exp_f32 (2^x) and v_rcp_f32, both accurate to ~1 ulp,
+// far below the bf16 rounding applied to P.  tanh-GELU is evaluated as
+// x sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3), since 0.5(1 + tanh u) =
+// sigmoid(2u).
+//   IDENTITY   y = s                          pscale = c   d = 1
+//   GELU       y = s (1 + erf(k0 s))          pscale = c/2 d = (1 + erf(k0 s))/2 + a0 s 2^(a1 s^2)
+//   GELU_TANH  r = 1/(1 + 2^(s (k0 + k1 s^2))), y = s r, pscale = c,
+//              d = r + r (1 - r) s (a0 + a1 s^2)
+//   RELU       y = max(k0 s, 0)               pscale = 1   d = [k0 s > 0]
+//   RELU2      y = max(k0 s, 0)^2             pscale = 1   d = 2 max(k0 s, 0)
+//   LEAKY      x = k0 s, y = x >= 0 ? x : alpha x, pscale = 1, d = x > 0 ? 1 : alpha
+//   SILU       r = 1/(1 + 2^(k0 s)), y = s r, pscale = c, d = r + r (1 - r) a0 s
+//   HARDSWISH  y = s clamp(k0 s + 3, 0, 6)    pscale = c/6 d = x < -3 ? 0 : x > 3 ? 1 : x/3 + 1/2 (x = k0 s)
 template <int ACT>
 struct Act;
 
 template <>
 struct Act<ACT_IDENTITY> {
-  static __device__ __forceinline__ float f(float x, float) { return x; }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) { df = 1.0f; return x; }
+  static __device__ __forceinline__ float f(float s, const ActConsts&) { return s; }
+  static __device__ __forceinline__ float f_df(float s, const ActConsts&, float& d) { d = 1.0f; return s; }
 };
 
 template <>
 struct Act<ACT_RELU> {
-  static __device__ __forceinline__ float f(float x, float) { return fmaxf(x, 0.0f); }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    df = x > 0.0f ? 1.0f : 0.0f;
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) { return fmaxf(k.k0 * s, 0.0f); }
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float x = k.k0 * s;
+    d = x > 0.0f ? 1.0f : 0.0f;
     return fmaxf(x, 0.0f);
   }
 };
 
 template <>
 struct Act<ACT_RELU2> {
-  static __device__ __forceinline__ float f(float x, float) { float r = fmaxf(x, 0.0f); return r * r; }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    float r = fmaxf(x, 0.0f);
-    df = 2.0f * r;
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    const float r = fmaxf(k.k0 * s, 0.0f);
+    return r * r;
+  }
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float r = fmaxf(k.k0 * s, 0.0f);
+    d = 2.0f * r;
     return r * r;
   }
 };
 
 template <>
 struct Act<ACT_LEAKY> {
-  static __device__ __forceinline__ float f(float x, float a) { return x >= 0.0f ? x : a * x; }
-  static __device__ __forceinline__ float f_df(float x, float a, float& df) {
-    df = x > 0.0f ? 1.0f : a;
-    return x >= 0.0f ? x : a * x;
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    const float x = k.k0 * s;
+    return x >= 0.0f ? x : k.alpha * x;
+  }
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float x = k.k0 * s;
+    d = x > 0.0f ? 1.0f : k.alpha;
+    return x >= 0.0f ? x : k.alpha * x;
   }
 };
 
 template <>
 struct Act<ACT_SILU> {
-  static __device__ __forceinline__ float f(float x, float) {
-    return x * fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    return s * fast_rcp(1.0f + fast_exp2(k.k0 * s));
   }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    float s = fast_rcp(1.0f + fast_exp2(-kLog2e * x));
-    df = s * (1.0f + x * (1.0f - s));
-    return x * s;
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float r = fast_rcp(1.0f + fast_exp2(k.k0 * s));
+    d = __builtin_fmaf(r * (1.0f - r), k.a0 * s, r);
+    return s * r;
   }
 };
 
 template <>
 struct Act<ACT_GELU_TANH> {
-  // sigmoid(2u) = 1 / (1 + 2^(x * (c0 + c1 x^2)))
-  static constexpr float c0 = -2.0f * kSqrt2OverPi * kLog2e;
-  static constexpr float c1 = c0 * kGeluC;
-  static __device__ __forceinline__ float f(float x, float) {
-    float t = x * __builtin_fmaf(c1, x * x, c0);
-    return x * fast_rcp(1.0f + fast_exp2(t));
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    return s * fast_rcp(1.0f + fast_exp2(s * __builtin_fmaf(k.k1, s * s, k.k0)));
   }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    float x2 = x * x;
-    float s = fast_rcp(1.0f + fast_exp2(x * __builtin_fmaf(c1, x2, c0)));
-    // d/dx x s(2u) = s + x s (1 - s) 2 u',  2u' = 2 sqrt(2/pi) (1 + 3 c x^2)
-    float du2 = 2.0f * kSqrt2OverPi * __builtin_fmaf(3.0f * kGeluC, x2, 1.0f);
-    df = __builtin_fmaf(x * s * (1.0f - s), du2, s);
-    return x * s;
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float s2 = s * s;
+    const float r = fast_rcp(1.0f + fast_exp2(s * __builtin_fmaf(k.k1, s2, k.k0)));
+    d = __builtin_fmaf(r * (1.0f - r), s * __builtin_fmaf(k.a1, s2, k.a0), r);
+    return s * r;
   }
 };
 
 template <>
 struct Act<ACT_GELU> {
-  static __device__ __forceinline__ float f(float x, float) { return 0.5f * x * (1.0f + erff(x * kInvSqrt2)); }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    float cdf = 0.5f * (1.0f + erff(x * kInvSqrt2));
-    df = __builtin_fmaf(x * kInvSqrt2Pi, fast_exp2(-0.5f * kLog2e * x * x), cdf);
-    return x * cdf;
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) { return s * (1.0f + erff(k.k0 * s)); }
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float e = 1.0f + erff(k.k0 * s);
+    d = __builtin_fmaf(k.a0 * s, fast_exp2(k.a1 * s * s), 0.5f * e);
+    return s * e;
   }
 };
 
 template <>
 struct Act<ACT_HARDSWISH> {
-  static __device__ __forceinline__ float f(float x, float) {
-    return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    return s * fminf(fmaxf(__builtin_fmaf(k.k0, s, 3.0f), 0.0f), 6.0f);
   }
-  static __device__ __forceinline__ float f_df(float x, float, float& df) {
-    df = x < -3.0f ? 0.0f : (x > 3.0f ? 1.0f : __builtin_fmaf(x, 1.0f / 3.0f, 0.5f));
-    return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+  static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
+    const float x = k.k0 * s;
+    d = x < -3.0f ? 0.0f : (x > 3.0f ? 1.0f : __builtin_fmaf(x, 1.0f / 3.0f, 0.5f));
+    return s * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f);
   }
 };
 
-// ------------------------------------------------------------- LDS tile layouts
-// Row tile: [rows][D] bf16 (row = key or query), 16-byte chunks XOR-swizzled by
-// (row & 7) so that 8 consecutive rows read at one chunk hit distinct banks.
-template <int D>
-__device__ __forceinline__ int row_tile_off(int row, int chunk) {  // in bf16 elements
-  return row * D + ((chunk ^ (row & 7)) << 3);
+// Element-wise mask of a 32x32 accumulator block: element r sits at offset
+// c_r = 8 (r/4) + r%4 (plus a lane-dependent base) along the accumulator rows;
+// it is kept iff lo <= c_r <= hi, where lo/hi are the allowed range relative to
+// that base (two compares and one select per element).
+__device__ __forceinline__ bool in_range(int r, int lo, int hi) {
+  const int c = 8 * (r >> 2) + (r & 3);
+  return c >= lo && c <= hi;
 }
 
-// FP8 row tile: [rows][D] bytes, 8-byte units swizzled for conflict-free
-// ds_read_b64 of 16 consecutive rows.
-template <int D>
-__device__ __forceinline__ int row_tile8_off(int row, int unit) {  // in bytes
-  constexpr int kShift = (D == 64) ? 1 : 0;
-  return row * D + ((unit ^ ((row >> kShift) & (D / 8 - 1))) << 3);
-}
-
-// Transposed tile: [D][NCOL] bf16, row = head-dim index d, columns = NCOL keys
-// (or queries) in "accumulator order": within every 32-column block, logical
-// 16-byte chunk 2*t + hf holds columns 16 t + 8 (p/4) + 4 hf + p%4, p = 0..7.
-// Chunks are XOR-swizzled within their 128-byte bank sweep: by
-// ((d ^ (d >> 3)) & 7) for rows of >= 64 columns, by (((d >> 1) ^ (d >> 3)) & 3)
-// for 32-column rows (two rows per sweep).  Reads of 8 consecutive rows at one
-// chunk are conflict-free; the transposing writes (rows 8c + e) are <= 4-way.
-__device__ __forceinline__ int tr_chunk_of(int col) {  // logical chunk of column col
-  int kk = col & 31;
-  return ((col >> 5) << 2) + ((kk >> 4) << 1) + ((kk >> 2) & 1);
-}
-__device__ __forceinline__ int tr_pos_of(int col) {  // element position inside the chunk
-  int kk = col & 31;
-  return (((kk >> 3) & 1) << 2) + (kk & 3);
-}
-template <int NCOL>
-__device__ __forceinline__ int tr_tile_off(int d, int chunk) {  // in bf16 elements
-  static_assert(NCOL == 32 || NCOL == 64 || NCOL == 128, "transposed tile width");
-  const int swz = (NCOL == 32) ? (((d >> 1) ^ (d >> 3)) & 3) : ((d ^ (d >> 3)) & 7);
-  return d * NCOL + ((chunk ^ swz) << 3);
-}
-
+// ------------------------------------------------------------- global loads
 // Loads below are branch-free: an out-of-range row is redirected to row
 // nvalid-1 (callers guarantee nvalid >= 1) and its value replaced by zero with
 // a select.  Keeping every load unconditional lets the compiler count
 // outstanding loads exactly, so the prefetch of the next tile is not drained
-// (s_waitcnt vmcnt(0)) before the current tile's MFMAs.  The tile stagers
-// apply the select only when they write LDS, after the current tile's math,
-// so no instruction consumes the prefetched registers early.
+// (s_waitcnt vmcnt(0)) before the current tile's MFMAs.
 __device__ __forceinline__ u32x4 load16_or_zero(const void* p, bool valid) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(p);
   return valid ? v : u32x4{0u, 0u, 0u, 0u};
@@ -202,142 +190,18 @@ __device__ __forceinline__ u32x2 load8_or_zero(const void* p, bool valid) {
   return valid ? v : u32x2{0u, 0u};
 }
 
-// Stage a [NROW x D] bf16 tile from global memory (row stride `ld` elements,
-// rows at or beyond `nvalid` >= 1 read as zero) into registers: thread t owns
-// the 16-byte chunks t, t+256, ...
-template <int NROW, int D>
-struct RowTileRegs {
-  static constexpr int CPR = D / 8;                    // chunks per row
-  static constexpr int PER_THREAD = NROW * CPR / 256;
-  u32x4 r[PER_THREAD];
-  int nvalid;
-  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid_, int tid) {
-    nvalid = nvalid_;
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int c = tid + 256 * i;
-      int row = c / CPR, col = c % CPR;
-      r[i] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + col * 8);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int c = tid + 256 * i;
-      int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(row, col)) = row < nvalid ? r[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-};
-
-// Same for an FP8 tile ([NROW x D] bytes).
-template <int NROW, int D>
-struct RowTile8Regs {
-  static constexpr int CPR = D / 16;
-  static constexpr int PER_THREAD = NROW * CPR / 256;
-  u32x4 r[PER_THREAD];
-  int nvalid;
-  __device__ __forceinline__ void load(const uint8_t* base, long ld, int nvalid_, int tid) {
-    nvalid = nvalid_;
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int c = tid + 256 * i;
-      int row = c / CPR, col = c % CPR;
-      r[i] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + col * 16);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int c = tid + 256 * i;
-      int row = c / CPR, col = c % CPR;
-      const u32x4 v = row < nvalid ? r[i] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col)) = u32x2{v[0], v[1]};
-      *reinterpret_cast<u32x2*>(lds + row_tile8_off<D>(row, 2 * col + 1)) = u32x2{v[2], v[3]};
-    }
-  }
-};
-
-// Stage a [NROW x D] bf16 tile and store it transposed ([D][NROW], accumulator
-// column order).  Thread t owns 4 consecutive rows (4a..4a+3) of one 8-wide
-// column chunk cd; lanes with consecutive cd read one row contiguously.
-template <int NROW, int D>
-struct TrTileRegs {
-  static constexpr int CPR = D / 8;
-  static constexpr int GROUPS = (NROW / 4) * CPR;      // (4-row group, chunk) pairs
-  static constexpr int PER_THREAD = (GROUPS + 255) / 256;
-  u32x4 r[PER_THREAD][4];
-  int nvalid;
-  __device__ __forceinline__ void load(const __bf16* base, long ld, int nvalid_, int tid) {
-    nvalid = nvalid_;
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int g = tid + 256 * i;
-      int a = g / CPR, cd = g % CPR;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        int row = 4 * a + rr;
-        r[i][rr] = *reinterpret_cast<const u32x4*>(base + (long)min(row, nvalid - 1) * ld + cd * 8);
-      }
-    }
-  }
-  // zero the rows at or beyond nvalid (applied when writing LDS)
-  __device__ __forceinline__ u32x4 val(int i, int rr, int tid) const {
-    const int row = 4 * ((tid + 256 * i) / CPR) + rr;
-    return row < nvalid ? r[i][rr] : u32x4{0u, 0u, 0u, 0u};
-  }
-  // The same registers written as a row tile (row_tile_off layout).
-  __device__ __forceinline__ void store_rows(__bf16* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int g = tid + 256 * i;
-      if (GROUPS % 256 != 0 && g >= GROUPS) continue;
-      int a = g / CPR, cd = g % CPR;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<u32x4*>(lds + row_tile_off<D>(4 * a + rr, cd)) = val(i, rr, tid);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      int g = tid + 256 * i;
-      if (GROUPS % 256 != 0 && g >= GROUPS) continue;
-      int a = g / CPR, cd = g % CPR;
-      int col = 4 * a;
-      int chunk = tr_chunk_of(col);
-      int pos = tr_pos_of(col);
-      const u32x4 v0 = val(i, 0, tid), v1 = val(i, 1, tid), v2 = val(i, 2, tid), v3 = val(i, 3, tid);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int d = cd * 8 + e;
-        int w = e >> 1;
-        uint32_t x0 = v0[w], x1 = v1[w], x2 = v2[w], x3 = v3[w];
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (x0 >> 16) | (x1 & 0xffff0000u);
-          hi = (x2 >> 16) | (x3 & 0xffff0000u);
-        } else {
-          lo = (x0 & 0xffffu) | (x1 << 16);
-          hi = (x2 & 0xffffu) | (x3 << 16);
-        }
-        *reinterpret_cast<u32x2*>(lds + tr_tile_off<NROW>(d, chunk) + pos) = u32x2{lo, hi};
-      }
-    }
-  }
-};
-
-
 // ------------------------------------------------- direct HBM -> LDS row tiles
 // Row-major [rows][ROWB bytes] tiles written by global_load_lds_dwordx4: each
 // lane's 16 bytes land at (LDS base of the instruction) + 16 * lane, so the
 // chunk swizzle is chosen by picking which source chunk each lane fetches.
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte chunk swizzle of a row-major LDS row tile.
+// Chunk swizzle f(row) for rows of >= 128 bytes: f maps rows 8m..8m+7 onto
+// distinct chunks (row-wise 16-byte reads of 8 consecutive rows are
+// conflict-free) and rows 4m..4m+3 onto distinct chunk pairs (the 4 rows x
+// 32 bytes a 16-lane group touches in a transposing read cover all 32 banks).
+// 64-byte rows (FP8 K at D = 64) pair rows per bank sweep instead.
 template <int ROWB>
 __device__ __forceinline__ int chunk_swz(int row) {
-  return (ROWB >= 128) ? (row & 7) : ((row >> 1) & 3);  // 64-byte rows: two rows per bank sweep
+  return (ROWB >= 128) ? (((row & 3) << 1) | ((row >> 2) & 1)) : ((row >> 1) & 3);
 }
 template <int ROWB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk

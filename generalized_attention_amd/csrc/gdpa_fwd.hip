@@ -44,8 +44,8 @@ struct FwdKernel {
   // window / key-tail mask element-wise.
   template <bool MASK>
   static __device__ __forceinline__ void tile(const uint8_t* kl, const uint8_t* vl, const u32x4* qreg,
-                                              const u32x2* qreg8, f32x16* oacc, int lane, int n0, int ip,
-                                              int lk, const FwdArgs& a) {
+                                              const u32x2* qreg8, f32x16* oacc, int lane, int n0, int jlo,
+                                              int jhi, const FwdArgs& a) {
     const int hf = lane >> 5;
     f32x16 sacc[NKB];
 #pragma unroll
@@ -66,6 +66,9 @@ struct FwdKernel {
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      // allowed keys of this lane relative to the block's first key for this lane
+      const int base = n0 + kb * 32 + hf * 4;
+      const int lo = jlo - base, hi = jhi - base;
       u32x4 phi[2], plo[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -75,19 +78,13 @@ struct FwdKernel {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * t + 2 * w + u;
-            float v = Act<ACT>::f(sacc[kb][r] * a.s_scale, a.act_param);
-            if constexpr (MASK) {
-              const int j = n0 + kb * 32 + hf * 4 + 8 * (r >> 2) + (r & 3);
-              bool ok = j < lk;
-              if (a.wl >= 0) ok = ok && j >= ip - a.wl;
-              if (a.wr >= 0) ok = ok && j <= ip + a.wr;
-              v = ok ? v : 0.0f;
-            }
+            float v = Act<ACT>::f(sacc[kb][r], a.act);
+            if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
             y[u] = v;
           }
-          const uint32_t hi = pack_bf16x2(y[0], y[1]);
-          phi[t][w] = hi;
-          if constexpr (PSPLIT) plo[t][w] = pack_bf16x2(y[0] - bf16_lo_to_f32(hi), y[1] - bf16_hi_to_f32(hi));
+          const uint32_t hi2 = pack_bf16x2(y[0], y[1]);
+          phi[t][w] = hi2;
+          if constexpr (PSPLIT) plo[t][w] = split_lo(y[0], y[1], hi2);
         }
       }
       // V^T operand straight from the row-major V tile (transpose read).
@@ -152,6 +149,9 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
   const int qmax_w = min(q0w + 31, lq - 1);
   const int qi = q0w + (lane & 31);
   const int hf = lane >> 5;
+  // keys this lane's query may see: [jlo, jhi]
+  const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
+  const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step.
   const long q_ld = (long)a.hq * D;
@@ -196,9 +196,9 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
     }
     if (!wave_active || empty) return;
     if (full)
-      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, qi + off, lk, a);
+      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, 0, 0, a);
     else
-      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, qi + off, lk, a);
+      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, a);
   };
 
   if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
@@ -224,14 +224,13 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
-        if (a.out_f32) {
-          f32x4 val{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3]};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = val;
-        } else {
-          u32x2 val{pack_bf16x2(oacc[db][4 * i4], oacc[db][4 * i4 + 1]),
-                    pack_bf16x2(oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3])};
-          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d) = val;
-        }
+        const float ps = a.act.pscale;
+        const float o0 = oacc[db][4 * i4] * ps, o1 = oacc[db][4 * i4 + 1] * ps;
+        const float o2 = oacc[db][4 * i4 + 2] * ps, o3 = oacc[db][4 * i4 + 3] * ps;
+        if (a.out_f32)
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = f32x4{o0, o1, o2, o3};
+        else
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
       }
     }
   }

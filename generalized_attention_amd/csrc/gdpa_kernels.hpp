@@ -20,6 +20,18 @@ enum ActKind : int {
 };
 
 
+// Activation constants with the score scale folded in (computed on the host).
+// With c = scale (times the FP8 descales) and s the raw dot product q.k, the
+// kernels evaluate y(s) such that act(c s) = pscale * y(s), and d(s) =
+// act'(c s); the chain-rule factor c of dQ and dK is applied once, as gscale,
+// to the accumulators.  k0, k1, a0, a1 are per-activation (see gdpa_common.hpp).
+struct ActConsts {
+  float k0, k1, a0, a1;
+  float alpha;    // LeakyReLU slope
+  float pscale;   // act(c s) = pscale * y(s)
+  float gscale;   // = c
+};
+
 // One forward launch.  Sequence b of a jagged batch owns query rows
 // cu_q[b]..cu_q[b+1]-1 and key rows cu_k[b]..cu_k[b+1]-1; with cu_q == nullptr
 // the batch is fixed-length (lq_fixed / lk_fixed rows per sequence).
@@ -37,8 +49,7 @@ struct FwdArgs {
   int32_t hkv;
   int32_t group;      // hq / hkv
   int32_t mblocks;    // ceil(max_seqlen_q / 128)
-  float s_scale;      // scale * q_descale * k_descale
-  float act_param;
+  ActConsts act;      // activation constants (c = scale * q_descale * k_descale)
   int32_t wl;         // window left  (-1: unbounded)
   int32_t wr;         // window right (-1: unbounded)
   int32_t out_f32;    // 1: fp32 output, 0: bf16
@@ -64,8 +75,7 @@ struct BwdArgs {
   int32_t group;
   int32_t mblocks;    // dQ kernel: ceil(max_seqlen_q / 128)
   int32_t nblocks;    // dK/dV kernel: ceil(max_seqlen_k / 128)
-  float scale;
-  float act_param;
+  ActConsts act;      // activation constants (c = scale)
   int32_t wl;
   int32_t wr;
   int32_t out_f32;
