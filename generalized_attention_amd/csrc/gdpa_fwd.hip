@@ -66,6 +66,13 @@ struct FwdKernel {
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      // V^T operands of this 32-key block, read (transposed) from the row-major
+      // V tile before the activation so the LDS latency hides behind it.
+      bf16x8 vop[2][NDB];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vop[t][db] = tr_operand<VROWB>(vl, kb * 32 + 16 * t, db * 32, lane);
       // allowed keys of this lane relative to the block's first key for this lane
       const int base = n0 + kb * 32 + hf * 4;
       const int lo = jlo - base, hi = jhi - base;
@@ -87,15 +94,13 @@ struct FwdKernel {
           if constexpr (PSPLIT) plo[t][w] = split_lo(y[0], y[1], hi2);
         }
       }
-      // V^T operand straight from the row-major V tile (transpose read).
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 aop = tr_operand<VROWB>(vl, kb * 32 + 16 * t, db * 32, lane);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, phi[t]), oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, phi[t]), oacc[db], 0, 0, 0);
           if constexpr (PSPLIT)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, __builtin_bit_cast(bf16x8, plo[t]), oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, plo[t]), oacc[db], 0, 0, 0);
         }
       }
     }
