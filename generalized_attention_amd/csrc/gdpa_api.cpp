@@ -18,7 +18,8 @@ namespace {
 using gdpa::BwdArgs;
 using gdpa::FwdArgs;
 
-constexpr int64_t kMaxGrid = 2147483647LL;
+// A dispatch packet counts work-items in 32 bits: at most 2^32 - 1 threads of 256.
+constexpr int64_t kMaxGrid = ((1LL << 32) - 1) / 256;
 
 bool debug_log() {
   static const bool on = [] {
@@ -160,7 +161,6 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kFwdBM - 1) / gdpa::kFwdBM;
   if (mblocks == 0) return GDPA_OK;
-  if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
 
   FwdArgs a{};
   a.q = q;
@@ -184,10 +184,11 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   // no longer averages out; P is then carried as hi + lo (such short rows are
   // bandwidth-bound, so the second MFMA is free).
   a.psplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
+  if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
                  c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, (int)fp8, c.wl, c.wr,
-                 a.psplit, (long long)(c.batch * c.hq * mblocks));
+                 a.psplit, (long long)gdpa::fwd_grid(a));
   return hip_status(gdpa::launch_fwd(a, c.d, c.act_kind, fp8, static_cast<hipStream_t>(stream)),
                     "forward launch");
 }

@@ -211,15 +211,15 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of 
 // Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile.  Rows at or
 // beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks the
 // matching keys, so the duplicated rows never contribute.
-template <int NROW, int ROWB>
+template <int NROW, int ROWB, int NWAVES = 4>
 __device__ __forceinline__ void stage_tile(const uint8_t* g, long ld_bytes, int nvalid, uint8_t* lds, int wave,
                                            int lane) {
   constexpr int U = ROWB / 16;                // 16-byte units per row
-  constexpr int NI = NROW * U / 256;          // instructions per wave
-  static_assert(NROW * U % 256 == 0, "tile must be a multiple of 4 KiB");
+  constexpr int NI = NROW * U / (64 * NWAVES);  // instructions per wave
+  static_assert(NROW * U % (64 * NWAVES) == 0, "tile must be a multiple of NWAVES KiB");
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int blk = i * 4 + wave;             // 1 KiB block of LDS written by this instruction
+    const int blk = i * NWAVES + wave;        // 1 KiB block of LDS written by this instruction
     const int p = blk * 64 + lane;            // destination unit
     const int row = p / U, pc = p % U;
     const int c = pc ^ chunk_swz<ROWB>(row);  // logical chunk stored at physical chunk pc

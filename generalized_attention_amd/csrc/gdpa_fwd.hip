@@ -6,21 +6,21 @@
 // partial sum to O: there is no running maximum, no rescaling and no final
 // division, unlike softmax flash attention.
 //
-// Work decomposition: one workgroup (4 waves, two workgroups per CU) per
-// (sequence, query head, 128-row query block); wave w owns query rows
-// 32w..32w+31.  Per KV tile of BN = 8192/D keys:
+// Work decomposition: one workgroup of NW waves per (sequence, query head,
+// BM-row query block), BM = 32 * NQB * NW; wave w owns NQB blocks of 32 query
+// rows.  Per KV tile of BN = 8192/D keys:
 //   * K and V are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //     staging), row-major with 16-byte chunks XOR-swizzled by the row index;
 //     tiles are double-buffered, the next tile's copy is in flight while the
 //     current tile is computed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (Q^T stays in registers as the B
-//     operand for the whole loop), then scale, mask and activation in
-//     registers;
+//     operand for the whole loop; each K operand read from LDS feeds the NQB
+//     query blocks), then scale, mask and activation in registers;
 //   * P^T is packed to bf16 straight from the accumulators and is the B
 //     operand of O^T += V^T P^T.  The V^T operand comes from the row-major V
 //     tile through ds_read_b64_tr_b16, whose 16-lane transpose hands each lane
 //     4 consecutive keys of one head-dim column, in exactly the key order of
-//     the accumulator rows.
+//     the accumulator rows; each V^T operand also feeds the NQB query blocks.
 // Query blocks are dispatched last-block-first: for self-attention the late
 // blocks exist only in long sequences and carry the most KV tiles, so the
 // hardware dispatcher sees roughly longest-processing-time-first order (the
@@ -30,26 +30,31 @@
 
 namespace gdpa {
 
-template <int D, int ACT, bool FP8, bool PSPLIT>
+template <int D, int ACT, bool FP8, bool PSPLIT, int NW, int NQB>
 struct FwdKernel {
-  static constexpr int BM = kFwdBM;
+  static constexpr int BM = 32 * NQB * NW;
   static constexpr int BN = 8192 / D;     // keys per KV tile
   static constexpr int NKB = BN / 32;     // 32-key blocks per tile
   static constexpr int KS = D / 16;       // k-steps of Q K^T
   static constexpr int NDB = D / 32;      // 32-row blocks of O^T
   static constexpr int KROWB = FP8 ? D : 2 * D;
   static constexpr int VROWB = 2 * D;
+  static constexpr int NQR = FP8 ? 1 : KS;   // bf16 Q registers per query block
+  static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers per query block
 
-  // S^T for one tile, activation, and O^T += V^T P^T.  MASK: apply the
-  // window / key-tail mask element-wise.
+  // One KV tile for this wave: S^T = K Q^T, P = act(S) (masked to each
+  // lane's [jlo, jhi] when MASK), O^T += V^T P^T.  qact: query blocks with at
+  // least one valid row.
   template <bool MASK>
-  static __device__ __forceinline__ void tile(const uint8_t* kl, const uint8_t* vl, const u32x4* qreg,
-                                              const u32x2* qreg8, f32x16* oacc, int lane, int n0, int jlo,
-                                              int jhi, const FwdArgs& a) {
+  static __device__ __forceinline__ void tile(const uint8_t* kl, const uint8_t* vl, const u32x4 (*qreg)[NQR],
+                                              const u32x2 (*qreg8)[NQR8], f32x16 (*oacc)[NDB], int lane, int n0,
+                                              const int* jlo, const int* jhi, int qact, const FwdArgs& a) {
     const int hf = lane >> 5;
-    f32x16 sacc[NKB];
+    f32x16 sacc[NQB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[qb][kb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -57,10 +62,14 @@ struct FwdKernel {
         const int row = kb * 32 + (lane & 31);
         if constexpr (FP8) {
           const u32x2 aop = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(row, s) + hf * 8);
-          sacc[kb] = mfma_fp8(aop, qreg8[s], sacc[kb]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            if (qb < qact) sacc[qb][kb] = mfma_fp8(aop, qreg8[qb][s], sacc[qb][kb]);
         } else {
           const u32x4 aop = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, 2 * s + hf));
-          sacc[kb] = mfma_bf16(aop, qreg[s], sacc[kb]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            if (qb < qact) sacc[qb][kb] = mfma_bf16(aop, qreg[qb][s], sacc[qb][kb]);
         }
       }
     }
@@ -73,43 +82,49 @@ struct FwdKernel {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) vop[t][db] = tr_operand<VROWB>(vl, kb * 32 + 16 * t, db * 32, lane);
-      // allowed keys of this lane relative to the block's first key for this lane
-      const int base = n0 + kb * 32 + hf * 4;
-      const int lo = jlo - base, hi = jhi - base;
-      u32x4 phi[2], plo[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (qb >= qact) continue;
+        // allowed keys of this lane relative to the block's first key for this lane
+        const int base = n0 + kb * 32 + hf * 4;
+        const int lo = jlo[qb] - base, hi = jhi[qb] - base;
+        u32x4 phi[2], plo[2];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float y[2];
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * t + 2 * w + u;
-            float v = Act<ACT>::f(sacc[kb][r], a.act);
-            if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
-            y[u] = v;
+          for (int w = 0; w < 4; ++w) {
+            float y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * t + 2 * w + u;
+              float v = Act<ACT>::f(sacc[qb][kb][r], a.act);
+              if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
+              y[u] = v;
+            }
+            const uint32_t hi2 = pack_bf16x2(y[0], y[1]);
+            phi[t][w] = hi2;
+            if constexpr (PSPLIT) plo[t][w] = split_lo(y[0], y[1], hi2);
           }
-          const uint32_t hi2 = pack_bf16x2(y[0], y[1]);
-          phi[t][w] = hi2;
-          if constexpr (PSPLIT) plo[t][w] = split_lo(y[0], y[1], hi2);
         }
-      }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, phi[t]), oacc[db], 0, 0, 0);
-          if constexpr (PSPLIT)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, plo[t]), oacc[db], 0, 0, 0);
+          for (int db = 0; db < NDB; ++db) {
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, phi[t]),
+                                                                   oacc[qb][db], 0, 0, 0);
+            if constexpr (PSPLIT)
+              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, plo[t]),
+                                                                     oacc[qb][db], 0, 0, 0);
+          }
         }
       }
     }
   }
 };
 
-template <int D, int ACT, bool FP8, bool PSPLIT>
-__global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
-  using K = FwdKernel<D, ACT, FP8, PSPLIT>;
+template <int D, int ACT, bool FP8, bool PSPLIT, int NW, int NQB>
+__global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
+  using K = FwdKernel<D, ACT, FP8, PSPLIT, NW, NQB>;
   constexpr int BM = K::BM, BN = K::BN, KS = K::KS, NDB = K::NDB;
   constexpr int KBYTES = BN * K::KROWB, VBYTES = BN * K::VROWB;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KBYTES];
@@ -120,11 +135,25 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int idx = blockIdx.x;
-  const int h = idx % a.hq;
-  idx /= a.hq;
-  const int b = idx % a.batch;
-  const int m = a.mblocks - 1 - idx / a.batch;
+  // Block -> work mapping.  The dispatcher deals consecutive workgroup ids to
+  // the 8 XCDs in turn, and each XCD has its own L2.  All workgroups that read
+  // one (sequence, KV head) pair -- its query heads times its query blocks --
+  // go to one XCD back to back, so each K/V tile is fetched into that L2 once
+  // and re-read there by the others while they walk the keys together.
+  // Within a pair, query blocks run last-first.
+  const int per_pair = a.group * a.mblocks;
+#if GDPA_FWD_XCD
+  const int xcd = blockIdx.x & (kNumXcd - 1), local = blockIdx.x / kNumXcd;
+  const int pair = (local / per_pair) * kNumXcd + xcd;
+  const int rest = local % per_pair;
+#else
+  const int pair = blockIdx.x / per_pair, rest = blockIdx.x % per_pair;
+#endif
+  if (pair >= a.batch * a.hkv) return;
+  const int b = pair / a.hkv;
+  const int g = pair % a.hkv;
+  const int h = g * a.group + rest / a.mblocks;
+  const int m = a.mblocks - 1 - rest % a.mblocks;
 
   int qs, lq, ks, lk;
   if (a.cu_q != nullptr) {
@@ -140,7 +169,6 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
   }
   const int row0 = m * BM;
   if (row0 >= lq) return;
-  const int g = h / a.group;
   const int off = lk - lq;  // bottom-right alignment of masks
   const int rlast = min(row0 + BM, lq) - 1;
   int j_lo = 0, j_hi = lk;
@@ -149,32 +177,43 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
   const int nb_begin = j_lo / BN;
   const int nb_end = (j_hi > j_lo) ? (j_hi + BN - 1) / BN : nb_begin;
 
-  const int q0w = row0 + wave * 32;
+  const int q0w = row0 + wave * 32 * NQB;  // first query row of this wave
   const bool wave_active = q0w < lq;
-  const int qmax_w = min(q0w + 31, lq - 1);
-  const int qi = q0w + (lane & 31);
+  const int qmax_w = min(q0w + 32 * NQB - 1, lq - 1);
+  const int qact = min(NQB, (lq - q0w + 31) / 32);  // query blocks with valid rows
   const int hf = lane >> 5;
-  // keys this lane's query may see: [jlo, jhi]
-  const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
-  const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
+  int qi[NQB], jlo[NQB], jhi[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    qi[qb] = q0w + qb * 32 + (lane & 31);
+    // keys this lane's query may see: [jlo, jhi]
+    jlo[qb] = a.wl >= 0 ? qi[qb] + off - a.wl : 0;
+    jhi[qb] = min(lk - 1, a.wr >= 0 ? qi[qb] + off + a.wr : lk - 1);
+  }
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step.
   const long q_ld = (long)a.hq * D;
-  u32x4 qreg[FP8 ? 1 : KS];
-  u32x2 qreg8[FP8 ? KS : 1];
-  if constexpr (FP8) {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
+  u32x4 qreg[NQB][K::NQR];
+  u32x2 qreg8[NQB][K::NQR8];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qreg8[s] = load8_or_zero(qp + s * 16, qi < lq);
-  } else {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const long qrow = (long)(qs + min(qi[qb], lq - 1)) * q_ld + h * D + hf * 8;
+    if constexpr (FP8) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
+      for (int s = 0; s < KS; ++s) qreg8[qb][s] = load8_or_zero(qp + s * 16, qi[qb] < lq);
+    } else {
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qreg[qb][s] = load16_or_zero(qp + s * 16, qi[qb] < lq);
+    }
   }
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[NQB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[qb][i] = f32x16{};
 
   const int esz = FP8 ? 1 : 2;
   const long kv_ld = (long)a.hkv * D;
@@ -183,8 +222,8 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
 
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile<BN, K::KROWB>(kbase + (long)n0 * kv_ld * esz, kv_ld * esz, lk - n0, kl, wave, lane);
-    stage_tile<BN, K::VROWB>(vbase + (long)n0 * kv_ld * 2, kv_ld * 2, lk - n0, vl, wave, lane);
+    stage_tile<BN, K::KROWB, NW>(kbase + (long)n0 * kv_ld * esz, kv_ld * esz, lk - n0, kl, wave, lane);
+    stage_tile<BN, K::VROWB, NW>(vbase + (long)n0 * kv_ld * 2, kv_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave; the mask is applied only where the
   // window cuts the tile or the tile runs past the last key.
@@ -201,9 +240,9 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
     }
     if (!wave_active || empty) return;
     if (full)
-      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, 0, 0, a);
+      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, qact, a);
     else
-      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, a);
+      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, qact, a);
   };
 
   if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
@@ -222,16 +261,19 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
   }
 
   // ---- epilogue: lane stores 4 consecutive head-dim values per register group
-  if (wave_active && qi < lq) {
-    const long orow = ((long)(qs + qi) * a.hq + h) * D;
+  if (!wave_active) return;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (qi[qb] >= lq) continue;
+    const long orow = ((long)(qs + qi[qb]) * a.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
         const float ps = a.act.pscale;
-        const float o0 = oacc[db][4 * i4] * ps, o1 = oacc[db][4 * i4 + 1] * ps;
-        const float o2 = oacc[db][4 * i4 + 2] * ps, o3 = oacc[db][4 * i4 + 3] * ps;
+        const float o0 = oacc[qb][db][4 * i4] * ps, o1 = oacc[qb][db][4 * i4 + 1] * ps;
+        const float o2 = oacc[qb][db][4 * i4 + 2] * ps, o3 = oacc[qb][db][4 * i4 + 3] * ps;
         if (a.out_f32)
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = f32x4{o0, o1, o2, o3};
         else
@@ -243,15 +285,14 @@ __global__ __launch_bounds__(256, 2) void gdpa_fwd_kernel(const FwdArgs a) {
 
 template <int D, bool FP8>
 static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t stream) {
-  const long grid = (long)a.batch * a.hq * a.mblocks;
-  dim3 g((unsigned)grid), blk(256);
+  dim3 g((unsigned)fwd_grid(a)), blk(64 * kFwdNW);
   switch (act_kind) {
-#define GDPA_FWD_CASE(K)                                                                   \
-  case K:                                                                                  \
-    if (a.psplit)                                                                          \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, true>), g, blk, 0, stream, a);        \
-    else                                                                                   \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, false>), g, blk, 0, stream, a);       \
+#define GDPA_FWD_CASE(K)                                                                                  \
+  case K:                                                                                                 \
+    if (a.psplit)                                                                                         \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, true, kFwdNW, kFwdNQB>), g, blk, 0, stream, a);      \
+    else                                                                                                  \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, false, kFwdNW, kFwdNQB>), g, blk, 0, stream, a);     \
     break;
     GDPA_FWD_CASE(ACT_IDENTITY)
     GDPA_FWD_CASE(ACT_GELU)

@@ -83,8 +83,27 @@ struct BwdArgs {
   int32_t kvsplit;    // 1: P and dS carried as bf16 hi/lo pairs in dV, dK
 };
 
-// Forward block of 4 waves covers 128 query rows.
-constexpr int kFwdBM = 128;
+// Forward workgroup shape: kFwdNW waves, each owning kFwdNQB blocks of 32 query rows.
+#ifndef GDPA_FWD_NW
+#define GDPA_FWD_NW 4
+#endif
+#ifndef GDPA_FWD_NQB
+#define GDPA_FWD_NQB 1
+#endif
+constexpr int kFwdNW = GDPA_FWD_NW, kFwdNQB = GDPA_FWD_NQB;
+constexpr int kFwdBM = 32 * kFwdNW * kFwdNQB;
+#ifndef GDPA_FWD_XCD
+#define GDPA_FWD_XCD 1
+#endif
+// XCDs per MI355X; workgroup ids are dealt to them round-robin.
+constexpr int kNumXcd = 8;
+
+// Forward grid: (sequence, KV head) pairs rounded up to a multiple of the XCD
+// count, times query heads per KV head, times query blocks.
+inline long fwd_grid(const FwdArgs& a) {
+  const long pairs = ((long)a.batch * a.hkv + kNumXcd - 1) / kNumXcd * kNumXcd;
+  return pairs * a.group * a.mblocks;
+}
 // Backward: dK/dV blocks cover 128 key rows, dQ blocks 128 query rows.
 constexpr int kBwdBN = 128;
 constexpr int kBwdBM = 128;
