@@ -185,6 +185,8 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   // bandwidth-bound, so the second MFMA is free).
   a.psplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
   if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
+  // The forward kernel addresses one sequence's K and V rows with 32-bit byte offsets.
+  if ((int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
                  c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, (int)fp8, c.wl, c.wr,
@@ -210,6 +212,9 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   if (c.batch == 0 || (c.total_q == 0 && c.total_k == 0)) return GDPA_OK;
   if (c.total_q > 0 && (q == nullptr || dout == nullptr)) return GDPA_ERR_INVALID_ARG;
   if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
+  // The backward kernels address one sequence's rows with 32-bit byte offsets.
+  if ((int64_t)c.max_lq * c.hq * c.d * 2 > INT32_MAX || (int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX)
+    return GDPA_ERR_UNSUPPORTED;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kBwdBM - 1) / gdpa::kBwdBM;
   const int64_t nblocks = ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN;
   if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid || (int64_t)c.batch * c.hkv * nblocks > kMaxGrid)

@@ -177,13 +177,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
     dvacc[i] = f32x16{};
   }
 
-  const long q_ld_b = (long)a.hq * D * 2;  // bytes per token row of q / dO
+  const int q_ld_b = a.hq * D * 2;  // bytes per token row of q / dO
+  // this sequence's q and dO rows (all heads); 32-bit offsets, bounded on the host
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(static_cast<const uint8_t*>(a.q) + (long)qs * q_ld_b, lq * q_ld_b);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(static_cast<const uint8_t*>(a.dout) + (long)qs * q_ld_b, lq * q_ld_b);
   auto stage = [&](int step, uint8_t* ql, uint8_t* dl) {
     const int h = g * a.group + step % a.group;
     const int m0 = (mb_begin + step / a.group) * BQ;
-    const long base = (long)(qs + m0) * q_ld_b + (long)h * D * 2;
-    stage_tile<BQ, ROWB>(static_cast<const uint8_t*>(a.q) + base, q_ld_b, lq - m0, ql, wave, lane);
-    stage_tile<BQ, ROWB>(static_cast<const uint8_t*>(a.dout) + base, q_ld_b, lq - m0, dl, wave, lane);
+    const int off = m0 * q_ld_b + h * D * 2;
+    stage_tile_buf<BQ, ROWB, 4>(qrs, off, q_ld_b, lq - m0, ql, wave, lane);
+    stage_tile_buf<BQ, ROWB, 4>(drs, off, q_ld_b, lq - m0, dl, wave, lane);
   };
   auto compute = [&](int step, const uint8_t* ql, const uint8_t* dl) {
     if (!wave_active) return;
@@ -366,10 +369,12 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   const long kv_ld_b = (long)a.hkv * D * 2;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (long)ks * kv_ld_b + (long)g * D * 2;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (long)ks * kv_ld_b + (long)g * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld_b);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile<BN, ROWB>(kbase + (long)n0 * kv_ld_b, kv_ld_b, lk - n0, kl, wave, lane);
-    stage_tile<BN, ROWB>(vbase + (long)n0 * kv_ld_b, kv_ld_b, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, ROWB, 4>(krs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, kl, wave, lane);
+    stage_tile_buf<BN, ROWB, 4>(vrs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, vl, wave, lane);
   };
   auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) {
     if (!wave_active) return;

@@ -191,7 +191,7 @@ __device__ __forceinline__ u32x2 load8_or_zero(const void* p, bool valid) {
 }
 
 // ------------------------------------------------- direct HBM -> LDS row tiles
-// Row-major [rows][ROWB bytes] tiles written by global_load_lds_dwordx4: each
+// Row-major [rows][ROWB bytes] tiles written by LDS-direct 16-byte loads: each
 // lane's 16 bytes land at (LDS base of the instruction) + 16 * lane, so the
 // chunk swizzle is chosen by picking which source chunk each lane fetches.
 // Chunk swizzle f(row) for rows of >= 128 bytes: f maps rows 8m..8m+7 onto
@@ -208,26 +208,33 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of 
   return row * ROWB + ((chunk ^ chunk_swz<ROWB>(row)) << 4);
 }
 
-// Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile.  Rows at or
-// beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks the
-// matching keys, so the duplicated rows never contribute.
-template <int NROW, int ROWB, int NWAVES = 4>
-__device__ __forceinline__ void stage_tile(const uint8_t* g, long ld_bytes, int nvalid, uint8_t* lds, int wave,
-                                           int lane) {
-  constexpr int U = ROWB / 16;                // 16-byte units per row
-  constexpr int NI = NROW * U / (64 * NWAVES);  // instructions per wave
+// Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile with
+// buffer_load_dwordx4 ... lds.  rsrc covers the rows of one sequence (see
+// make_rsrc); row0_off is the byte offset of the tile's first row in it.  Rows
+// at or beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks
+// the matching keys, so the duplicated rows never contribute.  (The FLAT form,
+// global_load_lds, would also work, but the compiler then treats LDS counters
+// as unordered and waits for lgkmcnt(0) before every later LDS read.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <int NROW, int ROWB, int NWAVES>
+__device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int row0_off, int ld_bytes, int nvalid,
+                                               uint8_t* lds, int wave, int lane) {
+  constexpr int U = ROWB / 16;
+  constexpr int NI = NROW * U / (64 * NWAVES);
   static_assert(NROW * U % (64 * NWAVES) == 0, "tile must be a multiple of NWAVES KiB");
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int blk = i * NWAVES + wave;        // 1 KiB block of LDS written by this instruction
-    const int p = blk * 64 + lane;            // destination unit
+    const int blk = i * NWAVES + wave;
+    const int p = blk * 64 + lane;
     const int row = p / U, pc = p % U;
-    const int c = pc ^ chunk_swz<ROWB>(row);  // logical chunk stored at physical chunk pc
-    const uint8_t* src = g + (long)min(row, nvalid - 1) * ld_bytes + c * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+    const int c = pc ^ chunk_swz<ROWB>(row);
+    const int voff = row0_off + min(row, nvalid - 1) * ld_bytes + c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
+                                             voff, 0, 0, 0);
   }
 }
-
 
 // Transposed MFMA A operand from a row-major bf16 row tile via
 // ds_read_b64_tr_b16.  Within each 16-lane group the instruction hands lane j
@@ -245,7 +252,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, int row_base, 
   for (int c = 0; c < 2; ++c) {
     const int row = row_base + 8 * c + 4 * (g >> 1) + (r >> 2);
     const int col = col_base + 16 * (g & 1) + 4 * (r & 3);
-    const uint8_t* p = tile + lds_off<ROWB>(row, col >> 3) + ((col & 4) << 1);
+    // one integer offset, one pointer step: a short pointer chain lets the
+    // compiler trace the read to its LDS array (and not drain unrelated
+    // in-flight LDS copies before it)
+    const uint8_t* p = tile + (lds_off<ROWB>(row, col >> 3) + ((col & 4) << 1));
     part[c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
   }
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);

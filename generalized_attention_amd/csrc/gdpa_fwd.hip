@@ -9,7 +9,7 @@
 // Work decomposition: one workgroup of NW waves per (sequence, query head,
 // BM-row query block), BM = 32 * NQB * NW; wave w owns NQB blocks of 32 query
 // rows.  Per KV tile of BN = 8192/D keys:
-//   * K and V are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//   * K and V are copied HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //     staging), row-major with 16-byte chunks XOR-swizzled by the row index;
 //     tiles are double-buffered, the next tile's copy is in flight while the
 //     current tile is computed;
@@ -142,13 +142,9 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   // and re-read there by the others while they walk the keys together.
   // Within a pair, query blocks run last-first.
   const int per_pair = a.group * a.mblocks;
-#if GDPA_FWD_XCD
   const int xcd = blockIdx.x & (kNumXcd - 1), local = blockIdx.x / kNumXcd;
   const int pair = (local / per_pair) * kNumXcd + xcd;
   const int rest = local % per_pair;
-#else
-  const int pair = blockIdx.x / per_pair, rest = blockIdx.x % per_pair;
-#endif
   if (pair >= a.batch * a.hkv) return;
   const int b = pair / a.hkv;
   const int g = pair % a.hkv;
@@ -220,10 +216,14 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)ks * kv_ld + g * D) * esz;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)ks * kv_ld + g * D) * 2;
 
+  // Byte ranges of this sequence's K and V rows (all KV heads), addressed by
+  // 32-bit offsets; the host keeps them below 2^31.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld * esz);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld * 2);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile<BN, K::KROWB, NW>(kbase + (long)n0 * kv_ld * esz, kv_ld * esz, lk - n0, kl, wave, lane);
-    stage_tile<BN, K::VROWB, NW>(vbase + (long)n0 * kv_ld * 2, kv_ld * 2, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, K::KROWB, NW>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0, kl, wave, lane);
+    stage_tile_buf<BN, K::VROWB, NW>(vrs, n0 * (int)kv_ld * 2, (int)kv_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave; the mask is applied only where the
   // window cuts the tile or the tile runs past the last key.

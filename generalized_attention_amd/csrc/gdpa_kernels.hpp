@@ -84,17 +84,8 @@ struct BwdArgs {
 };
 
 // Forward workgroup shape: kFwdNW waves, each owning kFwdNQB blocks of 32 query rows.
-#ifndef GDPA_FWD_NW
-#define GDPA_FWD_NW 4
-#endif
-#ifndef GDPA_FWD_NQB
-#define GDPA_FWD_NQB 1
-#endif
-constexpr int kFwdNW = GDPA_FWD_NW, kFwdNQB = GDPA_FWD_NQB;
+constexpr int kFwdNW = 4, kFwdNQB = 1;
 constexpr int kFwdBM = 32 * kFwdNW * kFwdNQB;
-#ifndef GDPA_FWD_XCD
-#define GDPA_FWD_XCD 1
-#endif
 // XCDs per MI355X; workgroup ids are dealt to them round-robin.
 constexpr int kNumXcd = 8;
 
