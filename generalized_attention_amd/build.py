@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdpa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_api.cpp"]
+SOURCES = ["gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched.hip", "gdpa_api.cpp"]
 ARCH = "gfx950"
 
 

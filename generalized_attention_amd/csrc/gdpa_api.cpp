@@ -143,12 +143,34 @@ gdpa_status_t hip_status(hipError_t e, const char* what) {
   return GDPA_ERR_HIP;
 }
 
+// Workspace of a jagged call: the longest-first sequence order (int32 per
+// sequence), built on the device before the main kernels.  Batches beyond
+// kSortMax keep index order and need no workspace.
+size_t schedule_bytes(int64_t batch) {
+  if (batch <= 0 || batch > gdpa::kSortMax) return 0;
+  return (size_t)((batch * 4 + 255) / 256 * 256);
+}
+
+// Builds the schedule into the workspace when this is a jagged call that has
+// one; *perm stays nullptr otherwise.
+gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, int32_t batch, void* workspace,
+                             size_t workspace_bytes, void* stream, const int32_t** perm) {
+  *perm = nullptr;
+  if (cu_q == nullptr) return GDPA_OK;
+  const size_t need = schedule_bytes(batch);
+  if (need == 0) return GDPA_OK;
+  if (workspace == nullptr || workspace_bytes < need) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  int32_t* p = static_cast<int32_t*>(workspace);
+  const gdpa_status_t st =
+      hip_status(gdpa::launch_schedule(cu_q, cu_k, batch, p, static_cast<hipStream_t>(stream)), "schedule launch");
+  if (st == GDPA_OK) *perm = p;
+  return st;
+}
+
 gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_q,
                       const int32_t* cu_k, const Common& c, float scale, float act_param,
                       int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale,
                       float k_descale, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (qk_dtype == GDPA_DTYPE_FP16 || v_dtype == GDPA_DTYPE_FP16 || out_dtype == GDPA_DTYPE_FP16)
     return GDPA_ERR_UNSUPPORTED;
   if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_INVALID_ARG;
@@ -187,6 +209,8 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
   // The forward kernel addresses one sequence's K and V rows with 32-bit byte offsets.
   if ((int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
+  gdpa_status_t sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm);
+  if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
                  c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, (int)fp8, c.wl, c.wr,
@@ -199,8 +223,6 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
                       void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (in_dtype == GDPA_DTYPE_FP8_E4M3 || in_dtype == GDPA_DTYPE_FP16 || grad_dtype == GDPA_DTYPE_FP16)
     return GDPA_ERR_UNSUPPORTED;
   if (in_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
@@ -217,7 +239,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
     return GDPA_ERR_UNSUPPORTED;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kBwdBM - 1) / gdpa::kBwdBM;
   const int64_t nblocks = ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN;
-  if ((int64_t)c.batch * c.hq * mblocks > kMaxGrid || (int64_t)c.batch * c.hkv * nblocks > kMaxGrid)
+  if (gdpa::pair_grid(c.batch, c.hkv, (long)(c.hq / c.hkv) * mblocks) > kMaxGrid ||
+      gdpa::pair_grid(c.batch, c.hkv, nblocks) > kMaxGrid)
     return GDPA_ERR_UNSUPPORTED;
 
   BwdArgs a{};
@@ -244,6 +267,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.out_f32 = grad_dtype == GDPA_DTYPE_FP32;
   a.dsplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
   a.kvsplit = few_terms(c.max_lq, a.group, c) ? 1 : 0;
+  gdpa_status_t sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm);
+  if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,
                  c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr);
@@ -318,9 +343,13 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
 }
 
 size_t gdpa_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
-size_t gdpa_varlen_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t, int32_t, int32_t, int32_t, int32_t) {
+  return schedule_bytes(batch);
+}
 size_t gdpa_bwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
-size_t gdpa_varlen_bwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t, int32_t, int32_t, int32_t, int32_t) {
+  return schedule_bytes(batch);
+}
 
 const char* gdpa_status_string(gdpa_status_t s) {
   switch (s) {

@@ -130,11 +130,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hf = lane >> 5;
-  int idx = blockIdx.x;
-  const int g = idx % a.hkv;
-  idx /= a.hkv;
-  const int b = idx % a.batch;
-  const int nblk = a.nblocks - 1 - idx / a.batch;
+  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // sequences first; within a pair, key blocks run last-first.
+  WorkItem w;
+  if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
+  const int g = w.g;
+  const int b = w.b;
+  const int nblk = a.nblocks - 1 - w.rest;
   int qs, lq, ks, lk;
   seq_bounds(a, b, qs, lq, ks, lk);
   const int n0 = nblk * BNB;
@@ -324,16 +326,18 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hf = lane >> 5;
-  int idx = blockIdx.x;
-  const int h = idx % a.hq;
-  idx /= a.hq;
-  const int b = idx % a.batch;
-  const int m = a.mblocks - 1 - idx / a.batch;
+  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // sequences first; within a pair, query blocks run last-first.
+  WorkItem w;
+  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
+  const int b = w.b;
+  const int h = w.g * a.group + w.rest / a.mblocks;
+  const int m = a.mblocks - 1 - w.rest % a.mblocks;
   int qs, lq, ks, lk;
   seq_bounds(a, b, qs, lq, ks, lk);
   const int row0 = m * BM;
   if (row0 >= lq) return;
-  const int g = h / a.group;
+  const int g = w.g;
   const int off = lk - lq;
   const int rlast = min(row0 + BM, lq) - 1;
   int j_lo = 0, j_hi = lk;
@@ -436,8 +440,8 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
 
 template <int D, bool SPLIT_KV, bool SPLIT_Q>
 static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
-  const long grid_kv = want_dkv ? (long)a.batch * a.hkv * a.nblocks : 0;
-  const long grid_q = want_dq ? (long)a.batch * a.hq * a.mblocks : 0;
+  const long grid_kv = want_dkv ? pair_grid(a.batch, a.hkv, a.nblocks) : 0;
+  const long grid_q = want_dq ? pair_grid(a.batch, a.hkv, a.group * a.mblocks) : 0;
   dim3 blk(256);
   switch (act_kind) {
 #define GDPA_BWD_CASE(K)                                                                                       \

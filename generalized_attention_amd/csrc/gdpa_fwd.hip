@@ -135,21 +135,14 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // Block -> work mapping.  The dispatcher deals consecutive workgroup ids to
-  // the 8 XCDs in turn, and each XCD has its own L2.  All workgroups that read
-  // one (sequence, KV head) pair -- its query heads times its query blocks --
-  // go to one XCD back to back, so each K/V tile is fetched into that L2 once
-  // and re-read there by the others while they walk the keys together.
-  // Within a pair, query blocks run last-first.
-  const int per_pair = a.group * a.mblocks;
-  const int xcd = blockIdx.x & (kNumXcd - 1), local = blockIdx.x / kNumXcd;
-  const int pair = (local / per_pair) * kNumXcd + xcd;
-  const int rest = local % per_pair;
-  if (pair >= a.batch * a.hkv) return;
-  const int b = pair / a.hkv;
-  const int g = pair % a.hkv;
-  const int h = g * a.group + rest / a.mblocks;
-  const int m = a.mblocks - 1 - rest % a.mblocks;
+  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // sequences first; within a pair, query blocks run last-first.
+  WorkItem w;
+  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
+  const int b = w.b;
+  const int g = w.g;
+  const int h = g * a.group + w.rest / a.mblocks;
+  const int m = a.mblocks - 1 - w.rest % a.mblocks;
 
   int qs, lq, ks, lk;
   if (a.cu_q != nullptr) {

@@ -54,6 +54,7 @@ struct FwdArgs {
   int32_t wr;         // window right (-1: unbounded)
   int32_t out_f32;    // 1: fp32 output, 0: bf16
   int32_t psplit;     // 1: P carried as a bf16 hi/lo pair (two MFMAs for P V)
+  const int32_t* perm;  // sequences in processing order (longest first), or nullptr
 };
 
 // One backward launch (both kernels take the same block).
@@ -81,6 +82,7 @@ struct BwdArgs {
   int32_t out_f32;
   int32_t dsplit;     // 1: dS carried as a bf16 hi/lo pair in dQ = dS K
   int32_t kvsplit;    // 1: P and dS carried as bf16 hi/lo pairs in dV, dK
+  const int32_t* perm;  // sequences in processing order (longest first), or nullptr
 };
 
 // Forward workgroup shape: kFwdNW waves, each owning kFwdNQB blocks of 32 query rows.
@@ -89,12 +91,43 @@ constexpr int kFwdBM = 32 * kFwdNW * kFwdNQB;
 // XCDs per MI355X; workgroup ids are dealt to them round-robin.
 constexpr int kNumXcd = 8;
 
-// Forward grid: (sequence, KV head) pairs rounded up to a multiple of the XCD
-// count, times query heads per KV head, times query blocks.
-inline long fwd_grid(const FwdArgs& a) {
-  const long pairs = ((long)a.batch * a.hkv + kNumXcd - 1) / kNumXcd * kNumXcd;
-  return pairs * a.group * a.mblocks;
+// Workgroup -> work item.  Work is grouped by (sequence, KV head) pair; a
+// pair owns per_pair consecutive items (query heads x query blocks, or key
+// blocks).  The dispatcher deals consecutive workgroup ids to the XCDs in
+// turn and each XCD has its own L2, so pair p goes to XCD p % 8 and all its
+// items run there back to back: each K/V (or Q/dO) tile is fetched into that
+// L2 once and re-read there by the pair's other workgroups.  Pairs are taken
+// in rank order of perm (longest sequences first, when a schedule was built),
+// so every XCD works through its share longest-first and short items fill the
+// tail.  The grid is the pair count rounded up to the XCD count, times per_pair.
+inline long pair_grid(long batch, long hkv, long per_pair) {
+  const long pairs = ((long)batch * hkv + kNumXcd - 1) / kNumXcd * kNumXcd;
+  return pairs * per_pair;
 }
+struct WorkItem {
+  int b;     // sequence
+  int g;     // KV head
+  int rest;  // index within the pair, 0 .. per_pair-1
+};
+__device__ __forceinline__ bool map_work(int bid, int batch, int hkv, int per_pair, const int32_t* perm,
+                                         WorkItem& w) {
+  const int xcd = bid & (kNumXcd - 1), local = bid / kNumXcd;
+  const int pair = (local / per_pair) * kNumXcd + xcd;
+  if (pair >= batch * hkv) return false;
+  const int rank = pair / hkv;
+  w.b = perm != nullptr ? perm[rank] : rank;
+  w.g = pair % hkv;
+  w.rest = local % per_pair;
+  return true;
+}
+inline long fwd_grid(const FwdArgs& a) { return pair_grid(a.batch, a.hkv, (long)a.group * a.mblocks); }
+
+// Longest-first schedule of a jagged batch: perm[r] is the sequence with the
+// r-th largest lq + lk (ties by index).  Built on the device by one workgroup
+// for batches of at most kSortMax sequences; larger batches keep index order.
+constexpr int kSortMax = 4096;
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, hipStream_t stream);
+
 // Backward: dK/dV blocks cover 128 key rows, dQ blocks 128 query rows.
 constexpr int kBwdBN = 128;
 constexpr int kBwdBM = 128;

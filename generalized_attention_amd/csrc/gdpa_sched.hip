@@ -1,0 +1,57 @@
+// Longest-first processing order of a jagged batch.
+//
+// GDPA's jagged batches (the GDPA README's "Features": jagged sequences with
+// load-balanced scheduling) mix short and long sequences.  The kernels take
+// (sequence, KV head) pairs in the order of a permutation; processing the
+// longest sequences first is the longest-processing-time rule, which keeps
+// long work items out of the tail of the launch.  One workgroup sorts the
+// keys (lq + lk, index) with a bitonic network in LDS; keys are unique, so
+// the order is deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdpa_kernels.hpp"
+
+namespace gdpa {
+
+__global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q, const int32_t* cu_k, int batch,
+                                                             int32_t* perm) {
+  __shared__ uint64_t key[kSortMax];
+  int n = 1;
+  while (n < batch) n <<= 1;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    if (i < batch) {
+      const int64_t len = (int64_t)(cu_q[i + 1] - cu_q[i]) + (cu_k[i + 1] - cu_k[i]);
+      const uint64_t inv = (uint64_t)(0xffffffffLL - (len < 0xffffffffLL ? len : 0xffffffffLL));
+      key[i] = (inv << 32) | (uint32_t)i;  // ascending key = descending length, then index
+    } else {
+      key[i] = ~0ull;  // padding sorts last
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t x = key[i], y = key[l];
+          const bool ascending = (i & k) == 0;
+          if ((x > y) == ascending) {
+            key[i] = y;
+            key[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < batch; i += blockDim.x) perm[i] = (int32_t)(uint32_t)key[i];
+}
+
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, hipStream_t stream) {
+  if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, batch, perm);
+  return hipGetLastError();
+}
+
+}  // namespace gdpa

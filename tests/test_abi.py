@@ -147,6 +147,25 @@ def test_workspace_queries(lib):
     for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
               "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
         assert getattr(lib, n)(64, 1024, 1024, 4, 4, 128) >= 0
+    # fixed-length calls need none; jagged calls hold the longest-first order
+    # (one int32 per sequence, rounded up to 256 bytes) for up to 4096 sequences
+    assert lib.gdpa_fwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
+    assert lib.gdpa_bwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
+    for n in ("gdpa_varlen_fwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
+        f = getattr(lib, n)
+        assert f(64, 1024, 1024, 4, 4, 128) == 256
+        assert f(65, 1024, 1024, 4, 4, 128) == 512
+        assert f(4096, 1024, 1024, 4, 4, 128) == 4096 * 4
+        assert f(4097, 1024, 1024, 4, 4, 128) == 0
+        assert f(0, 1024, 1024, 4, 4, 128) == 0
+
+
+def test_jagged_calls_check_the_workspace_before_launching(lib):
+    # valid arguments, no workspace: refused on the host, nothing launched
+    assert varlen_fwd(lib) == WS_SMALL
+    assert varlen_fwd(lib, ws=FAKE, nws=255) == WS_SMALL
+    assert varlen_bwd(lib) == WS_SMALL
+    assert varlen_bwd(lib, ws=FAKE, nws=8) == WS_SMALL
 
 
 def test_python_binding_names_match_c_names():

@@ -188,3 +188,39 @@ def test_partial_gradients(g):
     dk2, dv2 = torch.full_like(dk, float("nan")), torch.full_like(dv, float("nan"))
     g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, dk2, dv2, *common, **kw)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+# ------------------------------------------------------- longest-first schedule
+def test_sequence_order_does_not_change_results(g):
+    # jagged calls process sequences longest first; reversing the batch must
+    # give each sequence bitwise the same output and gradients
+    import torch
+    lens = [5, 300, 1, 129, 64, 0, 257]
+    bt = gi.make_batch(_wl(act="gelu_tanh", mask="causal", batch=len(lens)), seqlens_q=lens, seqlens_k=lens)
+    rev = list(reversed(range(len(lens))))
+    cq = bt.cu_seqlens_q
+
+    def seq_rows(arr, order):
+        return np.concatenate([arr[cq[b]:cq[b + 1]] for b in order])
+
+    bt_rev = dataclasses.replace(bt, seqlens_q=np.asarray(lens)[rev], seqlens_k=np.asarray(lens)[rev],
+                                 cu_seqlens_q=np.concatenate([[0], np.cumsum(np.asarray(lens)[rev])]).astype(np.int32),
+                                 cu_seqlens_k=np.concatenate([[0], np.cumsum(np.asarray(lens)[rev])]).astype(np.int32),
+                                 q=seq_rows(bt.q, rev), k=seq_rows(bt.k, rev), v=seq_rows(bt.v, rev),
+                                 do=seq_rows(bt.do, rev))
+    o = run_forward(g, bt).cpu().numpy()
+    o_rev = run_forward(g, bt_rev).cpu().numpy()
+    assert np.array_equal(seq_rows(o, rev), o_rev)
+    for a, b in zip(run_backward(g, bt), run_backward(g, bt_rev)):
+        assert np.array_equal(seq_rows(a.cpu().numpy(), rev), b.cpu().numpy())
+
+
+def test_batch_beyond_schedule_limit(g):
+    # more sequences than the on-device sort handles: index order, no workspace
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 6, size=4100)
+    wl = _wl(act="relu2", head_dim=64, heads_q=2, heads_kv=1, batch=len(lens))
+    bt = gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens)
+    assert g._lib.gdpa_varlen_fwd_workspace_size(len(lens), 5, 5, 2, 1, 64) == 0
+    check_forward(g, bt)
+    check_backward(g, bt)
