@@ -45,82 +45,179 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
 }
 
 // ------------------------------------------------------------------ dK / dV
+// Per wave: 32 keys (B operands K, V in registers), per step one 64-row query
+// block of one query head (two 32-row blocks qb = 0, 1):
+//   S/dP:  S = Q K^T, dP = dO V^T                (2 KS MFMAs per block)
+//   pairs: P = act(S), dS = act'(S) dP, packed   (VALU, 8 pairs per block)
+//   dV/dK: dV^T += dO^T P, dK^T += Q^T dS       (2 NDB MFMAs x 2 per block)
+// One wave per SIMD (dK, dV, K and V stay in registers), so the wave itself
+// must keep its matrix core busy while its vector ALU works: a step is issued
+// as one stream of "units" (2 MFMAs each, their LDS operands read PREF units
+// ahead) in the order S/dP(0), S/dP(1), dV/dK(0), dV/dK(1), and the pairs of
+// block 0 ride under S/dP(1), those of block 1 under dV/dK(0).
 template <int D, int ACT, bool SPLIT>
 struct DkdvKernel {
-  static constexpr int BQ = 64;        // query rows per step (two 32-row blocks)
+  static constexpr int BQ = 64;                      // query rows per step
   static constexpr int KS = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int ROWB = 2 * D;
+  static constexpr int TB = BQ * ROWB;               // bytes of one Q (or dO) tile
+  static constexpr int LPS = 2 * TB / (256 * 16);    // LDS copies per wave per step
+  static constexpr int NP = SPLIT ? 2 : 1;           // bf16 words per P / dS element
+  static constexpr int NA = KS;                      // S/dP units per query block (2 MFMAs each)
+  static constexpr int NB = 2 * NDB;                 // dV/dK units per query block
+  static constexpr int NU = 2 * NA + 2 * NB;
+  static constexpr int PREF = 2;                     // units of operand prefetch
+  static_assert(8 % NA == 0 || NA % 8 == 0, "pair placement");
 
-  // One 32-query block against this wave's 32 keys.  [ilo, ihi]: queries
-  // allowed to see this lane's key.
+  struct Words {  // packed P and dS of one 32-query block: [hi/lo][t] x 4 words
+    u32x4 p[NP][2];
+    u32x4 ds[NP][2];
+  };
+
+  // One pair of accumulator elements (rows 8t+2w, +1) -> P, dS words.
   template <bool MASK>
-  static __device__ __forceinline__ void block(const uint8_t* ql, const uint8_t* dl, int qb, const u32x4* kreg,
-                                               const u32x4* vreg, f32x16* dkacc, f32x16* dvacc, int lane,
-                                               int m0, int ilo, int ihi, const BwdArgs& a) {
-    const int hf = lane >> 5;
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+  static __device__ __forceinline__ void pair(const f32x16& s, const f32x16& dp, int t, int w, int lo, int hi,
+                                              Words& wd, const ActConsts& k) {
+    float pv[2], dsv[2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc = mfma_bf16(row_operand<ROWB>(ql, qb * 32, 2 * s, lane), kreg[s], sacc);
-      dpacc = mfma_bf16(row_operand<ROWB>(dl, qb * 32, 2 * s, lane), vreg[s], dpacc);
-    }
-    // accumulator element r: query m0 + qb*32 + 4hf + 8(r/4) + r%4, this lane's key
-    const int base = m0 + qb * 32 + hf * 4;
-    const int lo = ilo - base, hi = ihi - base;
-    u32x4 pb[2], dsb[2], pbl[2], dsbl[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float pv[2], dsv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * t + 2 * w + u;
-          float dy;
-          float y = Act<ACT>::f_df(sacc[r], a.act, dy);
-          float ds = dpacc[r] * dy;
-          if constexpr (MASK) {
-            const bool ok = in_range(r, lo, hi);
-            y = ok ? y : 0.0f;
-            ds = ok ? ds : 0.0f;
-          }
-          pv[u] = y;
-          dsv[u] = ds;
-        }
-        pb[t][w] = pack_bf16x2(pv[0], pv[1]);
-        dsb[t][w] = pack_bf16x2(dsv[0], dsv[1]);
-        if constexpr (SPLIT) {
-          pbl[t][w] = split_lo(pv[0], pv[1], pb[t][w]);
-          dsbl[t][w] = split_lo(dsv[0], dsv[1], dsb[t][w]);
-        }
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * t + 2 * w + u;
+      float dy;
+      float y = Act<ACT>::f_df(s[r], k, dy);
+      float ds = dp[r] * dy;
+      if constexpr (MASK) {
+        const bool ok = in_range(r, lo, hi);
+        y = ok ? y : 0.0f;
+        ds = ok ? ds : 0.0f;
       }
+      pv[u] = y;
+      dsv[u] = ds;
     }
+    const uint32_t ph = pack_bf16x2(pv[0], pv[1]), dh = pack_bf16x2(dsv[0], dsv[1]);
+    wd.p[0][t][w] = ph;
+    wd.ds[0][t][w] = dh;
+    if constexpr (SPLIT) {
+      wd.p[1][t][w] = split_lo(pv[0], pv[1], ph);
+      wd.ds[1][t][w] = split_lo(dsv[0], dsv[1], dh);
+    }
+  }
+
+  // Per-lane byte offsets of the operands inside a row-major swizzled tile
+  // (the chunk swizzle depends on the row only modulo 8, so one offset per
+  // k-step serves every 32-row block, and two serve all transposed reads):
+  //   row[s] : A operand of rows (lane % 32) + 32 qb, k-step s  (+ 32 qb ROWB)
+  //   tr[p]  : transposed A operand, head-dim block db of parity p, query
+  //            rows 16 t' (+ 16 t' ROWB + 64 db)
+  // Keeping just these few registers live (and adding the tile's base and the
+  // constant parts per read) keeps the register file for the pipeline.
+  struct LaneOffs {
+    int row[KS];
+    int tr[2];
+  };
+  static __device__ __forceinline__ LaneOffs lane_offsets(int lane) {
+    LaneOffs o;
+    const int r = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < KS; ++s) o.row[s] = r * ROWB + (((2 * s + hf) ^ chunk_swz<ROWB>(r)) << 4);
+    const int g = lane >> 4, rr = lane & 15;
+    const int rowl = 4 * (g >> 1) + (rr >> 2);            // row within an 8-row group
+    const int x = (2 * (g & 1) + ((rr & 3) >> 1)) ^ chunk_swz<ROWB>(rowl);
+    const int base = rowl * ROWB + (x & 3) * 16 + 8 * (rr & 1);
+    o.tr[0] = base + 64 * (x >> 2);                        // even db: chunk 4 db + x
+    o.tr[1] = base - 64 * (x >> 2);                        // odd db
+    return o;
+  }
+  static __device__ __forceinline__ u32x4 row_at(const uint8_t* tile, int off) {
+    return *reinterpret_cast<const u32x4*>(tile + off);
+  }
+  static __device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, int off) {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + off));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(tile + (off + 8 * ROWB)));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // Unit u of a step: u < 2 NA: S/dP of block u / NA, k-step u % NA;
+  // else dV/dK of block (u - 2 NA) / NB, key-row half t and head-dim block db.
+  static __device__ __forceinline__ void load_unit(int u, const uint8_t* ql, const uint8_t* dl, const LaneOffs& lo,
+                                                   u32x4& o0, u32x4& o1) {
+    if (u < 2 * NA) {
+      const int qb = u / NA, s = u % NA;
+      o0 = row_at(ql, lo.row[s] + qb * 32 * ROWB);
+      o1 = row_at(dl, lo.row[s] + qb * 32 * ROWB);
+    } else {
+      const int v = u - 2 * NA, qb = v / NB, t = (v % NB) / NDB, db = v % NDB;
+      const int off = lo.tr[db & 1] + (qb * 32 + 16 * t) * ROWB + 64 * db;
+      o0 = tr_at(dl, off);
+      o1 = tr_at(ql, off);
+    }
+  }
+  static __device__ __forceinline__ void mma_unit(int u, const u32x4& o0, const u32x4& o1, const u32x4* kreg,
+                                                  const u32x4* vreg, f32x16* sacc, f32x16* dpacc, const Words* wd,
+                                                  f32x16* dkacc, f32x16* dvacc) {
+    if (u < 2 * NA) {
+      const int qb = u / NA, s = u % NA;
+      sacc[qb] = mfma_bf16(o0, kreg[s], sacc[qb]);
+      dpacc[qb] = mfma_bf16(o1, vreg[s], dpacc[qb]);
+    } else {
+      const int v = u - 2 * NA, qb = v / NB, t = (v % NB) / NDB, db = v % NDB;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 doa = tr_operand<ROWB>(dl, qb * 32 + 16 * t, db * 32, lane);
-        const bf16x8 qta = tr_operand<ROWB>(ql, qb * 32 + 16 * t, db * 32, lane);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, __builtin_bit_cast(bf16x8, pb[t]), dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, __builtin_bit_cast(bf16x8, dsb[t]), dkacc[db], 0, 0, 0);
-        if constexpr (SPLIT) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, __builtin_bit_cast(bf16x8, pbl[t]), dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, __builtin_bit_cast(bf16x8, dsbl[t]), dkacc[db], 0, 0, 0);
-        }
+      for (int h = 0; h < NP; ++h) {
+        dvacc[db] = mfma_bf16(o0, wd[qb].p[h][t], dvacc[db]);
+        dkacc[db] = mfma_bf16(o1, wd[qb].ds[h][t], dkacc[db]);
       }
     }
   }
+
+  // One step.  lo/hi[qb]: this lane's allowed-query range relative to the
+  // accumulator base of block qb (used when MASK).
+  template <bool MASK>
+  static __device__ __forceinline__ void step(const uint8_t* ql, const uint8_t* dl, const LaneOffs& lo,
+                                              const u32x4* kreg, const u32x4* vreg, f32x16* dkacc, f32x16* dvacc,
+                                              const int* mlo, const int* mhi, const ActConsts& k) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, dpacc[2] = {f32x16{}, f32x16{}};
+    Words wd[2];
+    u32x4 ring[PREF + 1][2];
+#pragma unroll
+    for (int u = 0; u < PREF; ++u) load_unit(u, ql, dl, lo, ring[u][0], ring[u][1]);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + PREF < NU)
+        load_unit(u + PREF, ql, dl, lo, ring[(u + PREF) % (PREF + 1)][0], ring[(u + PREF) % (PREF + 1)][1]);
+      mma_unit(u, ring[u % (PREF + 1)][0], ring[u % (PREF + 1)][1], kreg, vreg, sacc, dpacc, wd, dkacc, dvacc);
+      // pairs of block qb ride under the NA (or NB) units that follow its last S/dP unit
+      if (u >= NA && u < 2 * NA + NB) {
+        const int qb = u < 2 * NA ? 0 : 1;
+        const int v = u < 2 * NA ? u - NA : u - 2 * NA;
+        const int span = u < 2 * NA ? NA : NB;
+        if (span >= 8) {
+          if (v % (span / 8) == 0) {
+            const int j = v / (span / 8);
+            pair<MASK>(sacc[qb], dpacc[qb], j >> 2, j & 3, mlo[qb], mhi[qb], wd[qb], k);
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 8 / span; ++jj) {
+            const int j = v * (8 / span) + jj;
+            pair<MASK>(sacc[qb], dpacc[qb], j >> 2, j & 3, mlo[qb], mhi[qb], wd[qb], k);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 };
 
-// D = 128 keeps dK, dV, K and V (256 registers) live across the loop: one
-// wave per SIMD there; D = 64 fits two.
+// One workgroup (4 waves; one per SIMD at D = 128, two at D = 64) per (sequence, KV head, 128-key
+// block).  Q / dO tiles of the steps are double-buffered in LDS: the next
+// step's copy is in flight while the current step is computed.
 template <int D, int ACT, bool SPLIT>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
   using K = DkdvKernel<D, ACT, SPLIT>;
   constexpr int BNB = kBwdBN;  // keys per workgroup (32 per wave)
-  constexpr int BQ = K::BQ, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;
-  constexpr int TB = BQ * ROWB;
+  constexpr int BQ = K::BQ, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB, TB = K::TB;
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t do_lds0[TB];
@@ -178,54 +275,58 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
     dkacc[i] = f32x16{};
     dvacc[i] = f32x16{};
   }
+  const typename K::LaneOffs loffs = K::lane_offsets(lane);
 
   const int q_ld_b = a.hq * D * 2;  // bytes per token row of q / dO
   // this sequence's q and dO rows (all heads); 32-bit offsets, bounded on the host
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(static_cast<const uint8_t*>(a.q) + (long)qs * q_ld_b, lq * q_ld_b);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(static_cast<const uint8_t*>(a.dout) + (long)qs * q_ld_b, lq * q_ld_b);
-  auto stage = [&](int step, uint8_t* ql, uint8_t* dl) {
-    const int h = g * a.group + step % a.group;
-    const int m0 = (mb_begin + step / a.group) * BQ;
-    const int off = m0 * q_ld_b + h * D * 2;
-    stage_tile_buf<BQ, ROWB, 4>(qrs, off, q_ld_b, lq - m0, ql, wave, lane);
-    stage_tile_buf<BQ, ROWB, 4>(drs, off, q_ld_b, lq - m0, dl, wave, lane);
+  auto step_m0 = [&](int i) { return (mb_begin + i / a.group) * BQ; };
+  auto stage = [&](int i, uint8_t* ql, uint8_t* dl) {
+    const int h = g * a.group + i % a.group;
+    const int m0 = step_m0(i);
+    const int o = m0 * q_ld_b + h * D * 2;
+    stage_tile_buf<BQ, ROWB, 4>(qrs, o, q_ld_b, lq - m0, ql, wave, lane);
+    stage_tile_buf<BQ, ROWB, 4>(drs, o, q_ld_b, lq - m0, dl, wave, lane);
   };
-  auto compute = [&](int step, const uint8_t* ql, const uint8_t* dl) {
+  auto compute = [&](int i, const uint8_t* ql, const uint8_t* dl) {
     if (!wave_active) return;
-    const int m0 = (mb_begin + step / a.group) * BQ;
-#pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      const int mlo = m0 + qb * 32, mhi = mlo + 31;
-      if (mlo >= lq) break;
-      // wave-level classification of (queries mlo..mhi, keys k0w..kmax_w)
-      bool empty = false, full = mhi < lq;
-      if (a.wr >= 0) {
-        empty |= k0w > min(mhi, lq - 1) + off + a.wr;
-        full &= kmax_w <= mlo + off + a.wr;
-      }
-      if (a.wl >= 0) {
-        empty |= kmax_w < mlo + off - a.wl;
-        full &= k0w >= mhi + off - a.wl;
-      }
-      if (empty) continue;
-      if (full)
-        K::template block<false>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, 0, 0, a);
-      else
-        K::template block<true>(ql, dl, qb, kreg, vreg, dkacc, dvacc, lane, m0, ilo_l, ihi_l, a);
+    const int m0 = step_m0(i), mhi = m0 + BQ - 1;
+    // wave-level classification of (queries m0..mhi, keys k0w..kmax_w)
+    bool empty = false, full = mhi < lq;
+    if (a.wr >= 0) {
+      empty |= k0w > min(mhi, lq - 1) + off + a.wr;
+      full &= kmax_w <= m0 + off + a.wr;
     }
+    if (a.wl >= 0) {
+      empty |= kmax_w < m0 + off - a.wl;
+      full &= k0w >= mhi + off - a.wl;
+    }
+    if (empty) return;
+    int mlo[2], mhi2[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int base = m0 + qb * 32 + hf * 4;
+      mlo[qb] = ilo_l - base;
+      mhi2[qb] = ihi_l - base;
+    }
+    if (full)
+      K::template step<false>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
+    else
+      K::template step<true>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
   };
 
   if (nsteps > 0) stage(0, q_lds0, do_lds0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    if (step + 1 < nsteps) stage(step + 1, q_lds1, do_lds1);
-    compute(step, q_lds0, do_lds0);
+  for (int i = 0; i < nsteps; i += 2) {
+    if (i + 1 < nsteps) stage(i + 1, q_lds1, do_lds1);
+    compute(i, q_lds0, do_lds0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (step + 1 >= nsteps) break;
-    if (step + 2 < nsteps) stage(step + 2, q_lds0, do_lds0);
-    compute(step + 1, q_lds1, do_lds1);
+    if (i + 1 >= nsteps) break;
+    if (i + 2 < nsteps) stage(i + 2, q_lds0, do_lds0);
+    compute(i + 1, q_lds1, do_lds1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

@@ -236,6 +236,24 @@ __device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int 
   }
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence: completion of LDS-direct copies is
+// established explicitly with wait_vmcnt before it, and every LDS read before
+// it is consumed before it.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Transposed MFMA A operand from a row-major bf16 row tile via
 // ds_read_b64_tr_b16.  Within each 16-lane group the instruction hands lane j
 // element e of the 8-byte row that lane 4e + j/4 addressed, column j % 4.  So
