@@ -144,27 +144,50 @@ gdpa_status_t hip_status(hipError_t e, const char* what) {
 }
 
 // Workspace of a jagged call: the longest-first sequence order (int32 per
-// sequence), built on the device before the main kernels.  Batches beyond
-// kSortMax keep index order and need no workspace.
+// sequence) and the work-queue counters, built on the device before the main
+// kernels.  Batches beyond kSortMax keep index order and need no workspace.
 size_t schedule_bytes(int64_t batch) {
   if (batch <= 0 || batch > gdpa::kSortMax) return 0;
-  return (size_t)((batch * 4 + 255) / 256 * 256);
+  return (size_t)(((batch + gdpa::kNumCounters) * 4 + 255) / 256 * 256);
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static int cache[64] = {};
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
 }
 
 // Builds the schedule into the workspace when this is a jagged call that has
-// one; *perm stays nullptr otherwise.
+// one; *perm and *counters stay nullptr otherwise (index order, one workgroup
+// per item).
 gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, int32_t batch, void* workspace,
-                             size_t workspace_bytes, void* stream, const int32_t** perm) {
+                             size_t workspace_bytes, void* stream, const int32_t** perm, int32_t** counters,
+                             int32_t* ncu) {
   *perm = nullptr;
+  *counters = nullptr;
+  *ncu = 0;
   if (cu_q == nullptr) return GDPA_OK;
   const size_t need = schedule_bytes(batch);
   if (need == 0) return GDPA_OK;
   if (workspace == nullptr || workspace_bytes < need) return GDPA_ERR_WORKSPACE_TOO_SMALL;
   int32_t* p = static_cast<int32_t*>(workspace);
-  const gdpa_status_t st =
-      hip_status(gdpa::launch_schedule(cu_q, cu_k, batch, p, static_cast<hipStream_t>(stream)), "schedule launch");
-  if (st == GDPA_OK) *perm = p;
-  return st;
+  int32_t* cnt = p + batch;
+  const gdpa_status_t st = hip_status(
+      gdpa::launch_schedule(cu_q, cu_k, batch, p, cnt, static_cast<hipStream_t>(stream)), "schedule launch");
+  if (st != GDPA_OK) return st;
+  *perm = p;
+  const int n = device_cu_count();
+  if (n > 0) {
+    *counters = cnt;
+    *ncu = n;
+  }
+  return GDPA_OK;
 }
 
 gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_q,
@@ -209,7 +232,10 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
   // The forward kernel addresses one sequence's K and V rows with 32-bit byte offsets.
   if ((int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
-  gdpa_status_t sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm);
+  int32_t* counters = nullptr;  // the forward keeps one workgroup per item
+  int32_t ncu = 0;
+  gdpa_status_t sst =
+      build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
@@ -267,7 +293,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.out_f32 = grad_dtype == GDPA_DTYPE_FP32;
   a.dsplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
   a.kvsplit = few_terms(c.max_lq, a.group, c) ? 1 : 0;
-  gdpa_status_t sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm);
+  gdpa_status_t sst =
+      build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &a.counters, &a.ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,

@@ -227,13 +227,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hf = lane >> 5;
-  // Block -> work item: (sequence, KV head) pair on one XCD, longest
-  // sequences first; within a pair, key blocks run last-first.
-  WorkItem w;
-  if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
-  const int g = w.g;
-  const int b = w.b;
-  const int nblk = a.nblocks - 1 - w.rest;
+  // One work item: sequence b, KV head g, key block nblk.
+  auto process = [&](int b, int g, int nblk) __attribute__((always_inline)) {
   int qs, lq, ks, lk;
   seq_bounds(a, b, qs, lq, ks, lk);
   const int n0 = nblk * BNB;
@@ -353,6 +348,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(con
       }
     }
   }
+  };
+
+  if (a.counters == nullptr) {
+    // Block -> work item: (sequence, KV head) pair on one XCD, longest
+    // sequences first; within a pair, key blocks run last-first.
+    WorkItem w;
+    if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
+    process(w.b, w.g, a.nblocks - 1 - w.rest);
+  } else {
+    // Per-XCD work queue over the same pairs, longest sequence first (one
+    // workgroup per CU here, so the dispatcher's in-order hand-out of one
+    // item per workgroup would leave CUs idle between items).
+    run_queue(a.counters + (blockIdx.x & (kNumXcd - 1)), xcd_items(a.batch, a.hkv, a.nblocks),
+              [&](int j) __attribute__((always_inline)) {
+                WorkItem w;
+                xcd_item(j, a.hkv, a.nblocks, a.perm, w);
+                process(w.b, w.g, a.nblocks - 1 - w.rest);
+              });
+  }
 }
 
 // ----------------------------------------------------------------------- dQ
@@ -427,18 +441,12 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hf = lane >> 5;
-  // Block -> work item: (sequence, KV head) pair on one XCD, longest
-  // sequences first; within a pair, query blocks run last-first.
-  WorkItem w;
-  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
-  const int b = w.b;
-  const int h = w.g * a.group + w.rest / a.mblocks;
-  const int m = a.mblocks - 1 - w.rest % a.mblocks;
+  // One work item: sequence b, KV head g, query head h, query block m.
+  auto process = [&](int b, int g, int h, int m) __attribute__((always_inline)) {
   int qs, lq, ks, lk;
   seq_bounds(a, b, qs, lq, ks, lk);
   const int row0 = m * BM;
   if (row0 >= lq) return;
-  const int g = w.g;
   const int off = lk - lq;
   const int rlast = min(row0 + BM, lq) - 1;
   int j_lo = 0, j_hi = lk;
@@ -537,12 +545,21 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
       }
     }
   }
+  };
+
+  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // sequences first; within a pair, query blocks run last-first.
+  WorkItem w;
+  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
+  process(w.b, w.g, w.g * a.group + w.rest / a.mblocks, a.mblocks - 1 - w.rest % a.mblocks);
 }
 
 template <int D, bool SPLIT_KV, bool SPLIT_Q>
 static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
-  const long grid_kv = want_dkv ? pair_grid(a.batch, a.hkv, a.nblocks) : 0;
-  const long grid_q = want_dq ? pair_grid(a.batch, a.hkv, a.group * a.mblocks) : 0;
+  // dK/dV work queue: as many workgroups as are resident at once
+  const bool queue = a.counters != nullptr;
+  const long grid_kv = !want_dkv ? 0 : queue ? queue_grid(a.ncu, D == 64 ? 2 : 1) : pair_grid(a.batch, a.hkv, a.nblocks);
+  const long grid_q = !want_dq ? 0 : pair_grid(a.batch, a.hkv, a.group * a.mblocks);
   dim3 blk(256);
   switch (act_kind) {
 #define GDPA_BWD_CASE(K)                                                                                       \

@@ -135,15 +135,9 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // Block -> work item: (sequence, KV head) pair on one XCD, longest
-  // sequences first; within a pair, query blocks run last-first.
-  WorkItem w;
-  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
-  const int b = w.b;
-  const int g = w.g;
-  const int h = g * a.group + w.rest / a.mblocks;
-  const int m = a.mblocks - 1 - w.rest % a.mblocks;
 
+  // One work item: sequence b, KV head g, query head h, query block m.
+  auto process = [&](int b, int g, int h, int m) __attribute__((always_inline)) {
   int qs, lq, ks, lk;
   if (a.cu_q != nullptr) {
     qs = a.cu_q[b];
@@ -274,6 +268,13 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
       }
     }
   }
+  };
+
+  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // sequences first; within a pair, query blocks run last-first.
+  WorkItem w;
+  if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;
+  process(w.b, w.g, w.g * a.group + w.rest / a.mblocks, a.mblocks - 1 - w.rest % a.mblocks);
 }
 
 template <int D, bool FP8>

@@ -83,6 +83,8 @@ struct BwdArgs {
   int32_t dsplit;     // 1: dS carried as a bf16 hi/lo pair in dQ = dS K
   int32_t kvsplit;    // 1: P and dS carried as bf16 hi/lo pairs in dV, dK
   const int32_t* perm;  // sequences in processing order (longest first), or nullptr
+  int32_t* counters;    // per-XCD dK/dV work-queue counters (zeroed by the schedule), or nullptr
+  int32_t ncu;          // compute units of the device (sizes the work-queue launches)
 };
 
 // Forward workgroup shape: kFwdNW waves, each owning kFwdNQB blocks of 32 query rows.
@@ -122,11 +124,60 @@ __device__ __forceinline__ bool map_work(int bid, int batch, int hkv, int per_pa
 }
 inline long fwd_grid(const FwdArgs& a) { return pair_grid(a.batch, a.hkv, (long)a.group * a.mblocks); }
 
+// Queue-mode grid: occ workgroups per CU, a multiple of the XCD count so that
+// every XCD's queue has workgroups draining it.
+inline long queue_grid(int ncu, int occ) {
+  const long n = (long)ncu * occ;
+  return n < kNumXcd ? kNumXcd : (n + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+
+// Queue mode: the pairs of this workgroup's XCD and the pair of its list entry j.
+__device__ __forceinline__ long xcd_items(int batch, int hkv, int per_pair) {
+  const int xcd = blockIdx.x & (kNumXcd - 1);
+  const int pairs = batch * hkv;
+  return pairs > xcd ? (long)((pairs - xcd + kNumXcd - 1) / kNumXcd) * per_pair : 0;
+}
+__device__ __forceinline__ void xcd_item(int j, int hkv, int per_pair, const int32_t* perm, WorkItem& w) {
+  const int pair = (j / per_pair) * kNumXcd + (int)(blockIdx.x & (kNumXcd - 1));
+  w.b = perm[pair / hkv];
+  w.g = pair % hkv;
+  w.rest = j % per_pair;
+}
+
 // Longest-first schedule of a jagged batch: perm[r] is the sequence with the
 // r-th largest lq + lk (ties by index).  Built on the device by one workgroup
-// for batches of at most kSortMax sequences; larger batches keep index order.
+// for batches of at most kSortMax sequences, which also zeroes kNumCounters
+// work-queue counters; larger batches keep index order.
 constexpr int kSortMax = 4096;
-hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, hipStream_t stream);
+constexpr int kNumCounters = kNumXcd;
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
+                           hipStream_t stream);
+
+// Work-queue execution (jagged batches with a schedule): a launch of as many
+// workgroups as the device holds at once.  Work is still grouped by (sequence,
+// KV head) pair with pair p on XCD p % 8 (L2 reuse of the pair's tiles), but
+// the workgroups of an XCD take the next item of that XCD's list from an
+// atomic counter instead of being handed one item each by the dispatcher.
+// The lists run longest sequence first, so a free workgroup always picks the
+// heaviest remaining item of its XCD (list scheduling); the next index is
+// fetched while the current item runs.  Workgroup ids are dealt to the XCDs
+// in turn, so blockIdx % 8 names the XCD (only locality depends on that).
+template <typename F>
+__device__ __forceinline__ void run_queue(int32_t* counter, long total, F&& body) {
+  __shared__ int32_t nxt[2];
+  if (threadIdx.x == 0) nxt[0] = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int item = nxt[0];
+  int par = 0;
+  while (item < total) {
+    if (threadIdx.x == 0)
+      nxt[par ^ 1] = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    body(item);
+    __syncthreads();
+    item = nxt[par ^ 1];
+    par ^= 1;
+  }
+}
 
 // Backward: dK/dV blocks cover 128 key rows, dQ blocks 128 query rows.
 constexpr int kBwdBN = 128;

@@ -15,8 +15,9 @@
 namespace gdpa {
 
 __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q, const int32_t* cu_k, int batch,
-                                                             int32_t* perm) {
+                                                             int32_t* perm, int32_t* counters) {
   __shared__ uint64_t key[kSortMax];
+  if (threadIdx.x < kNumCounters) counters[threadIdx.x] = 0;
   int n = 1;
   while (n < batch) n <<= 1;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -48,9 +49,10 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
   for (int i = threadIdx.x; i < batch; i += blockDim.x) perm[i] = (int32_t)(uint32_t)key[i];
 }
 
-hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, hipStream_t stream) {
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
+                           hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, batch, perm);
+  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, batch, perm, counters);
   return hipGetLastError();
 }
 

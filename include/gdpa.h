@@ -165,13 +165,14 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
 
 /* Workspace each call needs, in bytes (0 = none; pass NULL then).  Arguments
  * mirror the shape arguments of the matching entry point.  Jagged calls of
- * 1..4096 sequences need 4 bytes per sequence (rounded up to 256): the call
- * first builds there, on the device, the order in which sequences are
- * processed (longest first; see the README's load-balanced scheduling of
- * jagged batches).  Fixed-length calls and larger batches need none.  A call
- * given less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before
- * launching anything.  The workspace is caller-owned and only used on the
- * call's stream. */
+ * 1..4096 sequences need 4 bytes per sequence plus 32, rounded up to 256: the
+ * call first builds there, on the device, the order in which sequences are
+ * processed (longest first) and the counters of the work queues its kernels
+ * draw items from (see the README's load-balanced scheduling of jagged
+ * batches).  Fixed-length calls and larger batches need none.  A call given
+ * less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before launching
+ * anything.  The workspace is caller-owned and only used on the call's
+ * stream; calls that share one must be ordered on one stream. */
 size_t gdpa_fwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
 size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,

@@ -147,15 +147,16 @@ def test_workspace_queries(lib):
     for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
               "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
         assert getattr(lib, n)(64, 1024, 1024, 4, 4, 128) >= 0
-    # fixed-length calls need none; jagged calls hold the longest-first order
-    # (one int32 per sequence, rounded up to 256 bytes) for up to 4096 sequences
+    # fixed-length calls need none; jagged calls of up to 4096 sequences hold
+    # the longest-first order (one int32 per sequence) and 8 work-queue
+    # counters, rounded up to 256 bytes
     assert lib.gdpa_fwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
     assert lib.gdpa_bwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
     for n in ("gdpa_varlen_fwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
         f = getattr(lib, n)
-        assert f(64, 1024, 1024, 4, 4, 128) == 256
-        assert f(65, 1024, 1024, 4, 4, 128) == 512
-        assert f(4096, 1024, 1024, 4, 4, 128) == 4096 * 4
+        assert f(56, 1024, 1024, 4, 4, 128) == 256
+        assert f(57, 1024, 1024, 4, 4, 128) == 512
+        assert f(4096, 1024, 1024, 4, 4, 128) == 16640
         assert f(4097, 1024, 1024, 4, 4, 128) == 0
         assert f(0, 1024, 1024, 4, 4, 128) == 0
 
