@@ -213,8 +213,16 @@ struct DkdvKernel {
 // One workgroup (4 waves; one per SIMD at D = 128, two at D = 64) per (sequence, KV head, 128-key
 // block).  Q / dO tiles of the steps are double-buffered in LDS: the next
 // step's copy is in flight while the current step is computed.
+// Workgroups per CU of the dK/dV kernel: two at D = 64 (K, V, dK, dV take 128
+// registers), except where the activation's gradient needs more registers
+// than two waves per SIMD leave (exact GELU, and the hi/lo split).
 template <int D, int ACT, bool SPLIT>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
+constexpr int dkdv_occupancy() {
+  return (D == 64 && !SPLIT && ACT != ACT_GELU) ? 2 : 1;
+}
+
+template <int D, int ACT, bool SPLIT>
+__global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
   using K = DkdvKernel<D, ACT, SPLIT>;
   constexpr int BNB = kBwdBN;  // keys per workgroup (32 per wave)
   constexpr int BQ = K::BQ, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB, TB = K::TB;
@@ -558,14 +566,17 @@ template <int D, bool SPLIT_KV, bool SPLIT_Q>
 static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, hipStream_t stream) {
   // dK/dV work queue: as many workgroups as are resident at once
   const bool queue = a.counters != nullptr;
-  const long grid_kv = !want_dkv ? 0 : queue ? queue_grid(a.ncu, D == 64 ? 2 : 1) : pair_grid(a.batch, a.hkv, a.nblocks);
+  const long grid_kv = !want_dkv ? 0 : queue ? -1 : pair_grid(a.batch, a.hkv, a.nblocks);
   const long grid_q = !want_dq ? 0 : pair_grid(a.batch, a.hkv, a.group * a.mblocks);
   dim3 blk(256);
   switch (act_kind) {
 #define GDPA_BWD_CASE(K)                                                                                       \
   case K:                                                                                                      \
-    if (grid_kv > 0)                                                                                           \
-      hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K, SPLIT_KV>), dim3((unsigned)grid_kv), blk, 0, stream, a); \
+    if (grid_kv != 0)                                                                                          \
+      hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K, SPLIT_KV>),                                               \
+                         dim3((unsigned)(grid_kv > 0 ? grid_kv                                                 \
+                                                     : queue_grid(a.ncu, dkdv_occupancy<D, K, SPLIT_KV>()))), \
+                         blk, 0, stream, a);                                                                   \
     if (grid_q > 0)                                                                                            \
       hipLaunchKernelGGL((gdpa_bwd_dq_kernel<D, K, SPLIT_Q>), dim3((unsigned)grid_q), blk, 0, stream, a);     \
     break;

@@ -52,7 +52,10 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
 hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
                            hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, batch, perm, counters);
+  // one compare-exchange per thread and stage: small batches sort in one wave
+  int threads = 64;
+  while (threads < 1024 && 2 * threads < batch) threads <<= 1;
+  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(threads), 0, stream, cu_q, cu_k, batch, perm, counters);
   return hipGetLastError();
 }
 
