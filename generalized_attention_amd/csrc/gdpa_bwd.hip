@@ -44,6 +44,45 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
   }
 }
 
+// Per-lane byte offsets of the MFMA operands inside a row-major swizzled
+// [rows][ROWB bytes] LDS tile (the chunk swizzle depends on the row only
+// modulo 8, so one offset per k-step serves every 32-row block, and two serve
+// all transposed reads):
+//   row[s] : A operand of rows (lane % 32) + 32 j, k-step s      (+ 32 j ROWB)
+//   tr[p]  : transposed A operand (ds_read_b64_tr_b16 pair) of head-dim block
+//            db of parity p, tile rows 16 t'                      (+ 16 t' ROWB + 64 db)
+// Keeping just these few registers live, and adding the tile's base and the
+// constant parts per read, leaves the register file to the pipelines.
+template <int ROWB>
+struct TileOffs {
+  static constexpr int KS = ROWB / 32;  // 16-element k-steps per row
+  int row[KS];
+  int tr[2];
+  static __device__ __forceinline__ TileOffs make(int lane) {
+    TileOffs o;
+    const int r = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) o.row[s] = r * ROWB + (((2 * s + hf) ^ chunk_swz<ROWB>(r)) << 4);
+    const int g = lane >> 4, rr = lane & 15;
+    const int rowl = 4 * (g >> 1) + (rr >> 2);  // row within an 8-row group
+    const int x = (2 * (g & 1) + ((rr & 3) >> 1)) ^ chunk_swz<ROWB>(rowl);
+    const int base = rowl * ROWB + (x & 3) * 16 + 8 * (rr & 1);
+    o.tr[0] = base + 64 * (x >> 2);  // even db: chunk 4 db + x
+    o.tr[1] = base - 64 * (x >> 2);  // odd db
+    return o;
+  }
+};
+__device__ __forceinline__ u32x4 row_at(const uint8_t* tile, int off) {
+  return *reinterpret_cast<const u32x4*>(tile + off);
+}
+template <int ROWB>
+__device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, int off) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + off));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(tile + (off + 8 * ROWB)));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ------------------------------------------------------------------ dK / dV
 // Per wave: 32 keys (B operands K, V in registers), per step one 64-row query
 // block of one query head (two 32-row blocks qb = 0, 1):
@@ -70,6 +109,7 @@ struct DkdvKernel {
   static constexpr int PREF = 2;                     // units of operand prefetch
   static_assert(8 % NA == 0 || NA % 8 == 0, "pair placement");
 
+  using LaneOffs = TileOffs<ROWB>;
   struct Words {  // packed P and dS of one 32-query block: [hi/lo][t] x 4 words
     u32x4 p[NP][2];
     u32x4 ds[NP][2];
@@ -103,41 +143,6 @@ struct DkdvKernel {
     }
   }
 
-  // Per-lane byte offsets of the operands inside a row-major swizzled tile
-  // (the chunk swizzle depends on the row only modulo 8, so one offset per
-  // k-step serves every 32-row block, and two serve all transposed reads):
-  //   row[s] : A operand of rows (lane % 32) + 32 qb, k-step s  (+ 32 qb ROWB)
-  //   tr[p]  : transposed A operand, head-dim block db of parity p, query
-  //            rows 16 t' (+ 16 t' ROWB + 64 db)
-  // Keeping just these few registers live (and adding the tile's base and the
-  // constant parts per read) keeps the register file for the pipeline.
-  struct LaneOffs {
-    int row[KS];
-    int tr[2];
-  };
-  static __device__ __forceinline__ LaneOffs lane_offsets(int lane) {
-    LaneOffs o;
-    const int r = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) o.row[s] = r * ROWB + (((2 * s + hf) ^ chunk_swz<ROWB>(r)) << 4);
-    const int g = lane >> 4, rr = lane & 15;
-    const int rowl = 4 * (g >> 1) + (rr >> 2);            // row within an 8-row group
-    const int x = (2 * (g & 1) + ((rr & 3) >> 1)) ^ chunk_swz<ROWB>(rowl);
-    const int base = rowl * ROWB + (x & 3) * 16 + 8 * (rr & 1);
-    o.tr[0] = base + 64 * (x >> 2);                        // even db: chunk 4 db + x
-    o.tr[1] = base - 64 * (x >> 2);                        // odd db
-    return o;
-  }
-  static __device__ __forceinline__ u32x4 row_at(const uint8_t* tile, int off) {
-    return *reinterpret_cast<const u32x4*>(tile + off);
-  }
-  static __device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, int off) {
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + off));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(tile + (off + 8 * ROWB)));
-    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
-
   // Unit u of a step: u < 2 NA: S/dP of block u / NA, k-step u % NA;
   // else dV/dK of block (u - 2 NA) / NB, key-row half t and head-dim block db.
   static __device__ __forceinline__ void load_unit(int u, const uint8_t* ql, const uint8_t* dl, const LaneOffs& lo,
@@ -149,8 +154,8 @@ struct DkdvKernel {
     } else {
       const int v = u - 2 * NA, qb = v / NB, t = (v % NB) / NDB, db = v % NDB;
       const int off = lo.tr[db & 1] + (qb * 32 + 16 * t) * ROWB + 64 * db;
-      o0 = tr_at(dl, off);
-      o1 = tr_at(ql, off);
+      o0 = tr_at<ROWB>(dl, off);
+      o1 = tr_at<ROWB>(ql, off);
     }
   }
   static __device__ __forceinline__ void mma_unit(int u, const u32x4& o0, const u32x4& o1, const u32x4* kreg,
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     dkacc[i] = f32x16{};
     dvacc[i] = f32x16{};
   }
-  const typename K::LaneOffs loffs = K::lane_offsets(lane);
+  const TileOffs<ROWB> loffs = TileOffs<ROWB>::make(lane);
 
   const int q_ld_b = a.hq * D * 2;  // bytes per token row of q / dO
   // this sequence's q and dO rows (all heads); 32-bit offsets, bounded on the host
@@ -386,56 +391,109 @@ struct DqKernel {
   static constexpr int NDB = D / 32;
   static constexpr int ROWB = 2 * D;
 
-  // One 32-key block of the tile against this wave's 32 queries.  [jlo, jhi]:
-  // keys this lane's query may see.
+  static constexpr int NP = SPLIT ? 2 : 1;   // bf16 words per dS element
+  static constexpr int NA = KS;               // S/dP units per key block (2 MFMAs each)
+  static constexpr int NB = 2 * NDB;          // dQ units per key block (NP MFMAs each)
+  static constexpr int NU = 2 * NA + 2 * NB;  // units of a pair of key blocks
+  static constexpr int PREF = 2;              // units of operand prefetch
+  using LaneOffs = TileOffs<ROWB>;
+
+  // One pair of accumulator elements (key rows 8t+2w, +1) -> dS words.
   template <bool MASK>
-  static __device__ __forceinline__ void block(const uint8_t* kl, const uint8_t* vl, int kb, const u32x4* qreg,
-                                               const u32x4* doreg, f32x16* dqacc, int lane, int n0, int jlo,
-                                               int jhi, const BwdArgs& a) {
-    const int hf = lane >> 5;
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+  static __device__ __forceinline__ void pair(const f32x16& s, const f32x16& dp, int t, int w, int lo, int hi,
+                                              u32x4 (*ds)[2], const ActConsts& k) {
+    float dsv[2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc = mfma_bf16(row_operand<ROWB>(kl, kb * 32, 2 * s, lane), qreg[s], sacc);
-      dpacc = mfma_bf16(row_operand<ROWB>(vl, kb * 32, 2 * s, lane), doreg[s], dpacc);
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * t + 2 * w + u;
+      float dy;
+      (void)Act<ACT>::f_df(s[r], k, dy);
+      float v = dp[r] * dy;
+      if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
+      dsv[u] = v;
     }
-    // accumulator element r: key n0 + kb*32 + 4hf + 8(r/4) + r%4, this lane's query
-    const int base = n0 + kb * 32 + hf * 4;
-    const int lo = jlo - base, hi = jhi - base;
-    u32x4 dsh[2], dsl[2];
+    const uint32_t dh = pack_bf16x2(dsv[0], dsv[1]);
+    ds[0][t][w] = dh;
+    if constexpr (SPLIT) ds[1][t][w] = split_lo(dsv[0], dsv[1], dh);
+  }
+
+  // Unit u of a block pair (blocks kb0, kb0+1 of the tile): u < 2 NA: S/dP of
+  // block u / NA, k-step u % NA; else dQ of block (u - 2 NA) / NB, key-row half
+  // t and head-dim block db.
+  static __device__ __forceinline__ void load_unit(int u, int kb0, const uint8_t* kl, const uint8_t* vl,
+                                                   const LaneOffs& lo, u32x4& o0, u32x4& o1) {
+    if (u < 2 * NA) {
+      const int kb = kb0 + u / NA, s = u % NA;
+      o0 = row_at(kl, lo.row[s] + kb * 32 * ROWB);
+      o1 = row_at(vl, lo.row[s] + kb * 32 * ROWB);
+    } else {
+      const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
+      o0 = tr_at<ROWB>(kl, lo.tr[db & 1] + (kb * 32 + 16 * t) * ROWB + 64 * db);
+      o1 = o0;
+    }
+  }
+
+  // S^T/dP^T of two 32-key blocks against this wave's 32 queries, their dS,
+  // and dQ^T += K^T dS^T, as one stream of units (LDS operands PREF units
+  // ahead); the dS pairs of block 0 ride under block 1's S/dP units, those of
+  // block 1 under block 0's dQ units.  lo/hi[j]: this lane's allowed-key range
+  // relative to block j's accumulator base (used when MASK).
+  template <bool MASK>
+  static __device__ __forceinline__ void block_pair(const uint8_t* kl, const uint8_t* vl, int kb0, const LaneOffs& lo,
+                                                    const u32x4* qreg, const u32x4* doreg, f32x16* dqacc,
+                                                    const int* mlo, const int* mhi, const ActConsts& k) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, dpacc[2] = {f32x16{}, f32x16{}};
+    u32x4 ds[2][NP][2];
+    u32x4 ring[PREF + 1][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int u = 0; u < PREF; ++u) load_unit(u, kb0, kl, vl, lo, ring[u][0], ring[u][1]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float dsv[2];
+    for (int u = 0; u < NU; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + PREF < NU)
+        load_unit(u + PREF, kb0, kl, vl, lo, ring[(u + PREF) % (PREF + 1)][0], ring[(u + PREF) % (PREF + 1)][1]);
+      const u32x4& o0 = ring[u % (PREF + 1)][0];
+      const u32x4& o1 = ring[u % (PREF + 1)][1];
+      if (u < 2 * NA) {
+        const int j = u / NA, s = u % NA;
+        sacc[j] = mfma_bf16(o0, qreg[s], sacc[j]);
+        dpacc[j] = mfma_bf16(o1, doreg[s], dpacc[j]);
+      } else {
+        const int v = u - 2 * NA, j = v / NB, t = (v % NB) / NDB, db = v % NDB;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * t + 2 * w + u;
-          float dy;
-          (void)Act<ACT>::f_df(sacc[r], a.act, dy);
-          float ds = dpacc[r] * dy;
-          if constexpr (MASK) ds = in_range(r, lo, hi) ? ds : 0.0f;
-          dsv[u] = ds;
+        for (int h = 0; h < NP; ++h) dqacc[db] = mfma_bf16(o0, ds[j][h][t], dqacc[db]);
+      }
+      if (u >= NA && u < 2 * NA + NB) {
+        const int j = u < 2 * NA ? 0 : 1;
+        const int v = u < 2 * NA ? u - NA : u - 2 * NA;
+        const int span = u < 2 * NA ? NA : NB;
+        if (span >= 8) {
+          if (v % (span / 8) == 0) {
+            const int q = v / (span / 8);
+            pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
+          }
+        } else {
+#pragma unroll
+          for (int qq = 0; qq < 8 / span; ++qq) {
+            const int q = v * (8 / span) + qq;
+            pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
+          }
         }
-        dsh[t][w] = pack_bf16x2(dsv[0], dsv[1]);
-        if constexpr (SPLIT) dsl[t][w] = split_lo(dsv[0], dsv[1], dsh[t][w]);
       }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 kta = tr_operand<ROWB>(kl, kb * 32 + 16 * t, db * 32, lane);
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, __builtin_bit_cast(bf16x8, dsh[t]), dqacc[db], 0, 0, 0);
-        if constexpr (SPLIT)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, __builtin_bit_cast(bf16x8, dsl[t]), dqacc[db], 0, 0, 0);
-      }
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
+// Two workgroups per CU, except where exact GELU's gradient needs more
+// registers than two waves per SIMD leave at D = 128.
+template <int D, int ACT>
+constexpr int dq_occupancy() {
+  return (D == 128 && ACT == ACT_GELU) ? 1 : 2;
+}
+
 template <int D, int ACT, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, (dq_occupancy<D, ACT>())) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   using K = DqKernel<D, ACT, SPLIT>;
   constexpr int BM = kBwdBM;
   constexpr int BN = K::BN, NKB = K::NKB, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;
@@ -486,6 +544,7 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
+  const TileOffs<ROWB> loffs = TileOffs<ROWB>::make(lane);
 
   const long kv_ld_b = (long)a.hkv * D * 2;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (long)ks * kv_ld_b + (long)g * D * 2;
@@ -497,27 +556,37 @@ __global__ __launch_bounds__(256, 2) void gdpa_bwd_dq_kernel(const BwdArgs a) {
     stage_tile_buf<BN, ROWB, 4>(krs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, kl, wave, lane);
     stage_tile_buf<BN, ROWB, 4>(vrs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, vl, wave, lane);
   };
-  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) {
+  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
     if (!wave_active) return;
     const int n0 = nb * BN;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int b_lo = n0 + kb * 32, b_hi = b_lo + 31;  // keys of this 32-key block
-      if (b_lo >= lk) break;
-      bool empty = false, full = b_hi < lk;
-      if (a.wr >= 0) {
-        empty |= b_lo > qmax_w + off + a.wr;
-        full &= b_hi <= q0w + off + a.wr;
+    for (int kb0 = 0; kb0 < NKB; kb0 += 2) {
+      // wave-level classification of the two 32-key blocks
+      bool any = false, all_full = true;
+      int mlo[2], mhi[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int b_lo = n0 + (kb0 + j) * 32, b_hi = b_lo + 31;  // keys of this 32-key block
+        bool empty = b_lo >= lk, full = b_hi < lk;
+        if (a.wr >= 0) {
+          empty |= b_lo > qmax_w + off + a.wr;
+          full &= b_hi <= q0w + off + a.wr;
+        }
+        if (a.wl >= 0) {
+          empty |= b_hi < q0w + off - a.wl;
+          full &= b_lo >= qmax_w + off - a.wl;
+        }
+        any |= !empty;
+        all_full &= full;
+        // accumulator element r: key b_lo + 4hf + 8(r/4) + r%4, this lane's query
+        mlo[j] = jlo - (b_lo + hf * 4);
+        mhi[j] = jhi - (b_lo + hf * 4);
       }
-      if (a.wl >= 0) {
-        empty |= b_hi < q0w + off - a.wl;
-        full &= b_lo >= qmax_w + off - a.wl;
-      }
-      if (empty) continue;
-      if (full)
-        K::template block<false>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, 0, 0, a);
+      if (!any) continue;
+      if (all_full)
+        K::template block_pair<false>(kl, vl, kb0, loffs, qreg, doreg, dqacc, mlo, mhi, a.act);
       else
-        K::template block<true>(kl, vl, kb, qreg, doreg, dqacc, lane, n0, jlo, jhi, a);
+        K::template block_pair<true>(kl, vl, kb0, loffs, qreg, doreg, dqacc, mlo, mhi, a.act);
     }
   };
 
