@@ -44,45 +44,6 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
   }
 }
 
-// Per-lane byte offsets of the MFMA operands inside a row-major swizzled
-// [rows][ROWB bytes] LDS tile (the chunk swizzle depends on the row only
-// modulo 8, so one offset per k-step serves every 32-row block, and two serve
-// all transposed reads):
-//   row[s] : A operand of rows (lane % 32) + 32 j, k-step s      (+ 32 j ROWB)
-//   tr[p]  : transposed A operand (ds_read_b64_tr_b16 pair) of head-dim block
-//            db of parity p, tile rows 16 t'                      (+ 16 t' ROWB + 64 db)
-// Keeping just these few registers live, and adding the tile's base and the
-// constant parts per read, leaves the register file to the pipelines.
-template <int ROWB>
-struct TileOffs {
-  static constexpr int KS = ROWB / 32;  // 16-element k-steps per row
-  int row[KS];
-  int tr[2];
-  static __device__ __forceinline__ TileOffs make(int lane) {
-    TileOffs o;
-    const int r = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) o.row[s] = r * ROWB + (((2 * s + hf) ^ chunk_swz<ROWB>(r)) << 4);
-    const int g = lane >> 4, rr = lane & 15;
-    const int rowl = 4 * (g >> 1) + (rr >> 2);  // row within an 8-row group
-    const int x = (2 * (g & 1) + ((rr & 3) >> 1)) ^ chunk_swz<ROWB>(rowl);
-    const int base = rowl * ROWB + (x & 3) * 16 + 8 * (rr & 1);
-    o.tr[0] = base + 64 * (x >> 2);  // even db: chunk 4 db + x
-    o.tr[1] = base - 64 * (x >> 2);  // odd db
-    return o;
-  }
-};
-__device__ __forceinline__ u32x4 row_at(const uint8_t* tile, int off) {
-  return *reinterpret_cast<const u32x4*>(tile + off);
-}
-template <int ROWB>
-__device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, int off) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + off));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) bf16x4*)(tile + (off + 8 * ROWB)));
-  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // ------------------------------------------------------------------ dK / dV
 // Per wave: 32 keys (B operands K, V in registers), per step one 64-row query
 // block of one query head (two 32-row blocks qb = 0, 1):

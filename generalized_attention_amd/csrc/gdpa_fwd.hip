@@ -6,126 +6,142 @@
 // partial sum to O: there is no running maximum, no rescaling and no final
 // division, unlike softmax flash attention.
 //
-// Work decomposition: one workgroup of NW waves per (sequence, query head,
-// BM-row query block), BM = 32 * NQB * NW; wave w owns NQB blocks of 32 query
-// rows.  Per KV tile of BN = 8192/D keys:
+// Work decomposition: one workgroup of 4 waves per (sequence, query head,
+// 128-row query block); wave w owns 32 query rows.  Per KV tile of
+// BN = 8192/D keys:
 //   * K and V are copied HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //     staging), row-major with 16-byte chunks XOR-swizzled by the row index;
 //     tiles are double-buffered, the next tile's copy is in flight while the
 //     current tile is computed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (Q^T stays in registers as the B
-//     operand for the whole loop; each K operand read from LDS feeds the NQB
-//     query blocks), then scale, mask and activation in registers;
+//     operand for the whole loop), then scale, mask and activation in
+//     registers;
 //   * P^T is packed to bf16 straight from the accumulators and is the B
 //     operand of O^T += V^T P^T.  The V^T operand comes from the row-major V
 //     tile through ds_read_b64_tr_b16, whose 16-lane transpose hands each lane
 //     4 consecutive keys of one head-dim column, in exactly the key order of
-//     the accumulator rows; each V^T operand also feeds the NQB query blocks.
-// Query blocks are dispatched last-block-first: for self-attention the late
-// blocks exist only in long sequences and carry the most KV tiles, so the
-// hardware dispatcher sees roughly longest-processing-time-first order (the
-// README's "Features" names load-balanced tile scheduling for jagged inputs).
+//     the accumulator rows.
+// Two 32-key blocks are issued as one interleaved stream so the activation
+// of one block runs on the vector ALU under the other block's MFMAs.
+// Work items are taken (sequence, KV head) pair by pair, each pair's blocks on
+// one XCD, longest sequences first, query blocks last-first (the README's
+// "Features" names load-balanced tile scheduling for jagged inputs).
 #include "gdpa_common.hpp"
 #include "gdpa_kernels.hpp"
 
 namespace gdpa {
 
-template <int D, int ACT, bool FP8, bool PSPLIT, int NW, int NQB>
+template <int D, int ACT, bool FP8, bool PSPLIT, int NW>
 struct FwdKernel {
-  static constexpr int BM = 32 * NQB * NW;
+  static constexpr int BM = 32 * NW;
   static constexpr int BN = 8192 / D;     // keys per KV tile
   static constexpr int NKB = BN / 32;     // 32-key blocks per tile
   static constexpr int KS = D / 16;       // k-steps of Q K^T
   static constexpr int NDB = D / 32;      // 32-row blocks of O^T
   static constexpr int KROWB = FP8 ? D : 2 * D;
   static constexpr int VROWB = 2 * D;
-  static constexpr int NQR = FP8 ? 1 : KS;   // bf16 Q registers per query block
-  static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers per query block
+  static constexpr int NQR = FP8 ? 1 : KS;   // bf16 Q registers
+  static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers
+  static constexpr int NP = PSPLIT ? 2 : 1;  // bf16 words per P element (hi, lo)
+  static constexpr int NA = KS;              // S units per key block (1 MFMA each)
+  static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
+  static constexpr int NU = 2 * NA + 2 * NB;
+  static constexpr int PREF = 2;             // units of operand prefetch
+  using KOffs = TileOffs<2 * D>;             // bf16 K rows and V rows (both 2D bytes)
 
-  // One KV tile for this wave: S^T = K Q^T, P = act(S) (masked to each
-  // lane's [jlo, jhi] when MASK), O^T += V^T P^T.  qact: query blocks with at
-  // least one valid row.
+  // One pair of accumulator elements (key rows 8t+2w, +1) -> packed P words.
   template <bool MASK>
-  static __device__ __forceinline__ void tile(const uint8_t* kl, const uint8_t* vl, const u32x4 (*qreg)[NQR],
-                                              const u32x2 (*qreg8)[NQR8], f32x16 (*oacc)[NDB], int lane, int n0,
-                                              const int* jlo, const int* jhi, int qact, const FwdArgs& a) {
-    const int hf = lane >> 5;
-    f32x16 sacc[NQB][NKB];
+  static __device__ __forceinline__ void pair(const f32x16& s, int t, int w, int lo, int hi, u32x4 (*p)[2],
+                                              const ActConsts& k) {
+    float y[2];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * t + 2 * w + u;
+      float v = Act<ACT>::f(s[r], k);
+      if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
+      y[u] = v;
+    }
+    const uint32_t h2 = pack_bf16x2(y[0], y[1]);
+    p[0][t][w] = h2;
+    if constexpr (PSPLIT) p[1][t][w] = split_lo(y[0], y[1], h2);
+  }
+
+  // Unit u of a key-block pair (blocks kb0, kb0+1): u < 2 NA: S of block
+  // u / NA, k-step u % NA (A operand: K rows); else P V of block
+  // (u - 2 NA) / NB, key-row half t, head-dim block db (A operand: V^T).
+  static __device__ __forceinline__ u32x4 load_unit(int u, int kb0, const uint8_t* kl, const uint8_t* vl,
+                                                    const KOffs& lo, int lane) {
+    if (u < 2 * NA) {
+      const int kb = kb0 + u / NA, s = u % NA;
+      if constexpr (FP8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(kb * 32 + (lane & 31), s) +
+                                                         (lane >> 5) * 8);
+        return u32x4{v[0], v[1], 0u, 0u};
+      } else {
+        return row_at(kl, lo.row[s] + kb * 32 * KROWB);
+      }
+    }
+    const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
+    return tr_at<VROWB>(vl, lo.tr[db & 1] + (kb * 32 + 16 * t) * VROWB + 64 * db);
+  }
+
+  // S^T = K Q^T of two 32-key blocks against this wave's 32 queries, P =
+  // act(S) (masked to each lane's allowed keys when MASK), and O^T += V^T P^T,
+  // as one stream of units whose LDS operands are read PREF units ahead; the
+  // activation of block 0 rides under block 1's S units, that of block 1
+  // under block 0's P V units.  mlo/mhi[j]: this lane's allowed-key range
+  // relative to block j's accumulator base.
+  template <bool MASK>
+  static __device__ __forceinline__ void block_pair(const uint8_t* kl, const uint8_t* vl, int kb0, const KOffs& lo,
+                                                    int lane, const u32x4* qreg, const u32x2* qreg8, f32x16* oacc,
+                                                    const int* mlo, const int* mhi, const ActConsts& k) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    u32x4 p[2][NP][2];
+    u32x4 ring[PREF + 1];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[qb][kb] = f32x16{};
+    for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, lane);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int u = 0; u < NU; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + PREF < NU) ring[(u + PREF) % (PREF + 1)] = load_unit(u + PREF, kb0, kl, vl, lo, lane);
+      const u32x4& op = ring[u % (PREF + 1)];
+      if (u < 2 * NA) {
+        const int j = u / NA, s = u % NA;
+        if constexpr (FP8)
+          sacc[j] = mfma_fp8(u32x2{op[0], op[1]}, qreg8[s], sacc[j]);
+        else
+          sacc[j] = mfma_bf16(op, qreg[s], sacc[j]);
+      } else {
+        const int v = u - 2 * NA, j = v / NB, t = (v % NB) / NDB, db = v % NDB;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int row = kb * 32 + (lane & 31);
-        if constexpr (FP8) {
-          const u32x2 aop = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(row, s) + hf * 8);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            if (qb < qact) sacc[qb][kb] = mfma_fp8(aop, qreg8[qb][s], sacc[qb][kb]);
+        for (int h = 0; h < NP; ++h) oacc[db] = mfma_bf16(op, p[j][h][t], oacc[db]);
+      }
+      if (u >= NA && u < 2 * NA + NB) {
+        const int j = u < 2 * NA ? 0 : 1;
+        const int v = u < 2 * NA ? u - NA : u - 2 * NA;
+        const int span = u < 2 * NA ? NA : NB;
+        if (span >= 8) {
+          if (v % (span / 8) == 0) {
+            const int q = v / (span / 8);
+            pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
+          }
         } else {
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, 2 * s + hf));
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            if (qb < qact) sacc[qb][kb] = mfma_bf16(aop, qreg[qb][s], sacc[qb][kb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      // V^T operands of this 32-key block, read (transposed) from the row-major
-      // V tile before the activation so the LDS latency hides behind it.
-      bf16x8 vop[2][NDB];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vop[t][db] = tr_operand<VROWB>(vl, kb * 32 + 16 * t, db * 32, lane);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        if (qb >= qact) continue;
-        // allowed keys of this lane relative to the block's first key for this lane
-        const int base = n0 + kb * 32 + hf * 4;
-        const int lo = jlo[qb] - base, hi = jhi[qb] - base;
-        u32x4 phi[2], plo[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            float y[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int r = 8 * t + 2 * w + u;
-              float v = Act<ACT>::f(sacc[qb][kb][r], a.act);
-              if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
-              y[u] = v;
-            }
-            const uint32_t hi2 = pack_bf16x2(y[0], y[1]);
-            phi[t][w] = hi2;
-            if constexpr (PSPLIT) plo[t][w] = split_lo(y[0], y[1], hi2);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, phi[t]),
-                                                                   oacc[qb][db], 0, 0, 0);
-            if constexpr (PSPLIT)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], __builtin_bit_cast(bf16x8, plo[t]),
-                                                                     oacc[qb][db], 0, 0, 0);
+          for (int qq = 0; qq < 8 / span; ++qq) {
+            const int q = v * (8 / span) + qq;
+            pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
           }
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
-template <int D, int ACT, bool FP8, bool PSPLIT, int NW, int NQB>
+template <int D, int ACT, bool FP8, bool PSPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
-  using K = FwdKernel<D, ACT, FP8, PSPLIT, NW, NQB>;
-  constexpr int BM = K::BM, BN = K::BN, KS = K::KS, NDB = K::NDB;
+  using K = FwdKernel<D, ACT, FP8, PSPLIT, NW>;
+  constexpr int BM = K::BM, BN = K::BN, KS = K::KS, NDB = K::NDB, NKB = K::NKB;
   constexpr int KBYTES = BN * K::KROWB, VBYTES = BN * K::VROWB;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KBYTES];
@@ -160,43 +176,36 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const int nb_begin = j_lo / BN;
   const int nb_end = (j_hi > j_lo) ? (j_hi + BN - 1) / BN : nb_begin;
 
-  const int q0w = row0 + wave * 32 * NQB;  // first query row of this wave
+  const int q0w = row0 + wave * 32;  // first query row of this wave
   const bool wave_active = q0w < lq;
-  const int qmax_w = min(q0w + 32 * NQB - 1, lq - 1);
-  const int qact = min(NQB, (lq - q0w + 31) / 32);  // query blocks with valid rows
+  const int qmax_w = min(q0w + 31, lq - 1);
   const int hf = lane >> 5;
-  int qi[NQB], jlo[NQB], jhi[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    qi[qb] = q0w + qb * 32 + (lane & 31);
-    // keys this lane's query may see: [jlo, jhi]
-    jlo[qb] = a.wl >= 0 ? qi[qb] + off - a.wl : 0;
-    jhi[qb] = min(lk - 1, a.wr >= 0 ? qi[qb] + off + a.wr : lk - 1);
-  }
+  const int qi = q0w + (lane & 31);
+  // keys this lane's query may see: [jlo, jhi]
+  const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
+  const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step.
   const long q_ld = (long)a.hq * D;
-  u32x4 qreg[NQB][K::NQR];
-  u32x2 qreg8[NQB][K::NQR8];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const long qrow = (long)(qs + min(qi[qb], lq - 1)) * q_ld + h * D + hf * 8;
+  u32x4 qreg[K::NQR];
+  u32x2 qreg8[K::NQR8];
+  {
+    const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
     if constexpr (FP8) {
       const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qreg8[qb][s] = load8_or_zero(qp + s * 16, qi[qb] < lq);
+      for (int s = 0; s < KS; ++s) qreg8[s] = load8_or_zero(qp + s * 16, qi < lq);
     } else {
       const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qreg[qb][s] = load16_or_zero(qp + s * 16, qi[qb] < lq);
+      for (int s = 0; s < KS; ++s) qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
     }
   }
 
-  f32x16 oacc[NQB][NDB];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[qb][i] = f32x16{};
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  const typename K::KOffs loffs = K::KOffs::make(lane);
 
   const int esz = FP8 ? 1 : 2;
   const long kv_ld = (long)a.hkv * D;
@@ -212,24 +221,39 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
     stage_tile_buf<BN, K::KROWB, NW>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0, kl, wave, lane);
     stage_tile_buf<BN, K::VROWB, NW>(vrs, n0 * (int)kv_ld * 2, (int)kv_ld * 2, lk - n0, vl, wave, lane);
   };
-  // One tile of math for this wave; the mask is applied only where the
-  // window cuts the tile or the tile runs past the last key.
-  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) {
+  // One tile of math for this wave, two 32-key blocks at a time; the mask is
+  // applied only where the window cuts a block or a block runs past the last key.
+  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
+    if (!wave_active) return;
     const int n0 = nb * BN;
-    bool empty = false, full = n0 + BN <= lk;
-    if (a.wr >= 0) {
-      empty |= n0 > qmax_w + off + a.wr;
-      full &= n0 + BN - 1 <= q0w + off + a.wr;
+#pragma unroll
+    for (int kb0 = 0; kb0 < NKB; kb0 += 2) {
+      bool any = false, all_full = true;
+      int mlo[2], mhi[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int b_lo = n0 + (kb0 + j) * 32, b_hi = b_lo + 31;  // keys of this 32-key block
+        bool empty = b_lo >= lk, full = b_hi < lk;
+        if (a.wr >= 0) {
+          empty |= b_lo > qmax_w + off + a.wr;
+          full &= b_hi <= q0w + off + a.wr;
+        }
+        if (a.wl >= 0) {
+          empty |= b_hi < q0w + off - a.wl;
+          full &= b_lo >= qmax_w + off - a.wl;
+        }
+        any |= !empty;
+        all_full &= full;
+        // accumulator element r: key b_lo + 4hf + 8(r/4) + r%4, this lane's query
+        mlo[j] = jlo - (b_lo + hf * 4);
+        mhi[j] = jhi - (b_lo + hf * 4);
+      }
+      if (!any) continue;
+      if (all_full)
+        K::template block_pair<false>(kl, vl, kb0, loffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
+      else
+        K::template block_pair<true>(kl, vl, kb0, loffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
     }
-    if (a.wl >= 0) {
-      empty |= n0 + BN - 1 < q0w + off - a.wl;
-      full &= n0 >= qmax_w + off - a.wl;
-    }
-    if (!wave_active || empty) return;
-    if (full)
-      K::template tile<false>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, qact, a);
-    else
-      K::template tile<true>(kl, vl, qreg, qreg8, oacc, lane, n0, jlo, jhi, qact, a);
   };
 
   if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
@@ -248,24 +272,20 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   }
 
   // ---- epilogue: lane stores 4 consecutive head-dim values per register group
-  if (!wave_active) return;
+  if (!wave_active || qi >= lq) return;
+  const long orow = ((long)(qs + qi) * a.hq + h) * D;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    if (qi[qb] >= lq) continue;
-    const long orow = ((long)(qs + qi[qb]) * a.hq + h) * D;
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + hf * 4 + 8 * i4;
-        const float ps = a.act.pscale;
-        const float o0 = oacc[qb][db][4 * i4] * ps, o1 = oacc[qb][db][4 * i4 + 1] * ps;
-        const float o2 = oacc[qb][db][4 * i4 + 2] * ps, o3 = oacc[qb][db][4 * i4 + 3] * ps;
-        if (a.out_f32)
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = f32x4{o0, o1, o2, o3};
-        else
-          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-      }
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = db * 32 + hf * 4 + 8 * i4;
+      const float ps = a.act.pscale;
+      const float o0 = oacc[db][4 * i4] * ps, o1 = oacc[db][4 * i4 + 1] * ps;
+      const float o2 = oacc[db][4 * i4 + 2] * ps, o3 = oacc[db][4 * i4 + 3] * ps;
+      if (a.out_f32)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = f32x4{o0, o1, o2, o3};
+      else
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     }
   }
   };
@@ -284,9 +304,9 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
 #define GDPA_FWD_CASE(K)                                                                                  \
   case K:                                                                                                 \
     if (a.psplit)                                                                                         \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, true, kFwdNW, kFwdNQB>), g, blk, 0, stream, a);      \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, true, kFwdNW>), g, blk, 0, stream, a);      \
     else                                                                                                  \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, false, kFwdNW, kFwdNQB>), g, blk, 0, stream, a);     \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, FP8, false, kFwdNW>), g, blk, 0, stream, a);     \
     break;
     GDPA_FWD_CASE(ACT_IDENTITY)
     GDPA_FWD_CASE(ACT_GELU)

@@ -87,9 +87,9 @@ struct BwdArgs {
   int32_t ncu;          // compute units of the device (sizes the work-queue launches)
 };
 
-// Forward workgroup shape: kFwdNW waves, each owning kFwdNQB blocks of 32 query rows.
-constexpr int kFwdNW = 4, kFwdNQB = 1;
-constexpr int kFwdBM = 32 * kFwdNW * kFwdNQB;
+// Forward workgroup: kFwdNW waves, each owning 32 query rows.
+constexpr int kFwdNW = 4;
+constexpr int kFwdBM = 32 * kFwdNW;
 // XCDs per MI355X; workgroup ids are dealt to them round-robin.
 constexpr int kNumXcd = 8;
 
