@@ -70,8 +70,13 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
     from threadpoolctl import threadpool_info
     wl = bt.wl
     pairs = workload_pairs(bt)
-    q, k, v, do = (oracle.decode_bf16(bt.q), oracle.decode_bf16(bt.k), oracle.decode_bf16(bt.v),
-                   oracle.decode_bf16(bt.do))
+    with_bwd = not wl.fp8_qk
+    if wl.fp8_qk:
+        q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
+    else:
+        q, k = oracle.decode_bf16(bt.q), oracle.decode_bf16(bt.k)
+    v = oracle.decode_bf16(bt.v)
+    do = oracle.decode_bf16(bt.do) if with_bwd else None
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
     t_total, flops, nseq = 0.0, 0, 0
     for b in range(wl.batch):
@@ -80,15 +85,16 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
         kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
         t0 = time.perf_counter()
         oracle.gdpa_forward(q[sq], k[sk], v[sk], lcq, lck, wl.scale, wl.act, **kw)
-        oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck, wl.scale, wl.act, **kw)
+        if with_bwd:
+            oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck, wl.scale, wl.act, **kw)
         t_total += time.perf_counter() - t0
-        flops += 14 * wl.head_dim * int(pairs[b])
+        flops += (14 if with_bwd else 4) * wl.head_dim * int(pairs[b])
         nseq += 1
         if t_total >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, forward+backward of the first {nseq} of {wl.batch} sequences "
+            "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of the first {nseq} of {wl.batch} sequences "
                       f"({flops / 1e9:.1f} GFLOP algorithmic) in {t_total:.1f} s"}
 
 
@@ -139,14 +145,17 @@ def main():
     import generalized_attention_amd as g
 
     wl = gi.WORKLOADS[args.workload]
-    if not wl.backward:
+    # FP8 Q/K is a forward-only path (the README's FP8 support is inference);
+    # every bf16 workload is timed forward + backward
+    with_bwd = not wl.fp8_qk
+    if with_bwd and not wl.backward:
         wl = gi.dataclasses.replace(wl, backward=True)
     print(f"[bench] drawing {wl.name} (seed {wl.seed})", file=sys.stderr, flush=True)
     bt = gi.make_batch(wl)
     pairs = workload_pairs(bt)
     P = int(pairs.sum())
     D = wl.head_dim
-    fwd_flops, bwd_flops = 4 * D * P, 10 * D * P
+    fwd_flops, bwd_flops = 4 * D * P, (10 * D * P if with_bwd else 0)
 
     def dev(a, kind):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -154,7 +163,8 @@ def main():
         return t.cuda()
 
     qk = "fp8" if wl.fp8_qk else "bf16"
-    q, k, v, do = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, "bf16"), dev(bt.do, "bf16")
+    q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, "bf16")
+    do = dev(bt.do, "bf16") if with_bwd else None
     cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
     o = torch.empty(q.shape[0], wl.heads_q, D, dtype=torch.float32, device="cuda")
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
@@ -174,7 +184,8 @@ def main():
 
     def step():
         fwd()
-        bwd()
+        if with_bwd:
+            bwd()
 
     for _ in range(args.warmup):
         step()
@@ -200,14 +211,29 @@ def main():
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
-    kern = {
-        "gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 4 * D * P),
-        "gdpa_bwd_dkdv_kernel": (avg_ms(lambda: bwd(False, True), args.kernel_reps), 8 * D * P),
-        "gdpa_bwd_dq_kernel": (avg_ms(lambda: bwd(True, False), args.kernel_reps), 2 * D * P),
-    }
+    # algorithmic work per launch: flops of the products the gradient needs
+    # (S, dP, dV, dK in the dK/dV kernel, dQ in the dQ kernel; the dQ kernel's
+    # recomputed S and dP are not counted) and the bytes each kernel must move
+    # at least (every input read once, every output written once)
+    isz = {"q": q.element_size(), "k": k.element_size(), "v": 2, "do": 2, "out": 4}
+    tq, tk = q.shape[0], k.shape[0]
+    nq, nkv = tq * wl.heads_q * D, tk * wl.heads_kv * D
+    kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 4 * D * P,
+                                nq * isz["q"] + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])}
+    if with_bwd:
+        kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps), 8 * D * P,
+                                        nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + 2 * nkv * isz["out"])
+        kern["gdpa_bwd_dq_kernel"] = (avg_ms(lambda: bwd(True, False), args.kernel_reps), 2 * D * P,
+                                      nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])
     dom = max(kern, key=lambda n: kern[n][0])
-    dom_ms, dom_flops = kern[dom]
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    dom_ms, dom_flops, dom_bytes = kern[dom]
+    # the roof that binds: the larger of the MFMA and HBM fractions
+    mfma_tf = dom_flops / (dom_ms * 1e-3) / 1e12
+    hbm_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    if hbm_gbs / HBM_PEAK_GBS > mfma_tf / BF16_PEAK_TFLOPS:
+        bound, achieved, peak, unit = "hbm", hbm_gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", mfma_tf, BF16_PEAK_TFLOPS, "TFLOP/s"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -233,15 +259,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.batch} sequences, lengths U[{wl.lq_range[0]},{wl.lq_range[1]}] "
                                f"(drawn total {int(bt.seqlens_q.sum())} tokens), Hq={wl.heads_q}, "
-                               f"Hkv={wl.heads_kv}, D={D}, act={wl.act}, mask={wl.mask}, fwd+bwd, fp32 outputs",
+                               f"Hkv={wl.heads_kv}, D={D}, act={wl.act}, mask={wl.mask}, "
+                               f"{'fwd+bwd' if with_bwd else 'fwd'}, fp32 outputs",
                    "global_batch": wl.batch, "seq_len": int(bt.max_seqlen_q), "parallelism": "none (1 GPU)"},
         "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "fwd_tflops": round(fwd_flops / (kern["gdpa_fwd_kernel"][0] * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(bwd_flops / ((kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]) * 1e-3)
-                            / 1e12, 2),
-        "kernel_ms": {n: round(t, 4) for n, (t, _) in kern.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "bwd_tflops": (round(bwd_flops / ((kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]) * 1e-3)
+                             / 1e12, 2) if with_bwd else None),
+        "kernel_ms": {n: round(t[0], 4) for n, t in kern.items()},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
