@@ -18,13 +18,30 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
                                                              int32_t* perm, int32_t* counters) {
   __shared__ uint64_t key[kSortMax];
   if (threadIdx.x < kNumCounters) counters[threadIdx.x] = 0;
+  auto make_key = [&](int i) {
+    const int64_t len = (int64_t)(cu_q[i + 1] - cu_q[i]) + (cu_k[i + 1] - cu_k[i]);
+    const uint64_t inv = (uint64_t)(0xffffffffLL - (len < 0xffffffffLL ? len : 0xffffffffLL));
+    return (inv << 32) | (uint32_t)i;  // ascending key = descending length, then index
+  };
+  if (blockDim.x == 64) {
+    // up to 64 sequences: the same network across the lanes of one wave
+    const int i = threadIdx.x;
+    uint64_t x = i < batch ? make_key(i) : ~0ull;
+    for (int k = 2; k <= 64; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint64_t y = __shfl_xor(x, j, 64);
+        const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+        x = take_min ? (x < y ? x : y) : (x < y ? y : x);
+      }
+    }
+    if (i < batch) perm[i] = (int32_t)(uint32_t)x;
+    return;
+  }
   int n = 1;
   while (n < batch) n <<= 1;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     if (i < batch) {
-      const int64_t len = (int64_t)(cu_q[i + 1] - cu_q[i]) + (cu_k[i + 1] - cu_k[i]);
-      const uint64_t inv = (uint64_t)(0xffffffffLL - (len < 0xffffffffLL ? len : 0xffffffffLL));
-      key[i] = (inv << 32) | (uint32_t)i;  // ascending key = descending length, then index
+      key[i] = make_key(i);
     } else {
       key[i] = ~0ull;  // padding sorts last
     }
@@ -52,9 +69,13 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
 hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
                            hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
-  // one compare-exchange per thread and stage: small batches sort in one wave
+  // up to 64 sequences sort in registers across one wave; larger batches in
+  // LDS, one compare-exchange per thread and stage
   int threads = 64;
-  while (threads < 1024 && 2 * threads < batch) threads <<= 1;
+  if (batch > 64) {
+    threads = 128;
+    while (threads < 1024 && 2 * threads < batch) threads <<= 1;
+  }
   hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(threads), 0, stream, cu_q, cu_k, batch, perm, counters);
   return hipGetLastError();
 }

@@ -224,3 +224,13 @@ def test_batch_beyond_schedule_limit(g):
     assert g._lib.gdpa_varlen_fwd_workspace_size(len(lens), 5, 5, 2, 1, 64) == 0
     check_forward(g, bt)
     check_backward(g, bt)
+
+
+def test_batch_sorted_in_lds(g):
+    # 65..4096 sequences take the schedule's LDS sort (64 or fewer sort across one wave)
+    rng = np.random.default_rng(9)
+    lens = rng.integers(0, 41, size=300)
+    wl = _wl(act="silu", head_dim=64, heads_q=2, heads_kv=1, batch=len(lens))
+    bt = gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens)
+    check_forward(g, bt)
+    check_backward(g, bt)
