@@ -126,8 +126,9 @@ struct Act<ACT_SILU> {
   }
   static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
     const float r = fast_rcp(1.0f + fast_exp2(k.k0 * s));
-    d = __builtin_fmaf(r * (1.0f - r), k.a0 * s, r);
-    return s * r;
+    const float y = s * r;
+    d = __builtin_fmaf(k.a0 * y, 1.0f - r, r);  // r + r (1 - r) a0 s, reusing y = s r
+    return y;
   }
 };
 
@@ -139,8 +140,9 @@ struct Act<ACT_GELU_TANH> {
   static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
     const float s2 = s * s;
     const float r = fast_rcp(1.0f + fast_exp2(s * __builtin_fmaf(k.k1, s2, k.k0)));
-    d = __builtin_fmaf(r * (1.0f - r), s * __builtin_fmaf(k.a1, s2, k.a0), r);
-    return s * r;
+    const float y = s * r;
+    d = __builtin_fmaf(y * __builtin_fmaf(k.a1, s2, k.a0), 1.0f - r, r);  // reusing y = s r
+    return y;
   }
 };
 
