@@ -114,9 +114,9 @@ struct DkdvKernel {
       o1 = row_at(dl, lo.row[s] + qb * 32 * ROWB);
     } else {
       const int v = u - 2 * NA, qb = v / NB, t = (v % NB) / NDB, db = v % NDB;
-      const int off = lo.tr[db & 1] + (qb * 32 + 16 * t) * ROWB + 64 * db;
-      o0 = tr_at<ROWB>(dl, off);
-      o1 = tr_at<ROWB>(ql, off);
+      const int base = (qb * 32 + 16 * t) * ROWB;
+      o0 = tr_at(dl, lo.tr[db], base);
+      o1 = tr_at(ql, lo.tr[db], base);
     }
   }
   static __device__ __forceinline__ void mma_unit(int u, const u32x4& o0, const u32x4& o1, const u32x4* kreg,
@@ -389,7 +389,7 @@ struct DqKernel {
       o1 = row_at(vl, lo.row[s] + kb * 32 * ROWB);
     } else {
       const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
-      o0 = tr_at<ROWB>(kl, lo.tr[db & 1] + (kb * 32 + 16 * t) * ROWB + 64 * db);
+      o0 = tr_at(kl, lo.tr[db], (kb * 32 + 16 * t) * ROWB);
       o1 = o0;
     }
   }

@@ -196,14 +196,18 @@ __device__ __forceinline__ u32x2 load8_or_zero(const void* p, bool valid) {
 // Row-major [rows][ROWB bytes] tiles written by LDS-direct 16-byte loads: each
 // lane's 16 bytes land at (LDS base of the instruction) + 16 * lane, so the
 // chunk swizzle is chosen by picking which source chunk each lane fetches.
-// Chunk swizzle f(row) for rows of >= 128 bytes: f maps rows 8m..8m+7 onto
-// distinct chunks (row-wise 16-byte reads of 8 consecutive rows are
-// conflict-free) and rows 4m..4m+3 onto distinct chunk pairs (the 4 rows x
-// 32 bytes a 16-lane group touches in a transposing read cover all 32 banks).
-// 64-byte rows (FP8 K at D = 64) pair rows per bank sweep instead.
+// Chunk swizzle f(row).  gfx950's LDS has 64 four-byte banks: a ds_read_b128
+// serves 16 lanes per cycle and a ds_read_b64_tr_b16 32 lanes (4 rows x 64
+// bytes).  f is a bijection on rows 16m..16m+15 modulo the 256-byte bank
+// sweep (16 consecutive rows read row-wise at one chunk hit 16 distinct
+// bank quads), and for rows of >= 128 bytes its upper bits put the 64-byte
+// column blocks of 4 consecutive rows in distinct quarters of the sweep (a
+// transposing read is conflict-free too).  f has period 16 in the row.
 template <int ROWB>
 __device__ __forceinline__ int chunk_swz(int row) {
-  return (ROWB >= 128) ? (((row & 3) << 1) | ((row >> 2) & 1)) : ((row >> 1) & 3);
+  if constexpr (ROWB >= 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (ROWB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return (row >> 2) & 3;
 }
 template <int ROWB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk
@@ -289,41 +293,45 @@ __device__ __forceinline__ u32x4 row_operand(const uint8_t* tile, int row_base, 
 }
 
 // Per-lane byte offsets of the MFMA operands inside a row-major swizzled
-// [rows][ROWB bytes] LDS tile (the chunk swizzle depends on the row only
-// modulo 8, so one offset per k-step serves every 32-row block, and two serve
-// all transposed reads):
-//   row[s] : A operand of rows (lane % 32) + 32 j, k-step s      (+ 32 j ROWB)
-//   tr[p]  : transposed A operand (ds_read_b64_tr_b16 pair) of head-dim block
-//            db of parity p, tile rows 16 t'                      (+ 16 t' ROWB + 64 db)
+// [rows][ROWB bytes] LDS tile (the chunk swizzle has period 16 in the row, so
+// one offset per k-step serves every 32-row block and one pair per head-dim
+// block every 16-row group):
+//   row[s]     : A operand of rows (lane % 32) + 32 j, k-step s     (+ 32 j ROWB)
+//   tr[db][c]  : transposed A operand (ds_read_b64_tr_b16 pair, half c) of
+//                head-dim block db, tile rows 16 t'                 (+ 16 t' ROWB)
 // Keeping just these few registers live, and adding the tile's base and the
 // constant parts per read, leaves the register file to the pipelines.
 template <int ROWB>
 struct TileOffs {
-  static constexpr int KS = ROWB / 32;  // 16-element k-steps per row
+  static constexpr int KS = ROWB / 32;   // 16-element k-steps per row
+  static constexpr int NDB = ROWB / 64;  // 32-column head-dim blocks per row
   int row[KS];
-  int tr[2];
+  int tr[NDB][2];
   static __device__ __forceinline__ TileOffs make(int lane) {
     TileOffs o;
     const int r = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int s = 0; s < KS; ++s) o.row[s] = r * ROWB + (((2 * s + hf) ^ chunk_swz<ROWB>(r)) << 4);
     const int g = lane >> 4, rr = lane & 15;
-    const int rowl = 4 * (g >> 1) + (rr >> 2);  // row within an 8-row group
-    const int x = (2 * (g & 1) + ((rr & 3) >> 1)) ^ chunk_swz<ROWB>(rowl);
-    const int base = rowl * ROWB + (x & 3) * 16 + 8 * (rr & 1);
-    o.tr[0] = base + 64 * (x >> 2);  // even db: chunk 4 db + x
-    o.tr[1] = base - 64 * (x >> 2);  // odd db
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 8 * c + 4 * (g >> 1) + (rr >> 2);
+        const int col = 32 * db + 16 * (g & 1) + 4 * (rr & 3);
+        o.tr[db][c] = row * ROWB + (((col >> 3) ^ chunk_swz<ROWB>(row)) << 4) + ((col & 4) << 1);
+      }
     return o;
   }
 };
 __device__ __forceinline__ u32x4 row_at(const uint8_t* tile, int off) {
   return *reinterpret_cast<const u32x4*>(tile + off);
 }
-template <int ROWB>
-__device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, int off) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + off));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) bf16x4*)(tile + (off + 8 * ROWB)));
+// Transposed operand of a 16-row group: base = byte offset of the group's
+// first row, o = the lane's TileOffs pair of the head-dim block.
+__device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, const int (&o)[2], int base) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + (o[0] + base)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(tile + (o[1] + base)));
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

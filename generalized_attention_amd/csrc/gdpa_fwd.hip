@@ -82,7 +82,7 @@ struct FwdKernel {
       }
     }
     const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
-    return tr_at<VROWB>(vl, lo.tr[db & 1] + (kb * 32 + 16 * t) * VROWB + 64 * db);
+    return tr_at(vl, lo.tr[db], (kb * 32 + 16 * t) * VROWB);
   }
 
   // S^T = K Q^T of two 32-key blocks against this wave's 32 queries, P =
