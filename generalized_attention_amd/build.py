@@ -16,6 +16,11 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdpa.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched.hip", "gdpa_api.cpp"]
+# Per-source code generation options.  The forward kernels keep their MFMA
+# accumulators in architectural VGPRs (the activation reads the S tile with
+# no accumulator-to-VGPR copies; the register file still fits two workgroups
+# per CU).
+EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -35,7 +40,7 @@ def _flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + _flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
