@@ -71,12 +71,13 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
     wl = bt.wl
     pairs = workload_pairs(bt)
     with_bwd = not wl.fp8_qk
+    dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
     if wl.fp8_qk:
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
     else:
-        q, k = oracle.decode_bf16(bt.q), oracle.decode_bf16(bt.k)
-    v = oracle.decode_bf16(bt.v)
-    do = oracle.decode_bf16(bt.do) if with_bwd else None
+        q, k = dec(bt.q), dec(bt.k)
+    v = dec(bt.v)
+    do = dec(bt.do) if with_bwd else None
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
     t_total, flops, nseq = 0.0, 0, 0
     for b in range(wl.batch):
@@ -159,12 +160,14 @@ def main():
 
     def dev(a, kind):
         t = torch.from_numpy(np.ascontiguousarray(a))
-        t = t.view(torch.int16).view(torch.bfloat16) if kind == "bf16" else t.view(torch.float8_e4m3fn)
+        views = {"bf16": torch.bfloat16, "fp16": torch.float16}
+        t = t.view(torch.int16).view(views[kind]) if kind in views else t.view(torch.float8_e4m3fn)
         return t.cuda()
 
-    qk = "fp8" if wl.fp8_qk else "bf16"
-    q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, "bf16")
-    do = dev(bt.do, "bf16") if with_bwd else None
+    e16 = "fp16" if wl.fp16 else "bf16"
+    qk = "fp8" if wl.fp8_qk else e16
+    q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, e16)
+    do = dev(bt.do, e16) if with_bwd else None
     cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
     o = torch.empty(q.shape[0], wl.heads_q, D, dtype=torch.float32, device="cuda")
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
@@ -255,7 +258,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f8" if wl.fp8_qk else "bf16",
+        "dtype": "f8" if wl.fp8_qk else e16,
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.batch} sequences, lengths U[{wl.lq_range[0]},{wl.lq_range[1]}] "
                                f"(drawn total {int(bt.seqlens_q.sum())} tokens), Hq={wl.heads_q}, "

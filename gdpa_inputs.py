@@ -45,6 +45,7 @@ class Workload:
     window_left: int = -1    # -1 = unbounded
     window_right: int = -1
     fp8_qk: bool = False
+    fp16: bool = False       # fp16 Q/K/V/dO instead of bf16
     backward: bool = False
     varlen: bool = True      # False: fixed-length [B, L, H, D] API
     seed: int = 0
@@ -66,6 +67,8 @@ WORKLOADS = {
                           "silu", backward=True, varlen=False, seed=3),
     "short_kv_cross": Workload("short_kv_cross", 512, 4, 4, 128, (256, 2048),
                                (64, 64), "relu2", backward=True, seed=4),
+    "jagged_self_fp16": Workload("jagged_self_fp16", 64, 4, 4, 128, (1, 1024), None,
+                                 "fast_gelu", fp16=True, backward=True, seed=2),
     "window_gqa_fp8": Workload("window_gqa_fp8", 16, 16, 4, 64, (1024, 4096),
                                None, "leaky_relu", act_param=0.01,
                                mask="window", window_left=511, window_right=0,
@@ -84,6 +87,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     r += 0x7FFF
     r >>= 16
     return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (round to nearest even) and return uint16 bits."""
+    return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
 
 
 def quantize_e4m3(x: np.ndarray):
@@ -110,10 +118,10 @@ class Batch:
     seqlens_k: np.ndarray     # int64 [B]
     cu_seqlens_q: np.ndarray  # int32 [B+1]
     cu_seqlens_k: np.ndarray  # int32 [B+1]
-    q: np.ndarray             # uint16 bf16 bits, or uint8 E4M3 codes  [total_q, Hq, D]
-    k: np.ndarray             # same format as q                        [total_k, Hkv, D]
-    v: np.ndarray             # uint16 bf16 bits                        [total_k, Hkv, D]
-    do: Optional[np.ndarray]  # uint16 bf16 bits                        [total_q, Hq, D]
+    q: np.ndarray             # uint16 bf16/fp16 bits, or uint8 E4M3 codes  [total_q, Hq, D]
+    k: np.ndarray             # same format as q                             [total_k, Hkv, D]
+    v: np.ndarray             # uint16 bf16/fp16 bits                        [total_k, Hkv, D]
+    do: Optional[np.ndarray]  # uint16, same format as v                     [total_q, Hq, D]
     q_scale: float = 1.0      # per-tensor scale of q codes (fp8 only)
     k_scale: float = 1.0
 
@@ -139,7 +147,7 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool]
 
     Draw order: Q lengths, KV lengths (if drawn), then Q, K, V, dO as float32
     N(0,1).  Q/K are quantised to E4M3 for FP8 workloads, everything else is
-    rounded to bf16.  Explicit `seqlens_q`/`seqlens_k` override the draws.
+    rounded to bf16 (fp16 for fp16 workloads).  Explicit `seqlens_q`/`seqlens_k` override the draws.
     """
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     lq = draw_lengths(rng, wl.batch, wl.lq_range) if seqlens_q is None else np.asarray(seqlens_q, np.int64)
@@ -162,13 +170,14 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool]
     want_do = wl.backward if with_do is None else with_do
     dof = rng.standard_normal((tq, H, D), dtype=np.float32) if want_do else None
     qs = ks = 1.0
+    enc = f32_to_f16_bits if wl.fp16 else f32_to_bf16_bits
     if wl.fp8_qk:
         q, qs = quantize_e4m3(qf)
         k, ks = quantize_e4m3(kf)
     else:
-        q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
-    v = f32_to_bf16_bits(vf)
-    do = f32_to_bf16_bits(dof) if dof is not None else None
+        q, k = enc(qf), enc(kf)
+    v = enc(vf)
+    do = enc(dof) if dof is not None else None
     return Batch(wl, lq, lk, cu_q, cu_k, q, k, v, do, qs, ks)
 
 

@@ -112,6 +112,8 @@ def _out_dtype(t):
         return DTYPE_FP32
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
+    if t.dtype == torch.float16:
+        return DTYPE_FP16
     raise TypeError(f"unsupported output dtype {t.dtype}")
 
 

@@ -15,12 +15,14 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdpa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_sched.hip", "gdpa_api.cpp"]
+SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip", "gdpa_sched.hip",
+           "gdpa_api.cpp"]
 # Per-source code generation options.  The forward kernels keep their MFMA
 # accumulators in architectural VGPRs (the activation reads the S tile with
 # no accumulator-to-VGPR copies; the register file still fits two workgroups
 # per CU).
-EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 

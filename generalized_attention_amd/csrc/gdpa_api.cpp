@@ -85,6 +85,16 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
   return GDPA_OK;
 }
 
+// Output dtype -> kernel output kind (-1: not an output type).
+int out_kind_of(int32_t dtype) {
+  switch (dtype) {
+    case GDPA_DTYPE_FP32: return gdpa::OUT_F32;
+    case GDPA_DTYPE_BF16: return gdpa::OUT_BF16;
+    case GDPA_DTYPE_FP16: return gdpa::OUT_F16;
+    default: return -1;
+  }
+}
+
 // Upper bound on the number of products summed into one output row: `len`
 // rows of the other operand times `heads` query heads, with `len` capped by the
 // window width when both window sides are bounded.
@@ -194,12 +204,17 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
                       const int32_t* cu_k, const Common& c, float scale, float act_param,
                       int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale,
                       float k_descale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (qk_dtype == GDPA_DTYPE_FP16 || v_dtype == GDPA_DTYPE_FP16 || out_dtype == GDPA_DTYPE_FP16)
-    return GDPA_ERR_UNSUPPORTED;
-  if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_INVALID_ARG;
-  if (v_dtype != GDPA_DTYPE_BF16) return v_dtype == GDPA_DTYPE_FP8_E4M3 ? GDPA_ERR_UNSUPPORTED : GDPA_ERR_INVALID_ARG;
-  if (out_dtype != GDPA_DTYPE_FP32 && out_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP16 && qk_dtype != GDPA_DTYPE_FP8_E4M3)
+    return GDPA_ERR_INVALID_ARG;
+  if (v_dtype != GDPA_DTYPE_BF16 && v_dtype != GDPA_DTYPE_FP16)
+    return v_dtype == GDPA_DTYPE_FP8_E4M3 ? GDPA_ERR_UNSUPPORTED : GDPA_ERR_INVALID_ARG;
+  const int out_kind = out_kind_of(out_dtype);
+  if (out_kind < 0) return GDPA_ERR_INVALID_ARG;
+  // bf16 Q/K with bf16 V, fp16 with fp16, or FP8 Q/K with bf16 V (P takes V's type).
   const bool fp8 = qk_dtype == GDPA_DTYPE_FP8_E4M3;
+  const bool f16 = v_dtype == GDPA_DTYPE_FP16;
+  if (f16 != (qk_dtype == GDPA_DTYPE_FP16)) return GDPA_ERR_UNSUPPORTED;
+  const int in_kind = fp8 ? gdpa::EL_FP8 : f16 ? gdpa::EL_F16 : gdpa::EL_BF16;
   if (fp8 && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
   if (c.batch == 0 || c.total_q == 0) return GDPA_OK;
   if (q == nullptr || o == nullptr) return GDPA_ERR_INVALID_ARG;
@@ -224,11 +239,12 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   a.act = make_act(c.act_kind, fp8 ? (double)scale * q_descale * k_descale : (double)scale, act_param);
   a.wl = c.wl;
   a.wr = c.wr;
-  a.out_f32 = out_dtype == GDPA_DTYPE_FP32;
+  a.out_kind = out_kind;
   // When an output row sums at most kFewTerms products, the bf16 rounding of P
   // no longer averages out; P is then carried as hi + lo (such short rows are
-  // bandwidth-bound, so the second MFMA is free).
-  a.psplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
+  // bandwidth-bound, so the second MFMA is free).  fp16's 3 extra mantissa
+  // bits keep a single word within tolerance.
+  a.psplit = !f16 && few_terms(c.max_lk, 1, c) ? 1 : 0;
   if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
   // The forward kernel addresses one sequence's K and V rows with 32-bit byte offsets.
   if ((int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
@@ -238,10 +254,10 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
       build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
-    std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d fp8=%d wl=%d wr=%d psplit=%d grid=%lld\n",
-                 c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, (int)fp8, c.wl, c.wr,
+    std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d in=%d wl=%d wr=%d psplit=%d grid=%lld\n",
+                 c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, in_kind, c.wl, c.wr,
                  a.psplit, (long long)gdpa::fwd_grid(a));
-  return hip_status(gdpa::launch_fwd(a, c.d, c.act_kind, fp8, static_cast<hipStream_t>(stream)),
+  return hip_status(gdpa::launch_fwd(a, c.d, c.act_kind, in_kind, static_cast<hipStream_t>(stream)),
                     "forward launch");
 }
 
@@ -249,10 +265,11 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
                       void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (in_dtype == GDPA_DTYPE_FP8_E4M3 || in_dtype == GDPA_DTYPE_FP16 || grad_dtype == GDPA_DTYPE_FP16)
-    return GDPA_ERR_UNSUPPORTED;
-  if (in_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
-  if (grad_dtype != GDPA_DTYPE_FP32 && grad_dtype != GDPA_DTYPE_BF16) return GDPA_ERR_INVALID_ARG;
+  if (in_dtype == GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_UNSUPPORTED;
+  if (in_dtype != GDPA_DTYPE_BF16 && in_dtype != GDPA_DTYPE_FP16) return GDPA_ERR_INVALID_ARG;
+  const int out_kind = out_kind_of(grad_dtype);
+  if (out_kind < 0) return GDPA_ERR_INVALID_ARG;
+  const bool f16 = in_dtype == GDPA_DTYPE_FP16;
   // dq == NULL skips dQ; dk == dv == NULL skips dK and dV; at least one is wanted.
   const bool want_dq = dq != nullptr;
   const bool want_dkv = dk != nullptr;
@@ -290,16 +307,17 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.act = make_act(c.act_kind, scale, act_param);
   a.wl = c.wl;
   a.wr = c.wr;
-  a.out_f32 = grad_dtype == GDPA_DTYPE_FP32;
-  a.dsplit = few_terms(c.max_lk, 1, c) ? 1 : 0;
-  a.kvsplit = few_terms(c.max_lq, a.group, c) ? 1 : 0;
+  a.out_kind = out_kind;
+  a.dsplit = !f16 && few_terms(c.max_lk, 1, c) ? 1 : 0;
+  a.kvsplit = !f16 && few_terms(c.max_lq, a.group, c) ? 1 : 0;
   gdpa_status_t sst =
       build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &a.counters, &a.ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,
                  c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr);
-  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, want_dq, want_dkv, static_cast<hipStream_t>(stream)),
+  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, f16 ? gdpa::EL_F16 : gdpa::EL_BF16, want_dq, want_dkv,
+                                     static_cast<hipStream_t>(stream)),
                     "backward launch");
 }
 

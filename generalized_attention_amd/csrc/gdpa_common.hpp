@@ -39,6 +39,8 @@ __device__ __forceinline__ f32x16 mfma_fp8(const u32x2& a, const u32x2& b, const
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -51,6 +53,48 @@ __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_b
 // bf16 remainder of a packed pair: lo = bf16(x - float(hi)).
 __device__ __forceinline__ uint32_t split_lo(float x0, float x1, uint32_t hi) {
   return pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+}
+
+// ------------------------------------------- 16-bit element types (bf16, fp16)
+// Q, K, V, dO are bf16 or fp16 (or, forward only, FP8 Q/K with bf16 V); the
+// probabilities P and the score gradients dS are rounded to the type of the
+// operand they multiply, so every MFMA contracts two operands of one type.
+template <int EL>
+__device__ __forceinline__ f32x16 mfma16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (EL == EL_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return mfma_bf16(a, b, c);
+}
+// Two fp32 -> two 16-bit values, round to nearest even (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32).
+template <int EL>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (EL == EL_F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+  else
+    return pack_bf16x2(lo, hi);
+}
+// Remainder of a packed pair in the same type: lo = round(x - float(hi)).
+template <int EL>
+__device__ __forceinline__ uint32_t split2(float x0, float x1, uint32_t hi) {
+  if constexpr (EL == EL_F16) {
+    const f16x2 h = __builtin_bit_cast(f16x2, hi);
+    return pack2<EL_F16>(x0 - (float)h[0], x1 - (float)h[1]);
+  } else {
+    return split_lo(x0, x1, hi);
+  }
+}
+// Four consecutive fp32 results -> output element idx.. of an fp32, bf16 or
+// fp16 tensor (OUT_* kind).
+__device__ __forceinline__ void store4(void* base, long idx, float x0, float x1, float x2, float x3, int kind) {
+  if (kind == OUT_F32)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{x0, x1, x2, x3};
+  else if (kind == OUT_BF16)
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack2<EL_BF16>(x0, x1), pack2<EL_BF16>(x2, x3)};
+  else
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack2<EL_F16>(x0, x1), pack2<EL_F16>(x2, x3)};
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -8,6 +8,12 @@ namespace gdpa {
 
 // Activation kinds after folding the enum aliases (FAST_GELU*, GELU_TANH -> GELU_TANH;
 // FAST_SILU -> SILU).  Values match gdpa_act_t.
+// Element types of the MFMA inputs: bf16 or fp16 Q, K, V (and dO), or FP8
+// E4M3 Q and K with bf16 V (forward only).
+enum ElemKind : int { EL_BF16 = 0, EL_F16 = 1, EL_FP8 = 2 };
+// Output element types.
+enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
 enum ActKind : int {
   ACT_IDENTITY = 0,
   ACT_GELU = 1,
@@ -52,8 +58,8 @@ struct FwdArgs {
   ActConsts act;      // activation constants (c = scale * q_descale * k_descale)
   int32_t wl;         // window left  (-1: unbounded)
   int32_t wr;         // window right (-1: unbounded)
-  int32_t out_f32;    // 1: fp32 output, 0: bf16
-  int32_t psplit;     // 1: P carried as a bf16 hi/lo pair (two MFMAs for P V)
+  int32_t out_kind;   // OUT_F32, OUT_BF16 or OUT_F16
+  int32_t psplit;     // 1: P carried as a 16-bit hi/lo pair (two MFMAs for P V)
   const int32_t* perm;  // sequences in processing order (longest first), or nullptr
 };
 
@@ -79,9 +85,9 @@ struct BwdArgs {
   ActConsts act;      // activation constants (c = scale)
   int32_t wl;
   int32_t wr;
-  int32_t out_f32;
-  int32_t dsplit;     // 1: dS carried as a bf16 hi/lo pair in dQ = dS K
-  int32_t kvsplit;    // 1: P and dS carried as bf16 hi/lo pairs in dV, dK
+  int32_t out_kind;   // OUT_F32, OUT_BF16 or OUT_F16 (dQ, dK, dV)
+  int32_t dsplit;     // 1: dS carried as a 16-bit hi/lo pair in dQ = dS K
+  int32_t kvsplit;    // 1: P and dS carried as 16-bit hi/lo pairs in dV, dK
   const int32_t* perm;  // sequences in processing order (longest first), or nullptr
   int32_t* counters;    // per-XCD dK/dV work-queue counters (zeroed by the schedule), or nullptr
   int32_t ncu;          // compute units of the device (sizes the work-queue launches)
@@ -183,8 +189,12 @@ __device__ __forceinline__ void run_queue(int32_t* counter, long total, F&& body
 constexpr int kBwdBN = 128;
 constexpr int kBwdBM = 128;
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, int act_kind, bool fp8, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int act_kind, int in_kind, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, int in_kind, bool want_dq, bool want_dkv,
                       hipStream_t stream);
+// fp16 instantiations (own translation units)
+hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int act_kind, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
+                          hipStream_t stream);
 
 }  // namespace gdpa

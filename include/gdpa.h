@@ -94,7 +94,7 @@ typedef enum {
 
 typedef enum {
   GDPA_DTYPE_BF16 = 0,
-  GDPA_DTYPE_FP16 = 1,      /* reserved: not implemented (GDPA_ERR_UNSUPPORTED) */
+  GDPA_DTYPE_FP16 = 1,      /* IEEE binary16 */
   GDPA_DTYPE_FP8_E4M3 = 2,  /* OCP E4M3 codes, forward q/k only */
   GDPA_DTYPE_FP32 = 3       /* outputs only */
 } gdpa_dtype_t;
@@ -104,9 +104,12 @@ typedef enum {
  *   q, k, v, o     : device tensors in the layouts above.
  *   head_dim       : 64 or 128.
  *   scale          : multiplies Q K^T inside the activation (FA softmax_scale).
- *   qk_dtype       : GDPA_DTYPE_BF16 or GDPA_DTYPE_FP8_E4M3 (q and k codes).
- *   v_dtype        : GDPA_DTYPE_BF16.
- *   out_dtype      : GDPA_DTYPE_FP32 or GDPA_DTYPE_BF16.
+ *   qk_dtype, v_dtype : BF16 and BF16, FP16 and FP16, or FP8_E4M3 (q and k
+ *                    codes) and BF16.  P is rounded to v's type for P V, so
+ *                    other pairings return GDPA_ERR_UNSUPPORTED.  With FP16,
+ *                    |act(scale q.k)| must stay below 65504 * scale (P is
+ *                    kept unscaled in fp16; ReLU^2 scores above ~256 overflow).
+ *   out_dtype      : GDPA_DTYPE_FP32, GDPA_DTYPE_BF16 or GDPA_DTYPE_FP16.
  *   q_descale, k_descale : per-tensor fp32 factors of FP8 codes (ignored for bf16).
  *   workspace      : device scratch of at least gdpa_*_workspace_size() bytes
  *                    (may be NULL when that size is 0); contents are clobbered.
@@ -135,10 +138,12 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- backward
- * Gradients of L = sum(O .* dO) for the forward above (bf16 inputs only; the
- * README lists FP8 as forward-only, so an FP8 in_dtype returns
- * GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout; all three
- * are written in grad_dtype (GDPA_DTYPE_FP32 or GDPA_DTYPE_BF16).  The dQ
+ * Gradients of L = sum(O .* dO) for the forward above.  in_dtype (q, k, v and
+ * dout) is GDPA_DTYPE_BF16 or GDPA_DTYPE_FP16; P and dS are rounded to it for
+ * the products (the README lists FP8 as forward-only, so an FP8 in_dtype
+ * returns GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout;
+ * all three are written in grad_dtype (GDPA_DTYPE_FP32, GDPA_DTYPE_BF16 or
+ * GDPA_DTYPE_FP16).  The dQ
  * reduction over key blocks runs in a fixed order (deterministic).
  * Partial gradients: dq == NULL skips dQ; dk == dv == NULL skips dK and dV
  * (e.g. frozen keys/values).  dk and dv must be both NULL or both non-NULL,

@@ -3,6 +3,9 @@
 Test infrastructure (see the package docstring).
 
 * bf16: the upper 16 bits of an IEEE-754 binary32 value.
+* fp16: IEEE-754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10
+  mantissa bits; exponent field 0 is subnormal (m/1024 * 2^-14); field 31 is
+  infinity (m = 0) or NaN.
 * FP8 E4M3: the OCP 8-bit floating point format ("OCP 8-bit Floating Point
   Specification (OFP8)", E4M3 encoding): 1 sign bit, 4 exponent bits with bias
   7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is
@@ -19,6 +22,18 @@ import numpy as np
 def decode_bf16(bits) -> np.ndarray:
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode_f16(bits) -> np.ndarray:
+    c = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(c & 0x8000, -1.0, 1.0)
+    e = (c >> 10) & 0x1F
+    m = (c & 0x3FF).astype(np.float64)
+    normal = (1.0 + m / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = (m / 1024.0) * 2.0 ** -14
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where(e == 0x1F, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
 
 
 def decode_e4m3(codes, scale: float = 1.0) -> np.ndarray:

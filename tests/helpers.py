@@ -17,21 +17,24 @@ def to_dev(arr, dtype_name):
     t = torch.from_numpy(np.ascontiguousarray(arr))
     if dtype_name == "bf16":
         t = t.view(torch.int16).view(torch.bfloat16)
+    elif dtype_name == "fp16":
+        t = t.view(torch.int16).view(torch.float16)
     elif dtype_name == "fp8":
         t = t.view(torch.float8_e4m3fn)
     return t.cuda()
 
 
 def oracle_inputs(bt: gi.Batch):
-    """fp64 values the kernels consume (decoded bf16 / E4M3 codes x scale)."""
+    """fp64 values the kernels consume (decoded bf16 / fp16 / E4M3 codes x scale)."""
+    dec = oracle.decode_f16 if bt.wl.fp16 else oracle.decode_bf16
     if bt.wl.fp8_qk:
         q = oracle.decode_e4m3(bt.q, bt.q_scale)
         k = oracle.decode_e4m3(bt.k, bt.k_scale)
     else:
-        q = oracle.decode_bf16(bt.q)
-        k = oracle.decode_bf16(bt.k)
-    v = oracle.decode_bf16(bt.v)
-    do = oracle.decode_bf16(bt.do) if bt.do is not None else None
+        q = dec(bt.q)
+        k = dec(bt.k)
+    v = dec(bt.v)
+    do = dec(bt.do) if bt.do is not None else None
     return q, k, v, do
 
 
@@ -42,11 +45,12 @@ def mask_kw(wl: gi.Workload):
 def device_batch(bt: gi.Batch):
     import torch
     wl = bt.wl
-    qk = "fp8" if wl.fp8_qk else "bf16"
-    d = dict(q=to_dev(bt.q, qk), k=to_dev(bt.k, qk), v=to_dev(bt.v, "bf16"),
+    e16 = "fp16" if wl.fp16 else "bf16"
+    qk = "fp8" if wl.fp8_qk else e16
+    d = dict(q=to_dev(bt.q, qk), k=to_dev(bt.k, qk), v=to_dev(bt.v, e16),
              cu_q=torch.from_numpy(bt.cu_seqlens_q).cuda(), cu_k=torch.from_numpy(bt.cu_seqlens_k).cuda())
     if bt.do is not None:
-        d["do"] = to_dev(bt.do, "bf16")
+        d["do"] = to_dev(bt.do, e16)
     return d
 
 

@@ -94,7 +94,12 @@ def varlen_bwd(lib, **over):
     (dict(act=-1), INVALID),
     (dict(mask=3), INVALID),
     (dict(mask=2, wl=-2), INVALID),
-    (dict(qk=1), UNSUPPORTED),               # fp16 reserved
+    (dict(qk=1), UNSUPPORTED),               # fp16 Q/K with bf16 V (P takes V's type)
+    (dict(vd=1), UNSUPPORTED),               # bf16 Q/K with fp16 V
+    (dict(qk=2, vd=1), UNSUPPORTED),         # FP8 Q/K with fp16 V
+    (dict(qk=1, vd=1, B=0), OK),             # fp16 throughout
+    (dict(od=1, B=0), OK),                   # fp16 output
+    (dict(od=4), INVALID),
     (dict(vd=2), UNSUPPORTED),               # fp8 V
     (dict(od=2), INVALID),                   # fp8 output
     (dict(q=None), INVALID),
@@ -122,7 +127,9 @@ def test_varlen_fwd_validation(lib, over, expect):
 
 @pytest.mark.parametrize("over,expect", [
     (dict(ind=2), UNSUPPORTED),              # FP8 is forward-only (README "Features")
-    (dict(ind=1), UNSUPPORTED),
+    (dict(ind=1, B=0), OK),                  # fp16 inputs
+    (dict(ind=3), INVALID),                  # fp32 inputs
+    (dict(gd=1, B=0), OK),                   # fp16 gradients
     (dict(gd=2), INVALID),
     (dict(dk=None), INVALID),                # dk and dv must be requested together
     (dict(dq=None, dk=None, dv=None), INVALID),

@@ -1,4 +1,5 @@
-"""Full-size parity: the four large reference workloads at their real sizes, in
+"""Full-size parity: the four large reference workloads at their real sizes (and
+the jagged one with fp16 inputs), in
 the launch configuration the benchmark uses (same C entry points, same
 shapes).  Every output element is checked to have been written (outputs are
 NaN-poisoned before the call); sampled rows are recomputed one by one by the
@@ -13,7 +14,7 @@ from helpers import (TOL_BWD, TOL_FWD_BF16, TOL_FWD_FP8, device_batch, err_ratio
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["jagged_self", "full_self", "short_kv_cross", "window_gqa_fp8"]
+FULL = ["jagged_self", "full_self", "short_kv_cross", "window_gqa_fp8", "jagged_self_fp16"]
 N_ROWS = 96
 
 
@@ -25,8 +26,12 @@ def g():
     return generalized_attention_amd
 
 
+def _decode16(bt, arr):
+    return oracle.decode_f16(arr) if bt.wl.fp16 else oracle.decode_bf16(arr)
+
+
 def _decode_qk(bt, arr, scale):
-    return oracle.decode_e4m3(arr, scale) if bt.wl.fp8_qk else oracle.decode_bf16(arr)
+    return oracle.decode_e4m3(arr, scale) if bt.wl.fp8_qk else _decode16(bt, arr)
 
 
 def _seq(bt, b):
@@ -35,8 +40,8 @@ def _seq(bt, b):
     sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
     q = _decode_qk(bt, bt.q[sq], bt.q_scale)
     k = _decode_qk(bt, bt.k[sk], bt.k_scale)
-    v = oracle.decode_bf16(bt.v[sk])
-    do = oracle.decode_bf16(bt.do[sq]) if bt.do is not None else None
+    v = _decode16(bt, bt.v[sk])
+    do = _decode16(bt, bt.do[sq]) if bt.do is not None else None
     return q, k, v, do
 
 

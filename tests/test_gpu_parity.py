@@ -127,6 +127,60 @@ def test_fp8_forward(g, D):
     check_forward(g, bt)
 
 
+# ---------------------------------------------------------------- fp16 inputs
+# Q, K, V, dO in IEEE binary16; P and dS rounded to fp16 for the products.
+# Same bars as bf16 (the oracle consumes the decoded fp16 values).
+FP16_LENS = [37, 0, 300, 1, 129]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ["identity", "gelu", "fast_gelu", "relu", "relu2", "leaky_relu", "silu",
+                                 "hardswish"])
+def test_fp16_forward(g, act, D):
+    bt = gi.make_batch(_wl(act=act, head_dim=D, fp16=True, backward=False), seqlens_q=FP16_LENS,
+                       seqlens_k=FP16_LENS)
+    check_forward(g, bt)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ["gelu", "fast_gelu", "relu2", "silu", "hardswish"])
+def test_fp16_backward(g, act, D):
+    bt = gi.make_batch(_wl(act=act, head_dim=D, fp16=True), seqlens_q=FP16_LENS, seqlens_k=FP16_LENS)
+    check_backward(g, bt)
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 4])
+def test_fp16_masks_gqa(g, case):
+    mask, wl_, wr_, lq, lk = MASK_CASES[case]
+    wl = _wl(act="silu", fp16=True, mask=mask, window_left=wl_, window_right=wr_, batch=len(lq), heads_q=8,
+             heads_kv=2)
+    bt = gi.make_batch(wl, seqlens_q=lq, seqlens_k=lk)
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
+def test_fp16_short_kv(g):
+    # few products per output row: fp16 keeps P and dS in one word (no hi/lo split)
+    wl = dataclasses.replace(gi.WORKLOADS["short_kv_cross"], batch=4, fp16=True)
+    bt = gi.make_batch(wl)
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
+def test_fp16_outputs(g):
+    import torch
+    bt = gi.make_batch(_wl(act="gelu", fp16=True), seqlens_q=[300, 65], seqlens_k=[300, 65])
+    o = run_forward(g, bt, out_dtype=torch.float16).float().cpu().double().numpy()
+    q, k, v, do = oracle_inputs(bt)
+    wl = bt.wl
+    ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act)
+    assert err_ratio(o, ref) <= TOL_FWD_BF16
+    grads = [t.float().cpu().double().numpy() for t in run_backward(g, bt, grad_dtype=torch.float16)]
+    refs = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act)
+    for a, b in zip(grads, refs):
+        assert err_ratio(a, b) <= TOL_BWD
+
+
 def test_empty_kv_gives_zero_output(g):
     import torch
     bt = gi.make_batch(_wl(act="identity"), seqlens_q=[5, 70], seqlens_k=[0, 0])

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import act, act_grad, decode_bf16, decode_e4m3, gdpa_forward, gdpa_backward
+from oracle import act, act_grad, decode_bf16, decode_e4m3, decode_f16, gdpa_forward, gdpa_backward
 from oracle.gdpa import allowed_mask, gdpa_forward_rows, gdpa_backward_q_rows, gdpa_backward_k_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -105,6 +105,17 @@ def test_bf16_decode_matches_torch():
     fin = np.isfinite(ref)
     assert np.array_equal(got[fin], ref[fin])
     assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_f16_decode_matches_numpy():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = decode_f16(bits)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # binary16 landmarks: 1, -2, largest finite, smallest subnormal, infinity
+    assert list(decode_f16([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x7C00])) == [1.0, -2.0, 65504.0, 2.0 ** -24, np.inf]
 
 
 def test_e4m3_decode_matches_torch():
