@@ -69,6 +69,8 @@ WORKLOADS = {
                                (64, 64), "relu2", backward=True, seed=4),
     "jagged_self_fp16": Workload("jagged_self_fp16", 64, 4, 4, 128, (1, 1024), None,
                                  "fast_gelu", fp16=True, backward=True, seed=2),
+    "jagged_self_d96": Workload("jagged_self_d96", 64, 4, 4, 96, (1, 1024), None,
+                                "fast_gelu", backward=True, seed=2),
     "window_gqa_fp8": Workload("window_gqa_fp8", 16, 16, 4, 64, (1024, 4096),
                                None, "leaky_relu", act_param=0.01,
                                mask="window", window_left=511, window_right=0,

@@ -63,7 +63,7 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
   if (total_q > INT32_MAX || total_k > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return GDPA_ERR_INVALID_ARG;
   if (d <= 0) return GDPA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return GDPA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128) return GDPA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !std::isfinite(act_param)) return GDPA_ERR_INVALID_ARG;
   const int kind = act_kind_of(act);
   if (kind < 0) return GDPA_ERR_INVALID_ARG;

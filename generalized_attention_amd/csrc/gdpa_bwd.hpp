@@ -62,7 +62,7 @@ struct DkdvKernel {
   static constexpr int BQ = 64;                      // query rows per step
   static constexpr int KS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int ROWB = 2 * D;
+  static constexpr int ROWB = 2 * lds_dim(D);        // LDS row bytes (96 padded to 128)
   static constexpr int TB = BQ * ROWB;               // bytes of one Q (or dO) tile
   static constexpr int LPS = 2 * TB / (256 * 16);    // LDS copies per wave per step
   static constexpr int NP = SPLIT ? 2 : 1;           // 16-bit words per P / dS element
@@ -70,7 +70,6 @@ struct DkdvKernel {
   static constexpr int NB = 2 * NDB;                 // dV/dK units per query block
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;                     // units of operand prefetch
-  static_assert(8 % NA == 0 || NA % 8 == 0, "pair placement");
 
   using LaneOffs = TileOffs<ROWB>;
   struct Words {  // packed P and dS of one 32-query block: [hi/lo][t] x 4 words
@@ -160,18 +159,9 @@ struct DkdvKernel {
         const int qb = u < 2 * NA ? 0 : 1;
         const int v = u < 2 * NA ? u - NA : u - 2 * NA;
         const int span = u < 2 * NA ? NA : NB;
-        if (span >= 8) {
-          if (v % (span / 8) == 0) {
-            const int j = v / (span / 8);
-            pair<MASK>(sacc[qb], dpacc[qb], j >> 2, j & 3, mlo[qb], mhi[qb], wd[qb], k);
-          }
-        } else {
 #pragma unroll
-          for (int jj = 0; jj < 8 / span; ++jj) {
-            const int j = v * (8 / span) + jj;
-            pair<MASK>(sacc[qb], dpacc[qb], j >> 2, j & 3, mlo[qb], mhi[qb], wd[qb], k);
-          }
-        }
+        for (int j = 0; j < 8; ++j)
+          if (pair_at(j, v, span)) pair<MASK>(sacc[qb], dpacc[qb], j >> 2, j & 3, mlo[qb], mhi[qb], wd[qb], k);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -257,8 +247,8 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     const int h = g * a.group + i % a.group;
     const int m0 = step_m0(i);
     const int o = m0 * q_ld_b + h * D * 2;
-    stage_tile_buf<BQ, ROWB, 4>(qrs, o, q_ld_b, lq - m0, ql, wave, lane);
-    stage_tile_buf<BQ, ROWB, 4>(drs, o, q_ld_b, lq - m0, dl, wave, lane);
+    stage_tile_buf<BQ, ROWB, 4, D / 8>(qrs, o, q_ld_b, lq - m0, ql, wave, lane);
+    stage_tile_buf<BQ, ROWB, 4, D / 8>(drs, o, q_ld_b, lq - m0, dl, wave, lane);
   };
   auto compute = [&](int i, const uint8_t* ql, const uint8_t* dl) {
     if (!wave_active) return;
@@ -341,11 +331,11 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
 // ----------------------------------------------------------------------- dQ
 template <int D, int ACT, int EL, bool SPLIT>
 struct DqKernel {
-  static constexpr int BN = 8192 / D;  // keys per KV tile
+  static constexpr int BN = 8192 / lds_dim(D);  // keys per KV tile
   static constexpr int NKB = BN / 32;
   static constexpr int KS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int ROWB = 2 * D;
+  static constexpr int ROWB = 2 * lds_dim(D);  // LDS row bytes (96 padded to 128)
 
   static constexpr int NP = SPLIT ? 2 : 1;   // 16-bit words per dS element
   static constexpr int NA = KS;               // S/dP units per key block (2 MFMAs each)
@@ -423,18 +413,9 @@ struct DqKernel {
         const int j = u < 2 * NA ? 0 : 1;
         const int v = u < 2 * NA ? u - NA : u - 2 * NA;
         const int span = u < 2 * NA ? NA : NB;
-        if (span >= 8) {
-          if (v % (span / 8) == 0) {
-            const int q = v / (span / 8);
-            pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
-          }
-        } else {
 #pragma unroll
-          for (int qq = 0; qq < 8 / span; ++qq) {
-            const int q = v * (8 / span) + qq;
-            pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
-          }
-        }
+        for (int q = 0; q < 8; ++q)
+          if (pair_at(q, v, span)) pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -509,8 +490,8 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT>())) void gdpa_bwd_dq_ker
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld_b);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile_buf<BN, ROWB, 4>(krs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, kl, wave, lane);
-    stage_tile_buf<BN, ROWB, 4>(vrs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, ROWB, 4, D / 8>(krs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, kl, wave, lane);
+    stage_tile_buf<BN, ROWB, 4, D / 8>(vrs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, vl, wave, lane);
   };
   auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
     if (!wave_active) return;
@@ -636,6 +617,7 @@ template <int EL>
 static hipError_t launch_bwd_el(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
                                 hipStream_t stream) {
   if (head_dim == 64) return launch_bwd_d<64, EL>(a, act_kind, want_dq, want_dkv, stream);
+  if (head_dim == 96) return launch_bwd_d<96, EL>(a, act_kind, want_dq, want_dkv, stream);
   if (head_dim == 128) return launch_bwd_d<128, EL>(a, act_kind, want_dq, want_dkv, stream);
   return hipErrorInvalidValue;
 }

@@ -100,6 +100,15 @@ __device__ __forceinline__ void store4(void* base, long idx, float x0, float x1,
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// The unit streams below spread the 8 activation pairs of a 32 x 32 block over
+// the `span` MFMA units that follow the block: pair j rides under unit
+// (j * span) / 8 (span is 6, 8 or 16 with head dims 96, 128, or a split).
+__host__ __device__ constexpr bool pair_at(int j, int v, int span) { return (j * span) / 8 == v; }
+
+// Head dim as laid out in LDS: 96-wide rows are padded to 128 so the chunk
+// swizzle stays a bijection on whole 256-byte rows.
+__host__ __device__ constexpr int lds_dim(int d) { return d == 96 ? 128 : d; }
+
 // ----------------------------------------------------------------- activations
 // With c the score scale and s the raw dot product, y(s) satisfies
 // act(c s) = pscale * y(s) and d(s) = act'(c s) (constants in ActConsts, set
@@ -268,10 +277,15 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-template <int NROW, int ROWB, int NWAVES>
+// GCH: 16-byte chunks per source row (ROWB / 16 unless the LDS row is padded,
+// as for head dim 96 in 128-wide rows); lanes of padding chunks re-read a
+// chunk of the same row (same cache lines, no extra traffic) and their LDS
+// slots are never read.
+template <int NROW, int ROWB, int NWAVES, int GCH = ROWB / 16>
 __device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int row0_off, int ld_bytes, int nvalid,
                                                uint8_t* lds, int wave, int lane) {
   constexpr int U = ROWB / 16;
+  static_assert(GCH <= U && 2 * GCH >= U, "padding chunks re-read chunks of the same row");
   constexpr int NI = NROW * U / (64 * NWAVES);
   static_assert(NROW * U % (64 * NWAVES) == 0, "tile must be a multiple of NWAVES KiB");
 #pragma unroll
@@ -279,7 +293,8 @@ __device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int 
     const int blk = i * NWAVES + wave;
     const int p = blk * 64 + lane;
     const int row = p / U, pc = p % U;
-    const int c = pc ^ chunk_swz<ROWB>(row);
+    int c = pc ^ chunk_swz<ROWB>(row);
+    if constexpr (GCH < U) c = c < GCH ? c : c - (U - GCH);
     const int voff = row0_off + min(row, nvalid - 1) * ld_bytes + c * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
                                              voff, 0, 0, 0);

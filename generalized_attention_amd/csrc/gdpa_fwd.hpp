@@ -38,12 +38,13 @@ struct FwdKernel {
   static constexpr bool FP8 = IN == EL_FP8;
   static constexpr int EL = IN == EL_F16 ? EL_F16 : EL_BF16;  // V, P (and 16-bit Q, K)
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = 8192 / D;     // keys per KV tile
+  static constexpr int DP = lds_dim(D);   // head dim of an LDS row
+  static constexpr int BN = 8192 / DP;    // keys per KV tile
   static constexpr int NKB = BN / 32;     // 32-key blocks per tile
   static constexpr int KS = D / 16;       // k-steps of Q K^T
   static constexpr int NDB = D / 32;      // 32-row blocks of O^T
-  static constexpr int KROWB = FP8 ? D : 2 * D;
-  static constexpr int VROWB = 2 * D;
+  static constexpr int KROWB = FP8 ? DP : 2 * DP;
+  static constexpr int VROWB = 2 * DP;
   static constexpr int NQR = FP8 ? 1 : KS;   // 16-bit Q registers
   static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers
   static constexpr int NP = PSPLIT ? 2 : 1;  // 16-bit words per P element (hi, lo)
@@ -51,7 +52,7 @@ struct FwdKernel {
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;             // units of operand prefetch
-  using KOffs = TileOffs<2 * D>;             // 16-bit K rows and V rows (both 2D bytes)
+  using KOffs = TileOffs<2 * DP>;            // 16-bit K rows and V rows (both 2 DP bytes)
 
   // One pair of accumulator elements (key rows 8t+2w, +1) -> packed P words.
   template <bool MASK>
@@ -124,18 +125,9 @@ struct FwdKernel {
         const int j = u < 2 * NA ? 0 : 1;
         const int v = u < 2 * NA ? u - NA : u - 2 * NA;
         const int span = u < 2 * NA ? NA : NB;
-        if (span >= 8) {
-          if (v % (span / 8) == 0) {
-            const int q = v / (span / 8);
-            pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
-          }
-        } else {
 #pragma unroll
-          for (int qq = 0; qq < 8 / span; ++qq) {
-            const int q = v * (8 / span) + qq;
-            pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
-          }
-        }
+        for (int q = 0; q < 8; ++q)
+          if (pair_at(q, v, span)) pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -223,8 +215,9 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld * 2);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile_buf<BN, K::KROWB, NW>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0, kl, wave, lane);
-    stage_tile_buf<BN, K::VROWB, NW>(vrs, n0 * (int)kv_ld * 2, (int)kv_ld * 2, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, K::KROWB, NW, D * (FP8 ? 1 : 2) / 16>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0,
+                                                             kl, wave, lane);
+    stage_tile_buf<BN, K::VROWB, NW, D / 8>(vrs, n0 * (int)kv_ld * 2, (int)kv_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave, two 32-key blocks at a time; the mask is
   // applied only where the window cuts a block or a block runs past the last key.
@@ -333,6 +326,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
 template <int IN>
 static hipError_t launch_fwd_in(const FwdArgs& a, int head_dim, int act_kind, hipStream_t stream) {
   if (head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
+  if (head_dim == 96) return launch_fwd_d<96, IN>(a, act_kind, stream);
   if (head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
   return hipErrorInvalidValue;
 }

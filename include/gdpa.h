@@ -102,7 +102,7 @@ typedef enum {
 /* ------------------------------------------------------------------ forward
  * O = M .* act(scale * q_descale * k_descale * Q K^T) V per (sequence, head).
  *   q, k, v, o     : device tensors in the layouts above.
- *   head_dim       : 64 or 128.
+ *   head_dim       : 64, 96 or 128.
  *   scale          : multiplies Q K^T inside the activation (FA softmax_scale).
  *   qk_dtype, v_dtype : BF16 and BF16, FP16 and FP16, or FP8_E4M3 (q and k
  *                    codes) and BF16.  P is rounded to v's type for P V, so

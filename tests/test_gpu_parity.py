@@ -64,7 +64,7 @@ def test_tiny_fixed_length_forward(g):
 
 
 # ------------------------------------------------------------ activation x head dim
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("act", ALL_ACTS)
 def test_forward_every_activation(g, act, D):
     # jagged lengths incl. 0, 1 and ragged tails across several 128-row / KV tiles; GQA 4:2
@@ -73,7 +73,7 @@ def test_forward_every_activation(g, act, D):
     check_forward(g, bt)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("act", ALL_ACTS)
 def test_backward_every_activation(g, act, D):
     bt = gi.make_batch(_wl(act=act, head_dim=D, act_param=0.05), seqlens_q=[37, 0, 300, 1, 129],
@@ -94,7 +94,7 @@ MASK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("case", range(len(MASK_CASES)))
 def test_masks_forward_backward(g, case, D):
     mask, wl_, wr_, lq, lk = MASK_CASES[case]
@@ -119,7 +119,7 @@ def test_cross_attention_short_kv(g):
     check_backward(g, bt)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 def test_fp8_forward(g, D):
     wl = _wl(head_dim=D, fp8_qk=True, act="leaky_relu", mask="window", window_left=127, window_right=0,
              heads_q=8, heads_kv=2, backward=False)
@@ -133,7 +133,7 @@ def test_fp8_forward(g, D):
 FP16_LENS = [37, 0, 300, 1, 129]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("act", ["identity", "gelu", "fast_gelu", "relu", "relu2", "leaky_relu", "silu",
                                  "hardswish"])
 def test_fp16_forward(g, act, D):
@@ -142,7 +142,7 @@ def test_fp16_forward(g, act, D):
     check_forward(g, bt)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("act", ["gelu", "fast_gelu", "relu2", "silu", "hardswish"])
 def test_fp16_backward(g, act, D):
     bt = gi.make_batch(_wl(act=act, head_dim=D, fp16=True), seqlens_q=FP16_LENS, seqlens_k=FP16_LENS)
