@@ -22,7 +22,9 @@ SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip
 # no accumulator-to-VGPR copies; the register file still fits two workgroups
 # per CU).
 EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gdpa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gdpa_bwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
