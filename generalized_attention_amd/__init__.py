@@ -5,7 +5,10 @@ kernels behind the C entry points.  PyTorch provides device memory and the
 current stream.  The functions keep the C names (gdpa_fwd, gdpa_varlen_fwd,
 gdpa_bwd, gdpa_varlen_bwd); outputs are caller-allocated tensors, as in C.
 Small helpers (`varlen_forward`, `varlen_backward`, ...) allocate the outputs
-with torch and call the same entry points.
+with torch and call the same entry points; `GDPAFunction` makes them
+differentiable, and `flash_attn_func`, `flash_attn_varlen_func` and
+`generalized_dot_product_attention` take the call forms of the GDPA README's
+usage examples ("CUTE-DSL" and "Triton").
 
 The library must have been built (`python generalized_attention_amd/build.py`);
 importing this module fails loudly otherwise.
@@ -221,3 +224,85 @@ def backward(q, k, v, dout, scale=None, activation="fast_gelu", grad_dtype=torch
     dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
     dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
     return gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act=activation, **kw)
+
+
+# ------------------------------------------------------------------- autograd
+def _mask_args(causal, window_size):
+    """(causal, window_size=(left, right)) of the flash-attention call form ->
+    (mask, window_left, window_right); -1 is an unbounded side."""
+    left, right = window_size
+    if left >= 0 or right >= 0:
+        return "window", int(left), 0 if causal else int(right)
+    return ("causal" if causal else "none"), -1, -1
+
+
+class GDPAFunction(torch.autograd.Function):
+    """Differentiable GDPA over the C entry points: forward calls gdpa_fwd /
+    gdpa_varlen_fwd, backward calls gdpa_bwd / gdpa_varlen_bwd (gradients in
+    the inputs' dtype, dO rounded to it).  cu_seqlens_q is None for the
+    fixed-length layout [B, L, H, D]."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, act, act_param,
+                mask, window_left, window_right, out_dtype):
+        kw = dict(act=act, act_param=act_param, mask=mask, window_left=window_left, window_right=window_right)
+        if cu_seqlens_q is None:
+            o = torch.empty(*q.shape[:3], v.shape[3], dtype=out_dtype, device=q.device)
+            gdpa_fwd(q, k, v, o, scale, **kw)
+        else:
+            o = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=out_dtype, device=q.device)
+            gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, **kw)
+        ctx.save_for_backward(q, k, v, cu_seqlens_q, cu_seqlens_k)
+        ctx.args = (max_seqlen_q, max_seqlen_k, scale, kw)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, scale, kw = ctx.args
+        do = do.to(q.dtype).contiguous()
+        want_q, want_k, want_v = ctx.needs_input_grad[:3]
+        dq = torch.empty_like(q) if want_q else None
+        dk = torch.empty_like(k) if (want_k or want_v) else None
+        dv = torch.empty_like(v) if (want_k or want_v) else None
+        if dq is not None or dk is not None:
+            if cu_q is None:
+                gdpa_bwd(q, k, v, do, dq, dk, dv, scale, **kw)
+            else:
+                gdpa_varlen_bwd(q, k, v, do, dq, dk, dv, cu_q, cu_k, max_q, max_k, scale, **kw)
+        return (dq, dk if want_k else None, dv if want_v else None) + (None,) * 11
+
+
+def flash_attn_func(q, k, v, softmax_scale=None, causal=False, activation="fast_gelu", window_size=(-1, -1),
+                    act_param=0.01, out_dtype=None):
+    """The README's fixed-length call form: q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D].
+    Returns (out, None): there is no log-sum-exp without a softmax."""
+    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    mask, wl, wr = _mask_args(causal, window_size)
+    o = GDPAFunction.apply(q.contiguous(), k.contiguous(), v.contiguous(), None, None, q.shape[1], k.shape[1],
+                           float(scale), activation, float(act_param), mask, wl, wr, out_dtype or q.dtype)
+    return o, None
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                           causal=False, activation="fast_gelu", window_size=(-1, -1), act_param=0.01,
+                           out_dtype=None):
+    """The README's jagged call form: q [total_q, Hq, D], k/v [total_k, Hkv, D],
+    cu_seqlens int32 [B+1].  Returns (out, None)."""
+    scale = q.shape[-1] ** -0.5 if softmax_scale is None else softmax_scale
+    mask, wl, wr = _mask_args(causal, window_size)
+    o = GDPAFunction.apply(q.contiguous(), k.contiguous(), v.contiguous(), cu_seqlens_q.to(torch.int32),
+                           cu_seqlens_k.to(torch.int32), int(max_seqlen_q), int(max_seqlen_k), float(scale),
+                           activation, float(act_param), mask, wl, wr, out_dtype or q.dtype)
+    return o, None
+
+
+def generalized_dot_product_attention(query, key, value, query_offset, key_offset, max_seq_len_q, max_seq_len_kv,
+                                      activation="fast_gelu", scale=None, causal=False, window_size=(-1, -1),
+                                      act_param=0.01, out_dtype=None):
+    """The README's Triton call form: jagged tensors with query_offset /
+    key_offset (the cu_seqlens prefix sums) and max_seq_len_q / max_seq_len_kv."""
+    o, _ = flash_attn_varlen_func(query, key, value, query_offset, key_offset, max_seq_len_q, max_seq_len_kv,
+                                  softmax_scale=scale, causal=causal, activation=activation,
+                                  window_size=window_size, act_param=act_param, out_dtype=out_dtype)
+    return o

@@ -191,3 +191,16 @@ def test_binding_modules_do_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in re.sub(r"(#|//).*", "", text), f
+
+
+@pytest.mark.parametrize("causal,window,expect", [
+    (False, (-1, -1), ("none", -1, -1)),
+    (True, (-1, -1), ("causal", -1, -1)),
+    (True, (511, -1), ("window", 511, 0)),     # causal window of 512 keys
+    (False, (3, 4), ("window", 3, 4)),
+    (False, (-1, 40), ("window", -1, 40)),
+])
+def test_flash_attn_mask_arguments(causal, window, expect):
+    # the README's call form (causal, window_size) -> the C ABI's mask arguments
+    import generalized_attention_amd as g
+    assert g._mask_args(causal, window) == expect

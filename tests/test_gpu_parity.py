@@ -288,3 +288,55 @@ def test_batch_sorted_in_lds(g):
     bt = gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens)
     check_forward(g, bt)
     check_backward(g, bt)
+
+
+# ------------------------------------------------------ autograd and call forms
+def _oracle_check(bt, o, grads, mask="none", wl_=-1, wr_=-1):
+    wl = bt.wl
+    q, k, v, do = oracle_inputs(bt)
+    kw = dict(act_param=wl.act_param, mask=mask, window_left=wl_, window_right=wr_)
+    ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **kw)
+    assert err_ratio(o.detach().float().cpu().double().numpy().reshape(ref.shape), ref) <= TOL_FWD_BF16
+    refs = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **kw)
+    for name, a, b in zip("qkv", grads, refs):
+        r = err_ratio(a.float().cpu().double().numpy().reshape(b.shape), b)
+        assert r <= TOL_BWD, f"d{name} err/rms {r:.4g}"
+
+
+def test_autograd_varlen(g):
+    import torch
+    bt = gi.make_batch(_wl(act="silu", heads_q=4, heads_kv=2), seqlens_q=[300, 0, 65], seqlens_k=[300, 0, 65])
+    dev = device_batch(bt)
+    q, k, v = [dev[n].clone().requires_grad_() for n in ("q", "k", "v")]
+    o, lse = g.flash_attn_varlen_func(q, k, v, dev["cu_q"], dev["cu_k"], bt.max_seqlen_q, bt.max_seqlen_k,
+                                      activation="silu", out_dtype=torch.float32)
+    assert lse is None and o.dtype == torch.float32
+    (o * dev["do"].float()).sum().backward()
+    assert q.grad.dtype == q.dtype and k.grad.shape == k.shape
+    _oracle_check(bt, o, (q.grad, k.grad, v.grad))
+
+
+def test_autograd_fixed_length_causal(g):
+    import torch
+    wl = _wl(act="gelu", varlen=False, batch=2, heads_q=4, heads_kv=4, mask="causal", lq_range=(200, 200))
+    bt = gi.make_batch(wl)
+    dev = device_batch(bt)
+    B, L, H, D = 2, 200, 4, 128
+    q, k, v = [dev[n].view(B, L, H, D).clone().requires_grad_() for n in ("q", "k", "v")]
+    # fp32 output: the bf16 rounding of O alone takes most of the 2e-2 budget
+    o, _ = g.flash_attn_func(q, k, v, causal=True, activation="gelu", out_dtype=torch.float32)
+    assert o.shape == q.shape
+    (o.float() * dev["do"].view(B, L, H, D).float()).sum().backward()
+    _oracle_check(bt, o, (q.grad, k.grad, v.grad), mask="causal")
+
+
+def test_triton_call_form_equals_c_call(g):
+    import torch
+    bt = gi.make_batch(_wl(act="fast_gelu"), seqlens_q=[129, 7], seqlens_k=[129, 7])
+    dev = device_batch(bt)
+    o1 = g.generalized_dot_product_attention(dev["q"], dev["k"], dev["v"], query_offset=dev["cu_q"],
+                                             key_offset=dev["cu_k"], max_seq_len_q=bt.max_seqlen_q,
+                                             max_seq_len_kv=bt.max_seqlen_k, activation="fast_gelu",
+                                             out_dtype=torch.float32)
+    o2 = run_forward(g, bt, dev)
+    assert torch.equal(o1, o2)
