@@ -108,3 +108,51 @@ def test_full_size_workload(g, name):
     errs = dict(dq=err_ratio(got_q, ref_q), dk=err_ratio(got_k, ref_k), dv=err_ratio(got_v, ref_v))
     print(f"[fullsize] {name}: backward err/rms {errs}", flush=True)
     assert max(errs.values()) <= TOL_BWD, errs
+
+
+@pytest.mark.timeout(600)
+def test_tensors_beyond_2gib(g):
+    """Four 300k-token sequences (H = 8, D = 128): q, k, v, dO are 2.46 GB each and
+    the last sequence starts beyond 2^31 bytes of o, dq, dk, dv (and its tail beyond
+    2^31 bytes of q, k, v).  Causal window of 512 keys keeps the GPU work small; a
+    2048-query block at the end of the last sequence is recomputed by the oracle
+    with its 511 preceding keys, which holds every key its queries see and every
+    query that sees its first 1537 keys."""
+    import torch
+    B, L, H, D, W = 4, 300_000, 8, 128, 512
+    act, scale = "silu", D ** -0.5
+    total = B * L
+    print("[fullsize] beyond 2 GiB: drawing inputs on the GPU", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    def draw():
+        return torch.randn((total, H, D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    q, k, v, do = draw(), draw(), draw(), draw()
+    cu = torch.arange(0, total + 1, L, dtype=torch.int32, device="cuda")
+    kw = dict(act=act, mask="window", window_left=W - 1, window_right=0)
+    o = torch.full((total, H, D), float("nan"), device="cuda")
+    print("[fullsize] beyond 2 GiB: forward", flush=True)
+    g.gdpa_varlen_fwd(q, k, v, o, cu, cu, L, L, scale, **kw)
+    dq, dk, dv = (torch.full((total, H, D), float("nan"), device="cuda") for _ in range(3))
+    print("[fullsize] beyond 2 GiB: backward", flush=True)
+    g.gdpa_varlen_bwd(q, k, v, do, dq, dk, dv, cu, cu, L, L, scale, **kw)
+    torch.cuda.synchronize()
+    assert q.numel() * 2 > 2 ** 31 and 3 * L * H * D * 4 > 2 ** 31
+    for t_ in (o, dq, dk, dv):
+        assert not torch.isnan(t_).any(), "unwritten (NaN-poisoned) outputs"
+    t1 = total - 5
+    t0 = t1 - 2048                       # queries [t0, t1) of the last sequence
+    k0 = t0 - (W - 1)                     # keys [k0, t1)
+    assert (total - L) * H * D * 4 > 2 ** 31 and t0 * H * D * 2 > 2 ** 31
+    dec = lambda t: t.float().cpu().double().numpy()
+    qs, ks, vs, dos = dec(q[t0:t1]), dec(k[k0:t1]), dec(v[k0:t1]), dec(do[t0:t1])
+    cq, ck = [0, t1 - t0], [0, t1 - k0]
+    okw = dict(mask="window", window_left=W - 1, window_right=0)
+    ref_o = oracle.gdpa_forward(qs, ks, vs, cq, ck, scale, act, **okw)
+    rq, rk, rv = oracle.gdpa_backward(qs, ks, vs, dos, cq, ck, scale, act, **okw)
+    nk = t1 - W + 1 - t0                  # keys [t0, t1 - 511) see all their queries in the block
+    errs = dict(o=err_ratio(dec(o[t0:t1]), ref_o), dq=err_ratio(dec(dq[t0:t1]), rq),
+                dk=err_ratio(dec(dk[t0:t0 + nk]), rk[W - 1:W - 1 + nk]),
+                dv=err_ratio(dec(dv[t0:t0 + nk]), rv[W - 1:W - 1 + nk]))
+    print(f"[fullsize] beyond 2 GiB: err/rms {errs}", flush=True)
+    assert errs["o"] <= TOL_FWD_BF16
+    assert max(errs["dq"], errs["dk"], errs["dv"]) <= TOL_BWD
