@@ -340,3 +340,20 @@ def test_triton_call_form_equals_c_call(g):
                                              out_dtype=torch.float32)
     o2 = run_forward(g, bt, dev)
     assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------ long sequences
+# (several KV tiles per query block, window edges inside tiles, one 1-row sequence)
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("mask,wl_,wr_", [("none", -1, -1), ("causal", -1, -1), ("window", 300, 0)])
+def test_long_sequence_forward(g, D, mask, wl_, wr_):
+    lens = [1100, 1500, 1030, 1]
+    wl = _wl(act="silu", head_dim=D, mask=mask, window_left=wl_, window_right=wr_, batch=len(lens),
+             backward=False)
+    check_forward(g, gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens))
+
+
+def test_long_sequence_forward_fp16_gqa(g):
+    lens = [2048, 1000]
+    wl = _wl(act="fast_gelu", fp16=True, heads_q=8, heads_kv=2, batch=2, backward=False)
+    check_forward(g, gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens))
