@@ -301,55 +301,17 @@ __device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int 
   }
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without a memory fence: completion of LDS-direct copies is
-// established explicitly with wait_vmcnt before it, and every LDS read before
-// it is consumed before it.  The empty asm statements keep the compiler from
-// moving memory accesses across the barrier.
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Transposed MFMA A operand from a row-major bf16 row tile via
+// Transposed MFMA A operands come from a row-major 16-bit row tile via
 // ds_read_b64_tr_b16.  Within each 16-lane group the instruction hands lane j
 // element e of the 8-byte row that lane 4e + j/4 addressed, column j % 4.  So
 // if lane r of group g addresses row (r0 + r/4), columns c0 + 4 (r%4) .. +3,
 // lane j receives rows r0..r0+3 of column c0 + j.  Lane l thus obtains the A
 // operand (row = column index c of the tile, l % 32 within a 32-block; k =
 // 8 tile rows) whose k order matches the accumulator row order of a C tile:
-// k position 4c' + e  <->  tile row 16 t + 8 c' + 4 (l / 32) + e.
-template <int ROWB>
-__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, int row_base, int col_base, int lane) {
-  const int g = lane >> 4, r = lane & 15;
-  bf16x4 part[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = row_base + 8 * c + 4 * (g >> 1) + (r >> 2);
-    const int col = col_base + 16 * (g & 1) + 4 * (r & 3);
-    // one integer offset, one pointer step: a short pointer chain lets the
-    // compiler trace the read to its LDS array (and not drain unrelated
-    // in-flight LDS copies before it)
-    const uint8_t* p = tile + (lds_off<ROWB>(row, col >> 3) + ((col & 4) << 1));
-    part[c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
-  }
-  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Row-major MFMA A operand (row = tile row l % 32 of the 32-row block at
-// row_base; k = 8 consecutive bf16 columns at chunk `chunk` + l / 32).
-template <int ROWB>
-__device__ __forceinline__ u32x4 row_operand(const uint8_t* tile, int row_base, int chunk, int lane) {
-  return *reinterpret_cast<const u32x4*>(tile + lds_off<ROWB>(row_base + (lane & 31), chunk + (lane >> 5)));
-}
+// k position 4c' + e  <->  tile row 16 t + 8 c' + 4 (l / 32) + e.  Two such
+// reads (c' = 0, 1: rows +0 and +8) make one 16-row operand (tr_at below).
+// Row-major A operands: lane l reads row l % 32 of a 32-row block, 8
+// consecutive columns at chunk 2 s + l / 32 (row_at below).
 
 // Per-lane byte offsets of the MFMA operands inside a row-major swizzled
 // [rows][ROWB bytes] LDS tile (the chunk swizzle has period 16 in the row, so
