@@ -130,7 +130,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: the GDPA kernels here run on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); "
               "GDPA work units are independent per (sequence, head), so more GPUs would each run this "
               "kernel on their own share with no collective.", file=sys.stderr)
         sys.exit(2)
