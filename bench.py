@@ -70,7 +70,8 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
     from threadpoolctl import threadpool_info
     wl = bt.wl
     pairs = workload_pairs(bt)
-    with_bwd = not wl.fp8_qk
+    DV = wl.head_dim_v or wl.head_dim
+    with_bwd = not wl.fp8_qk and DV == wl.head_dim
     dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
     if wl.fp8_qk:
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
@@ -89,7 +90,7 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
         if with_bwd:
             oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck, wl.scale, wl.act, **kw)
         t_total += time.perf_counter() - t0
-        flops += (14 if with_bwd else 4) * wl.head_dim * int(pairs[b])
+        flops += (14 * wl.head_dim if with_bwd else 2 * (wl.head_dim + DV)) * int(pairs[b])
         nseq += 1
         if t_total >= budget_s:
             break
@@ -147,9 +148,10 @@ def main():
     import generalized_attention_amd as g
 
     wl = gi.WORKLOADS[args.workload]
-    # FP8 Q/K is a forward-only path (the README's FP8 support is inference);
-    # every bf16 workload is timed forward + backward
-    with_bwd = not wl.fp8_qk
+    DV = wl.head_dim_v or wl.head_dim
+    # FP8 Q/K and distinct V head dims are forward-only paths (the README's FP8
+    # support is inference); every other workload is timed forward + backward
+    with_bwd = not wl.fp8_qk and DV == wl.head_dim
     if with_bwd and not wl.backward:
         wl = gi.dataclasses.replace(wl, backward=True)
     print(f"[bench] drawing {wl.name} (seed {wl.seed})", file=sys.stderr, flush=True)
@@ -157,7 +159,7 @@ def main():
     pairs = workload_pairs(bt)
     P = int(pairs.sum())
     D = wl.head_dim
-    fwd_flops, bwd_flops = 4 * D * P, (10 * D * P if with_bwd else 0)
+    fwd_flops, bwd_flops = 2 * (D + DV) * P, (10 * D * P if with_bwd else 0)
 
     def dev(a, kind):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -170,7 +172,7 @@ def main():
     q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, e16)
     do = dev(bt.do, e16) if with_bwd else None
     cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
-    o = torch.empty(q.shape[0], wl.heads_q, D, dtype=torch.float32, device="cuda")
+    o = torch.empty(q.shape[0], wl.heads_q, DV, dtype=torch.float32, device="cuda")
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
@@ -222,8 +224,9 @@ def main():
     isz = {"q": q.element_size(), "k": k.element_size(), "v": 2, "do": 2, "out": 4}
     tq, tk = q.shape[0], k.shape[0]
     nq, nkv = tq * wl.heads_q * D, tk * wl.heads_kv * D
-    kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 4 * D * P,
-                                nq * isz["q"] + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])}
+    nqv, nkvv = tq * wl.heads_q * DV, tk * wl.heads_kv * DV  # V- and O-shaped tensors
+    kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 2 * (D + DV) * P,
+                                nq * isz["q"] + nkv * isz["k"] + nkvv * isz["v"] + nqv * isz["out"])}
     if with_bwd:
         kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps), 8 * D * P,
                                         nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + 2 * nkv * isz["out"])

@@ -36,7 +36,7 @@ class Workload:
     batch: int
     heads_q: int
     heads_kv: int
-    head_dim: int
+    head_dim: int            # of Q and K
     lq_range: tuple          # (lo, hi) inclusive; lo == hi means fixed length
     lk_range: Optional[tuple]  # None: KV lengths equal Q lengths (self-attention)
     act: str
@@ -46,6 +46,7 @@ class Workload:
     window_right: int = -1
     fp8_qk: bool = False
     fp16: bool = False       # fp16 Q/K/V/dO instead of bf16
+    head_dim_v: Optional[int] = None  # of V and O (None: head_dim)
     backward: bool = False
     varlen: bool = True      # False: fixed-length [B, L, H, D] API
     seed: int = 0
@@ -71,6 +72,8 @@ WORKLOADS = {
                                  "fast_gelu", fp16=True, backward=True, seed=2),
     "jagged_self_d96": Workload("jagged_self_d96", 64, 4, 4, 96, (1, 1024), None,
                                 "fast_gelu", backward=True, seed=2),
+    "jagged_self_d192": Workload("jagged_self_d192", 64, 4, 4, 192, (1, 1024), None,
+                                 "fast_gelu", head_dim_v=128, seed=2),
     "window_gqa_fp8": Workload("window_gqa_fp8", 16, 16, 4, 64, (1024, 4096),
                                None, "leaky_relu", act_param=0.01,
                                mask="window", window_left=511, window_right=0,
@@ -166,11 +169,12 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool]
     cu_k[1:] = np.cumsum(lk)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
     H, G, D = wl.heads_q, wl.heads_kv, wl.head_dim
+    DV = wl.head_dim_v or D
     qf = rng.standard_normal((tq, H, D), dtype=np.float32)
     kf = rng.standard_normal((tk, G, D), dtype=np.float32)
-    vf = rng.standard_normal((tk, G, D), dtype=np.float32)
+    vf = rng.standard_normal((tk, G, DV), dtype=np.float32)
     want_do = wl.backward if with_do is None else with_do
-    dof = rng.standard_normal((tq, H, D), dtype=np.float32) if want_do else None
+    dof = rng.standard_normal((tq, H, DV), dtype=np.float32) if want_do else None
     qs = ks = 1.0
     enc = f32_to_f16_bits if wl.fp16 else f32_to_bf16_bits
     if wl.fp8_qk:

@@ -52,14 +52,15 @@ def _load():
         raise ImportError(f"{LIB_PATH} is not built; run python generalized_attention_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.gdpa_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
+    # head dims: head_dim (Q, K) then head_dim_v (V, O)
+    lib.gdpa_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
                              I32, I32, I32, F32, F32, P, SZ, P]
-    lib.gdpa_varlen_fwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32, I32,
+    lib.gdpa_varlen_fwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, F32, I32, I32,
                                     I32, I32, F32, I32, I32, I32, F32, F32, P, SZ, P]
-    lib.gdpa_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
+    lib.gdpa_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
                              I32, I32, P, SZ, P]
-    lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32,
-                                    I32, I32, I32, F32, I32, I32, P, SZ, P]
+    lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, F32,
+                                    I32, I32, I32, I32, F32, I32, I32, P, SZ, P]
     for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
         getattr(lib, n).restype = ctypes.c_int
     for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
@@ -140,7 +141,8 @@ def gdpa_fwd(q, k, v, o, scale, act="fast_gelu", act_param=0.01, mask="none", wi
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     ws, nws = _workspace(_lib.gdpa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
-    st = _lib.gdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Lq, Lk, Hq, Hkv, D, float(scale), _mask(mask),
+    st = _lib.gdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Lq, Lk, Hq, Hkv, D, v.shape[-1], float(scale),
+                       _mask(mask),
                        window_left, window_right, _act(act), float(act_param), _qk_dtype(q), _qk_dtype(v),
                        _out_dtype(o), float(q_descale), float(k_descale), _ptr(ws), nws, _stream(q.device))
     _check(st, "gdpa_fwd")
@@ -157,7 +159,7 @@ def gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_se
     ws, nws = _workspace(_lib.gdpa_varlen_fwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
     st = _lib.gdpa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
                               int(max_seqlen_q), int(max_seqlen_k), q.shape[0], k.shape[0], Hq, Hkv, D,
-                              float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
+                              v.shape[-1], float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
                               _qk_dtype(q), _qk_dtype(v), _out_dtype(o), float(q_descale), float(k_descale),
                               _ptr(ws), nws, _stream(q.device))
     _check(st, "gdpa_varlen_fwd")
@@ -171,7 +173,7 @@ def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, 
     Lk, Hkv = k.shape[1], k.shape[2]
     ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
     st = _lib.gdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, Lq, Lk, Hq, Hkv,
-                       D, float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
+                       D, v.shape[-1], float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
                        _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws), nws, _stream(q.device))
     _check(st, "gdpa_bwd")
     return dq, dk, dv
@@ -186,7 +188,8 @@ def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_s
     ws, nws = _workspace(_lib.gdpa_varlen_bwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
     st = _lib.gdpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k),
-                              q.shape[0], k.shape[0], Hq, Hkv, D, float(scale), _mask(mask), window_left,
+                              q.shape[0], k.shape[0], Hq, Hkv, D, v.shape[-1], float(scale), _mask(mask),
+                              window_left,
                               window_right, _act(act), float(act_param), _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws),
                               nws, _stream(q.device))
     _check(st, "gdpa_varlen_bwd")

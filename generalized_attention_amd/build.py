@@ -21,8 +21,11 @@ SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip
 # accumulators in architectural VGPRs (the activation reads the S tile with
 # no accumulator-to-VGPR copies; the register file still fits two workgroups
 # per CU).
-EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+# The forward unit streams (up to 40 units at head dims (192, 128)) must unroll
+# completely: a partly unrolled stream indexes its register arrays at run time
+# and the compiler moves them to scratch or LDS.
+EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"],
+         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"],
          "gdpa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "gdpa_bwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"

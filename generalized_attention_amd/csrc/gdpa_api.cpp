@@ -48,7 +48,7 @@ int act_kind_of(int32_t act) {
 }
 
 struct Common {
-  int32_t batch, max_lq, max_lk, hq, hkv, d;
+  int32_t batch, max_lq, max_lk, hq, hkv, d, dv;  // d: head dim of Q and K, dv: of V and O
   int64_t total_q, total_k;
   int act_kind;
   int32_t wl, wr;
@@ -56,14 +56,15 @@ struct Common {
 
 // Shape/enum checks shared by all four entry points.
 gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_t total_q,
-                           int64_t total_k, int32_t hq, int32_t hkv, int32_t d, float scale,
+                           int64_t total_k, int32_t hq, int32_t hkv, int32_t d, int32_t dv, float scale,
                            int32_t mask, int32_t window_left, int32_t window_right, int32_t act,
                            float act_param, Common* c) {
   if (batch < 0 || max_lq < 0 || max_lk < 0 || total_q < 0 || total_k < 0) return GDPA_ERR_INVALID_ARG;
   if (total_q > INT32_MAX || total_k > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return GDPA_ERR_INVALID_ARG;
-  if (d <= 0) return GDPA_ERR_INVALID_ARG;
-  if (d != 64 && d != 96 && d != 128) return GDPA_ERR_UNSUPPORTED;
+  if (d <= 0 || dv <= 0) return GDPA_ERR_INVALID_ARG;
+  // (Q/K, V) head dims: (64, 64), (96, 96), (128, 128), (192, 128)
+  if (!(d == dv && (d == 64 || d == 96 || d == 128)) && !(d == 192 && dv == 128)) return GDPA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !std::isfinite(act_param)) return GDPA_ERR_INVALID_ARG;
   const int kind = act_kind_of(act);
   if (kind < 0) return GDPA_ERR_INVALID_ARG;
@@ -79,9 +80,10 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
     default: return GDPA_ERR_INVALID_ARG;
   }
   // Row offsets inside the kernels are 32-bit; tensor offsets are 64-bit.
-  if ((int64_t)total_q * hq * d > (int64_t)1 << 40 || (int64_t)total_k * hkv * d > (int64_t)1 << 40)
+  const int64_t dmax = std::max(d, dv);
+  if ((int64_t)total_q * hq * dmax > (int64_t)1 << 40 || (int64_t)total_k * hkv * dmax > (int64_t)1 << 40)
     return GDPA_ERR_UNSUPPORTED;
-  *c = Common{batch, max_lq, max_lk, hq, hkv, d, total_q, total_k, kind, wl, wr};
+  *c = Common{batch, max_lq, max_lk, hq, hkv, d, dv, total_q, total_k, kind, wl, wr};
   return GDPA_OK;
 }
 
@@ -247,7 +249,7 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   a.psplit = !f16 && few_terms(c.max_lk, 1, c) ? 1 : 0;
   if (gdpa::fwd_grid(a) > kMaxGrid) return GDPA_ERR_UNSUPPORTED;
   // The forward kernel addresses one sequence's K and V rows with 32-bit byte offsets.
-  if ((int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
+  if ((int64_t)c.max_lk * c.hkv * std::max(c.d, c.dv) * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   int32_t* counters = nullptr;  // the forward keeps one workgroup per item
   int32_t ncu = 0;
   gdpa_status_t sst =
@@ -257,7 +259,7 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d in=%d wl=%d wr=%d psplit=%d grid=%lld\n",
                  c.batch, c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, in_kind, c.wl, c.wr,
                  a.psplit, (long long)gdpa::fwd_grid(a));
-  return hip_status(gdpa::launch_fwd(a, c.d, c.act_kind, in_kind, static_cast<hipStream_t>(stream)),
+  return hip_status(gdpa::launch_fwd(a, c.d, c.dv, c.act_kind, in_kind, static_cast<hipStream_t>(stream)),
                     "forward launch");
 }
 
@@ -266,6 +268,7 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
   if (in_dtype == GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_UNSUPPORTED;
+  if (c.dv != c.d) return GDPA_ERR_UNSUPPORTED;  // (192, 128): forward only
   if (in_dtype != GDPA_DTYPE_BF16 && in_dtype != GDPA_DTYPE_FP16) return GDPA_ERR_INVALID_ARG;
   const int out_kind = out_kind_of(grad_dtype);
   if (out_kind < 0) return GDPA_ERR_INVALID_ARG;
@@ -326,14 +329,14 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
 extern "C" {
 
 gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t seqlen_q,
-                       int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float scale,
+                       int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v, float scale,
                        int32_t mask, int32_t window_left, int32_t window_right, int32_t act, float act_param,
                        int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale, float k_descale,
                        void* workspace, size_t workspace_bytes, void* stream) {
   Common c;
   if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return GDPA_ERR_INVALID_ARG;
   gdpa_status_t st = check_common(batch, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, (int64_t)batch * seqlen_k,
-                                  num_heads_q, num_heads_kv, head_dim, scale, mask, window_left, window_right, act,
+                                  num_heads_q, num_heads_kv, head_dim, head_dim_v, scale, mask, window_left, window_right, act,
                                   act_param, &c);
   if (st != GDPA_OK) return st;
   return run_fwd(q, k, v, o, nullptr, nullptr, c, scale, act_param, qk_dtype, v_dtype, out_dtype, q_descale,
@@ -343,13 +346,14 @@ gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o, int
 gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int64_t total_q, int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv,
-                              int32_t head_dim, float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                              int32_t head_dim, int32_t head_dim_v, float scale, int32_t mask, int32_t window_left,
+                       int32_t window_right,
                               int32_t act, float act_param, int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
                               float q_descale, float k_descale, void* workspace, size_t workspace_bytes,
                               void* stream) {
   Common c;
   gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
-                                  head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+                                  head_dim, head_dim_v, scale, mask, window_left, window_right, act, act_param, &c);
   if (st != GDPA_OK) return st;
   if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
   return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, qk_dtype, v_dtype, out_dtype,
@@ -358,13 +362,14 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
 
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_kv,
-                       int32_t head_dim, float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                       int32_t head_dim, int32_t head_dim_v, float scale, int32_t mask, int32_t window_left,
+                       int32_t window_right,
                        int32_t act, float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
   Common c;
   if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return GDPA_ERR_INVALID_ARG;
   gdpa_status_t st = check_common(batch, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, (int64_t)batch * seqlen_k,
-                                  num_heads_q, num_heads_kv, head_dim, scale, mask, window_left, window_right, act,
+                                  num_heads_q, num_heads_kv, head_dim, head_dim_v, scale, mask, window_left, window_right, act,
                                   act_param, &c);
   if (st != GDPA_OK) return st;
   return run_bwd(q, k, v, dout, dq, dk, dv, nullptr, nullptr, c, scale, act_param, in_dtype, grad_dtype, workspace,
@@ -374,13 +379,13 @@ gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* 
 gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                               void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                               int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q, int64_t total_k,
-                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float scale, int32_t mask,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v, float scale, int32_t mask,
                               int32_t window_left, int32_t window_right, int32_t act, float act_param,
                               int32_t in_dtype, int32_t grad_dtype, void* workspace, size_t workspace_bytes,
                               void* stream) {
   Common c;
   gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
-                                  head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+                                  head_dim, head_dim_v, scale, mask, window_left, window_right, act, act_param, &c);
   if (st != GDPA_OK) return st;
   if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
   return run_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, in_dtype, grad_dtype,

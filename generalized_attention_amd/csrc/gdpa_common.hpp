@@ -105,9 +105,9 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // (j * span) / 8 (span is 6, 8 or 16 with head dims 96, 128, or a split).
 __host__ __device__ constexpr bool pair_at(int j, int v, int span) { return (j * span) / 8 == v; }
 
-// Head dim as laid out in LDS: 96-wide rows are padded to 128 so the chunk
-// swizzle stays a bijection on whole 256-byte rows.
-__host__ __device__ constexpr int lds_dim(int d) { return d == 96 ? 128 : d; }
+// Head dim as laid out in LDS: 96- and 192-wide rows are padded to 128 and
+// 256 so the chunk swizzle stays a bijection on whole 256-byte bank sweeps.
+__host__ __device__ constexpr int lds_dim(int d) { return d == 96 ? 128 : d == 192 ? 256 : d; }
 
 // ----------------------------------------------------------------- activations
 // With c the score scale and s the raw dot product, y(s) satisfies

@@ -4,11 +4,11 @@
 
 namespace gdpa {
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, int act_kind, int in_kind, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, int in_kind, hipStream_t stream) {
   switch (in_kind) {
-    case EL_BF16: return launch_fwd_in<EL_BF16>(a, head_dim, act_kind, stream);
-    case EL_FP8: return launch_fwd_in<EL_FP8>(a, head_dim, act_kind, stream);
-    case EL_F16: return launch_fwd_f16(a, head_dim, act_kind, stream);
+    case EL_BF16: return launch_fwd_in<EL_BF16>(a, head_dim, head_dim_v, act_kind, stream);
+    case EL_FP8: return launch_fwd_in<EL_FP8>(a, head_dim, head_dim_v, act_kind, stream);
+    case EL_F16: return launch_fwd_f16(a, head_dim, head_dim_v, act_kind, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -33,18 +33,20 @@
 
 namespace gdpa {
 
-template <int D, int ACT, int IN, bool PSPLIT, int NW>
+// D: head dim of Q and K; DV: head dim of V and O.
+template <int D, int ACT, int IN, bool PSPLIT, int NW, int DV = D>
 struct FwdKernel {
   static constexpr bool FP8 = IN == EL_FP8;
   static constexpr int EL = IN == EL_F16 ? EL_F16 : EL_BF16;  // V, P (and 16-bit Q, K)
   static constexpr int BM = 32 * NW;
-  static constexpr int DP = lds_dim(D);   // head dim of an LDS row
-  static constexpr int BN = 8192 / DP;    // keys per KV tile
+  static constexpr int DPK = lds_dim(D);  // head dims of the LDS rows of K and V
+  static constexpr int DPV = lds_dim(DV);
+  static constexpr int BN = 8192 / (DPK > DPV ? DPK : DPV) < 64 ? 64 : 8192 / (DPK > DPV ? DPK : DPV);  // keys per tile
   static constexpr int NKB = BN / 32;     // 32-key blocks per tile
   static constexpr int KS = D / 16;       // k-steps of Q K^T
-  static constexpr int NDB = D / 32;      // 32-row blocks of O^T
-  static constexpr int KROWB = FP8 ? DP : 2 * DP;
-  static constexpr int VROWB = 2 * DP;
+  static constexpr int NDB = DV / 32;     // 32-row blocks of O^T
+  static constexpr int KROWB = FP8 ? DPK : 2 * DPK;
+  static constexpr int VROWB = 2 * DPV;
   static constexpr int NQR = FP8 ? 1 : KS;   // 16-bit Q registers
   static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers
   static constexpr int NP = PSPLIT ? 2 : 1;  // 16-bit words per P element (hi, lo)
@@ -52,7 +54,8 @@ struct FwdKernel {
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;             // units of operand prefetch
-  using KOffs = TileOffs<2 * DP>;            // 16-bit K rows and V rows (both 2 DP bytes)
+  using KOffs = TileOffs<FP8 ? VROWB : KROWB>;  // row reads of 16-bit K (unused for FP8 K)
+  using VOffs = TileOffs<VROWB>;                 // transposed reads of V
 
   // One pair of accumulator elements (key rows 8t+2w, +1) -> packed P words.
   template <bool MASK>
@@ -75,7 +78,7 @@ struct FwdKernel {
   // u / NA, k-step u % NA (A operand: K rows); else P V of block
   // (u - 2 NA) / NB, key-row half t, head-dim block db (A operand: V^T).
   static __device__ __forceinline__ u32x4 load_unit(int u, int kb0, const uint8_t* kl, const uint8_t* vl,
-                                                    const KOffs& lo, int lane) {
+                                                    const KOffs& lo, const VOffs& vo, int lane) {
     if (u < 2 * NA) {
       const int kb = kb0 + u / NA, s = u % NA;
       if constexpr (FP8) {
@@ -87,7 +90,7 @@ struct FwdKernel {
       }
     }
     const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
-    return tr_at(vl, lo.tr[db], (kb * 32 + 16 * t) * VROWB);
+    return tr_at(vl, vo.tr[db], (kb * 32 + 16 * t) * VROWB);
   }
 
   // S^T = K Q^T of two 32-key blocks against this wave's 32 queries, P =
@@ -98,17 +101,17 @@ struct FwdKernel {
   // relative to block j's accumulator base.
   template <bool MASK>
   static __device__ __forceinline__ void block_pair(const uint8_t* kl, const uint8_t* vl, int kb0, const KOffs& lo,
-                                                    int lane, const u32x4* qreg, const u32x2* qreg8, f32x16* oacc,
+                                                    const VOffs& vo, int lane, const u32x4* qreg, const u32x2* qreg8, f32x16* oacc,
                                                     const int* mlo, const int* mhi, const ActConsts& k) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     u32x4 p[2][NP][2];
     u32x4 ring[PREF + 1];
 #pragma unroll
-    for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, lane);
+    for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, vo, lane);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       __builtin_amdgcn_sched_barrier(0);
-      if (u + PREF < NU) ring[(u + PREF) % (PREF + 1)] = load_unit(u + PREF, kb0, kl, vl, lo, lane);
+      if (u + PREF < NU) ring[(u + PREF) % (PREF + 1)] = load_unit(u + PREF, kb0, kl, vl, lo, vo, lane);
       const u32x4& op = ring[u % (PREF + 1)];
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
@@ -134,9 +137,9 @@ struct FwdKernel {
   }
 };
 
-template <int D, int ACT, int IN, bool PSPLIT, int NW>
+template <int D, int ACT, int IN, bool PSPLIT, int NW, int DV>
 __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
-  using K = FwdKernel<D, ACT, IN, PSPLIT, NW>;
+  using K = FwdKernel<D, ACT, IN, PSPLIT, NW, DV>;
   constexpr bool FP8 = K::FP8;
   constexpr int BM = K::BM, BN = K::BN, KS = K::KS, NDB = K::NDB, NKB = K::NKB;
   constexpr int KBYTES = BN * K::KROWB, VBYTES = BN * K::VROWB;
@@ -203,21 +206,22 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   const typename K::KOffs loffs = K::KOffs::make(lane);
+  const typename K::VOffs voffs = K::VOffs::make(lane);
 
   const int esz = FP8 ? 1 : 2;
-  const long kv_ld = (long)a.hkv * D;
+  const long kv_ld = (long)a.hkv * D, v_ld = (long)a.hkv * DV;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)ks * kv_ld + g * D) * esz;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)ks * kv_ld + g * D) * 2;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)ks * v_ld + g * DV) * 2;
 
   // Byte ranges of this sequence's K and V rows (all KV heads), addressed by
   // 32-bit offsets; the host keeps them below 2^31.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld * esz);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)v_ld * 2);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
     stage_tile_buf<BN, K::KROWB, NW, D * (FP8 ? 1 : 2) / 16>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0,
                                                              kl, wave, lane);
-    stage_tile_buf<BN, K::VROWB, NW, D / 8>(vrs, n0 * (int)kv_ld * 2, (int)kv_ld * 2, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, K::VROWB, NW, DV / 8>(vrs, n0 * (int)v_ld * 2, (int)v_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave, two 32-key blocks at a time; the mask is
   // applied only where the window cuts a block or a block runs past the last key.
@@ -248,9 +252,9 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
       }
       if (!any) continue;
       if (all_full)
-        K::template block_pair<false>(kl, vl, kb0, loffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
+        K::template block_pair<false>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
       else
-        K::template block_pair<true>(kl, vl, kb0, loffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
+        K::template block_pair<true>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
     }
   };
 
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
 
   // ---- epilogue: lane stores 4 consecutive head-dim values per register group
   if (!wave_active || qi >= lq) return;
-  const long orow = ((long)(qs + qi) * a.hq + h) * D;
+  const long orow = ((long)(qs + qi) * a.hq + h) * DV;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -291,20 +295,18 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   process(w.b, w.g, w.g * a.group + w.rest / a.mblocks, a.mblocks - 1 - w.rest % a.mblocks);
 }
 
-template <int D, int IN>
+template <int D, int IN, int DV = D>
 static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t stream) {
   // fp16 never splits P (the host keeps a single word within tolerance)
   if (IN == EL_F16 && a.psplit) return hipErrorInvalidValue;
   dim3 g((unsigned)fwd_grid(a)), blk(64 * kFwdNW);
   switch (act_kind) {
-#define GDPA_FWD_CASE(K)                                                                      \
-  case K:                                                                                     \
-    if constexpr (IN == EL_F16)                                                               \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, IN, false, kFwdNW>), g, blk, 0, stream, a);   \
-    else if (a.psplit)                                                                        \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, IN, true, kFwdNW>), g, blk, 0, stream, a);    \
-    else                                                                                      \
-      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, IN, false, kFwdNW>), g, blk, 0, stream, a);   \
+#define GDPA_FWD_CASE(K)                                                                          \
+  case K:                                                                                         \
+    if (IN == EL_F16 || !a.psplit)                                                                \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, IN, false, kFwdNW, DV>), g, blk, 0, stream, a);   \
+    else                                                                                          \
+      hipLaunchKernelGGL((gdpa_fwd_kernel<D, K, IN, true, kFwdNW, DV>), g, blk, 0, stream, a);    \
     break;
     GDPA_FWD_CASE(ACT_IDENTITY)
     GDPA_FWD_CASE(ACT_GELU)
@@ -322,12 +324,17 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
 }
 
 // Forward launches of one input element kind (each kind is instantiated in
-// its own translation unit).
+// its own translation unit).  Head dims (Q/K, V): (64, 64), (96, 96),
+// (128, 128), and (192, 128) for 16-bit inputs.
 template <int IN>
-static hipError_t launch_fwd_in(const FwdArgs& a, int head_dim, int act_kind, hipStream_t stream) {
-  if (head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
-  if (head_dim == 96) return launch_fwd_d<96, IN>(a, act_kind, stream);
-  if (head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
+static hipError_t launch_fwd_in(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream) {
+  if (head_dim == head_dim_v) {
+    if (head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
+    if (head_dim == 96) return launch_fwd_d<96, IN>(a, act_kind, stream);
+    if (head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
+  }
+  if constexpr (IN != EL_FP8)
+    if (head_dim == 192 && head_dim_v == 128) return launch_fwd_d<192, IN, 128>(a, act_kind, stream);
   return hipErrorInvalidValue;
 }
 

@@ -3,8 +3,8 @@
 
 namespace gdpa {
 
-hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int act_kind, hipStream_t stream) {
-  return launch_fwd_in<EL_F16>(a, head_dim, act_kind, stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream) {
+  return launch_fwd_in<EL_F16>(a, head_dim, head_dim_v, act_kind, stream);
 }
 
 }  // namespace gdpa

@@ -189,11 +189,11 @@ __device__ __forceinline__ void run_queue(int32_t* counter, long total, F&& body
 constexpr int kBwdBN = 128;
 constexpr int kBwdBM = 128;
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, int act_kind, int in_kind, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, int in_kind, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, int in_kind, bool want_dq, bool want_dkv,
                       hipStream_t stream);
 // fp16 instantiations (own translation units)
-hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int act_kind, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream);
 hipError_t launch_bwd_f16(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
                           hipStream_t stream);
 

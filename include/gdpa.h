@@ -25,8 +25,12 @@
  *    never allocates, frees or retains them; they must stay valid until the
  *    work queued on `stream` completes.
  *  - Layouts are row-major with the head dimension fastest:
- *      fixed length:  q/o/dO [B, Lq, Hq, D],  k/v [B, Lk, Hkv, D]
- *      jagged:        q/o/dO [total_q, Hq, D], k/v [total_k, Hkv, D]
+ *      fixed length:  q [B, Lq, Hq, D], o/dO [B, Lq, Hq, Dv],
+ *                     k [B, Lk, Hkv, D], v [B, Lk, Hkv, Dv]
+ *      jagged:        q [total_q, Hq, D], o/dO [total_q, Hq, Dv],
+ *                     k [total_k, Hkv, D], v [total_k, Hkv, Dv]
+ *    with D = head_dim (Q and K) and Dv = head_dim_v (V and O); dq/dk/dv
+ *    have the layouts of q/k/v.
  *    cu_seqlens_{q,k}: device int32 [B+1], cu[0] = 0, non-decreasing,
  *    cu[B] = total.  Zero-length sequences are allowed.
  *  - Element types: inputs bf16 (or FP8 E4M3 codes for q/k in the forward,
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDPA_ABI_VERSION 1
+#define GDPA_ABI_VERSION 2  /* 2: head_dim_v after head_dim in the four entry points */
 
 typedef enum {
   GDPA_OK = 0,
@@ -102,7 +106,9 @@ typedef enum {
 /* ------------------------------------------------------------------ forward
  * O = M .* act(scale * q_descale * k_descale * Q K^T) V per (sequence, head).
  *   q, k, v, o     : device tensors in the layouts above.
- *   head_dim       : 64, 96 or 128.
+ *   head_dim, head_dim_v : head dims of Q/K and of V/O: (64, 64), (96, 96),
+ *                    (128, 128), or (192, 128) (the README's "(192, 128)"; 16-bit
+ *                    inputs, forward only).  Other pairs: GDPA_ERR_UNSUPPORTED.
  *   scale          : multiplies Q K^T inside the activation (FA softmax_scale).
  *   qk_dtype, v_dtype : BF16 and BF16, FP16 and FP16, or FP8_E4M3 (q and k
  *                    codes) and BF16.  P is rounded to v's type for P V, so
@@ -116,7 +122,7 @@ typedef enum {
  */
 gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
-                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v,
                        float scale, int32_t mask, int32_t window_left, int32_t window_right,
                        int32_t act, float act_param,
                        int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
@@ -130,7 +136,7 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                               int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int64_t total_q, int64_t total_k,
-                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v,
                               float scale, int32_t mask, int32_t window_left, int32_t window_right,
                               int32_t act, float act_param,
                               int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
@@ -151,7 +157,7 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout,
                        void* dq, void* dk, void* dv,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
-                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v,
                        float scale, int32_t mask, int32_t window_left, int32_t window_right,
                        int32_t act, float act_param,
                        int32_t in_dtype, int32_t grad_dtype,
@@ -162,7 +168,7 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                               int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int64_t total_q, int64_t total_k,
-                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t head_dim_v,
                               float scale, int32_t mask, int32_t window_left, int32_t window_right,
                               int32_t act, float act_param,
                               int32_t in_dtype, int32_t grad_dtype,

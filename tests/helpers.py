@@ -61,8 +61,9 @@ def run_forward(g, bt: gi.Batch, dev=None, out_dtype=None, poison=True):
     dev = dev or device_batch(bt)
     out_dtype = out_dtype or torch.float32
     tq, H, D = bt.q.shape
-    o = torch.full((tq, H, D), float("nan"), dtype=out_dtype, device="cuda") if poison else \
-        torch.empty((tq, H, D), dtype=out_dtype, device="cuda")
+    DV = bt.v.shape[2]
+    o = torch.full((tq, H, DV), float("nan"), dtype=out_dtype, device="cuda") if poison else \
+        torch.empty((tq, H, DV), dtype=out_dtype, device="cuda")
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
               window_right=wl.window_right, q_descale=bt.q_scale, k_descale=bt.k_scale)
     if wl.varlen:
@@ -71,9 +72,9 @@ def run_forward(g, bt: gi.Batch, dev=None, out_dtype=None, poison=True):
     else:
         B = wl.batch
         Lq, Lk = int(bt.seqlens_q[0]), int(bt.seqlens_k[0])
-        o4 = o.view(B, Lq, H, D)
+        o4 = o.view(B, Lq, H, DV)
         g.gdpa_fwd(dev["q"].view(B, Lq, H, D), dev["k"].view(B, Lk, wl.heads_kv, D),
-                   dev["v"].view(B, Lk, wl.heads_kv, D), o4, wl.scale, **kw)
+                   dev["v"].view(B, Lk, wl.heads_kv, DV), o4, wl.scale, **kw)
     return o
 
 

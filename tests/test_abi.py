@@ -54,40 +54,51 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 
 
 def fwd(lib, **over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128, scale=0.1, mask=0,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128, Dv=None, scale=0.1, mask=0,
              wl=-1, wr=-1, act=3, ap=0.01, qk=0, vd=0, od=3, qd=1.0, kd=1.0, ws=None, nws=0, stream=None)
     a.update(over)
+    if a["Dv"] is None:
+        a["Dv"] = a["D"]
     return lib.gdpa_fwd(*a.values())
 
 
 def varlen_fwd(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, cq=FAKE, ck=FAKE, B=2, mq=128, mk=128, tq=200, tk=200, Hq=4, Hkv=4,
-             D=64, scale=0.1, mask=0, wl=-1, wr=-1, act=3, ap=0.01, qk=0, vd=0, od=3, qd=1.0, kd=1.0, ws=None,
+             D=64, Dv=None, scale=0.1, mask=0, wl=-1, wr=-1, act=3, ap=0.01, qk=0, vd=0, od=3, qd=1.0, kd=1.0, ws=None,
              nws=0, stream=None)
     a.update(over)
+    if a["Dv"] is None:
+        a["Dv"] = a["D"]
     return lib.gdpa_varlen_fwd(*a.values())
 
 
 def bwd(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128,
-             scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3, ws=None, nws=0, stream=None)
+             Dv=None, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3, ws=None, nws=0, stream=None)
     a.update(over)
+    if a["Dv"] is None:
+        a["Dv"] = a["D"]
     return lib.gdpa_bwd(*a.values())
 
 
 def varlen_bwd(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cq=FAKE, ck=FAKE, B=2, mq=128, mk=128,
-             tq=200, tk=200, Hq=4, Hkv=2, D=128, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3,
+             tq=200, tk=200, Hq=4, Hkv=2, D=128, Dv=None, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3,
              ws=None, nws=0, stream=None)
     a.update(over)
+    if a["Dv"] is None:
+        a["Dv"] = a["D"]
     return lib.gdpa_varlen_bwd(*a.values())
 
 
 @pytest.mark.parametrize("over,expect", [
     (dict(Hq=3, Hkv=2), INVALID),            # Hq % Hkv != 0
     (dict(Hkv=0), INVALID),
-    (dict(D=192), UNSUPPORTED),              # (192, 128) is listed by the README, not built here
+    (dict(D=192, Dv=192), UNSUPPORTED),      # built: (192, 128) only
+    (dict(D=128, Dv=64), UNSUPPORTED),
     (dict(D=80), UNSUPPORTED),
+    (dict(Dv=0), INVALID),
+    (dict(D=192, Dv=128, B=0), OK),          # the README's (192, 128)
     (dict(D=0), INVALID),
     (dict(B=-1), INVALID),
     (dict(Lq=-5), INVALID),
@@ -129,6 +140,7 @@ def test_varlen_fwd_validation(lib, over, expect):
 @pytest.mark.parametrize("over,expect", [
     (dict(ind=2), UNSUPPORTED),              # FP8 is forward-only (README "Features")
     (dict(ind=1, B=0), OK),                  # fp16 inputs
+    (dict(D=192, Dv=128), UNSUPPORTED),      # (192, 128) is forward only
     (dict(ind=3), INVALID),                  # fp32 inputs
     (dict(gd=1, B=0), OK),                   # fp16 gradients
     (dict(gd=2), INVALID),

@@ -1,5 +1,5 @@
 """Full-size parity: the four large reference workloads at their real sizes (and
-the jagged one with fp16 inputs and with head dim 96), in
+the jagged one with fp16 inputs, with head dim 96 and with head dims (192, 128)), in
 the launch configuration the benchmark uses (same C entry points, same
 shapes).  Every output element is checked to have been written (outputs are
 NaN-poisoned before the call); sampled rows are recomputed one by one by the
@@ -14,7 +14,8 @@ from helpers import (TOL_BWD, TOL_FWD_BF16, TOL_FWD_FP8, device_batch, err_ratio
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["jagged_self", "full_self", "short_kv_cross", "window_gqa_fp8", "jagged_self_fp16", "jagged_self_d96"]
+FULL = ["jagged_self", "full_self", "short_kv_cross", "window_gqa_fp8", "jagged_self_fp16", "jagged_self_d96",
+        "jagged_self_d192"]
 N_ROWS = 96
 
 

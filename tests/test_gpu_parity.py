@@ -357,3 +357,34 @@ def test_long_sequence_forward_fp16_gqa(g):
     lens = [2048, 1000]
     wl = _wl(act="fast_gelu", fp16=True, heads_q=8, heads_kv=2, batch=2, backward=False)
     check_forward(g, gi.make_batch(wl, seqlens_q=lens, seqlens_k=lens))
+
+
+# ------------------------------------------- head dims (192, 128): Q/K 192, V/O 128
+@pytest.mark.parametrize("act", ["identity", "fast_gelu", "silu", "relu2", "leaky_relu", "gelu"])
+def test_head_dims_192_128_forward(g, act):
+    bt = gi.make_batch(_wl(act=act, head_dim=192, head_dim_v=128, backward=False, act_param=0.05),
+                       seqlens_q=FP16_LENS, seqlens_k=FP16_LENS)
+    check_forward(g, bt)
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 4])
+def test_head_dims_192_128_masks_gqa(g, case):
+    mask, wl_, wr_, lq, lk = MASK_CASES[case]
+    wl = _wl(act="silu", head_dim=192, head_dim_v=128, mask=mask, window_left=wl_, window_right=wr_,
+             batch=len(lq), heads_q=8, heads_kv=2, backward=False)
+    check_forward(g, gi.make_batch(wl, seqlens_q=lq, seqlens_k=lk))
+
+
+def test_head_dims_192_128_fp16_and_fixed_length(g):
+    check_forward(g, gi.make_batch(_wl(act="fast_gelu", head_dim=192, head_dim_v=128, fp16=True,
+                                       backward=False), seqlens_q=[1100, 33], seqlens_k=[1100, 33]))
+    wl = _wl(act="silu", head_dim=192, head_dim_v=128, varlen=False, batch=2, lq_range=(300, 300),
+             backward=False)
+    check_forward(g, gi.make_batch(wl))
+
+
+def test_head_dims_192_128_backward_is_unsupported(g):
+    bt = gi.make_batch(_wl(act="silu", head_dim=192, head_dim_v=128), seqlens_q=[40], seqlens_k=[40])
+    with pytest.raises(g.GDPAError) as e:
+        run_backward(g, bt)
+    assert e.value.status == 2

@@ -206,6 +206,21 @@ def test_forward_matches_brute_force(case, name):
     assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("case", [0, 1, 3])
+@pytest.mark.parametrize("name", ["fast_gelu", "silu", "relu2"])
+def test_forward_matches_brute_force_distinct_v_dim(case, name):
+    # head dim of V (and O) differs from that of Q and K (the README's "(192, 128)")
+    lq, lk, hq, hkv, mask, wl, wr = BRUTE_CASES[case]
+    rng = np.random.default_rng(200 + case)
+    q = _rand(rng, sum(lq), hq, 3)
+    k = _rand(rng, sum(lk), hkv, 3)
+    v = _rand(rng, sum(lk), hkv, 5)
+    o = gdpa_forward(q, k, v, _cu(lq), _cu(lk), 0.7, name, 0.05, mask, wl, wr)
+    assert o.shape == (sum(lq), hq, 5)
+    ref = _brute_forward(q, k, v, lq, lk, 0.7, name, 0.05, mask, wl, wr)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- closed forms
 def test_identity_closed_form_associativity():
     # identity act, no mask: O = scale Q (K^T V) per (b, h)
