@@ -422,15 +422,16 @@ struct DqKernel {
   }
 };
 
-// Two workgroups per CU, except where exact GELU's gradient needs more
-// registers than two waves per SIMD leave at D = 128.
-template <int D, int ACT>
+// Two workgroups per CU, except where the activation gradient needs more
+// registers than two waves per SIMD leave at D = 128 (exact GELU, and SiLU
+// with dS carried as a hi/lo pair).
+template <int D, int ACT, bool SPLIT>
 constexpr int dq_occupancy() {
-  return (D == 128 && ACT == ACT_GELU) ? 1 : 2;
+  return (D == 128 && (ACT == ACT_GELU || (SPLIT && ACT == ACT_SILU))) ? 1 : 2;
 }
 
 template <int D, int ACT, int EL, bool SPLIT>
-__global__ __launch_bounds__(256, (dq_occupancy<D, ACT>())) void gdpa_bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd_dq_kernel(const BwdArgs a) {
   using K = DqKernel<D, ACT, EL, SPLIT>;
   constexpr int BM = kBwdBM;
   constexpr int BN = K::BN, NKB = K::NKB, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;

@@ -388,3 +388,13 @@ def test_head_dims_192_128_backward_is_unsupported(g):
     with pytest.raises(g.GDPAError) as e:
         run_backward(g, bt)
     assert e.value.status == 2
+
+
+# ---------------------------------------- short key/value: hi/lo-split dS and P
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ["silu", "fast_gelu", "gelu", "hardswish"])
+def test_short_kv_backward(g, act, D):
+    # at most 128 keys per sequence: dQ carries dS as a bf16 hi/lo pair
+    bt = gi.make_batch(_wl(act=act, head_dim=D), seqlens_q=[300, 50, 7], seqlens_k=[64, 100, 1])
+    check_forward(g, bt)
+    check_backward(g, bt)
