@@ -271,6 +271,17 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
       mlo[qb] = ilo_l - base;
       mhi2[qb] = ihi_l - base;
     }
+    // With one wave per SIMD, K and V (MFMA B operands) live in AGPRs; tying
+    // them to one register each step stops the allocator from copying them
+    // between AGPR groups inside the step (one move per register and step).
+    // At D = 64 they fit among the arch VGPRs, and are left there.
+    if constexpr (D > 64) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        asm volatile("" : "+a"(kreg[s]));
+        asm volatile("" : "+a"(vreg[s]));
+      }
+    }
     if (full)
       K::template step<false>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
     else
