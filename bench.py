@@ -11,7 +11,7 @@ Flops are algorithmic: only allowed (query, key) pairs count, 4*D per pair and
 query head for the forward (Q K^T and P V) and 10*D for the backward (the five
 products S, dP, dV, dK, dQ); activation math is not counted.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--cold]
   python bench.py --calibrate-copy 1024     # plain 1 GiB device copy, for PMC scaling
 """
 from __future__ import annotations
@@ -62,16 +62,25 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(bt: gi.Batch, budget_s: float):
+# parity bars (max |err| / rms(reference)): bf16/fp16 forward, gradients, FP8 forward
+TOL = {"o": 2e-2, "dq": 3e-2, "dk": 3e-2, "dv": 3e-2}
+TOL_FP8 = 6e-2
+
+
+def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None):
     """Time the fp64 oracle (forward + backward) on leading sequences of the same
     batch until about `budget_s` seconds of CPU work; report TFLOP/s on the
-    algorithmic flops of the sequences processed."""
+    algorithmic flops of the sequences processed.
+
+    With `gpu` (host copies of the outputs the timed kernels wrote: o, and dq,
+    dk, dv for a backward workload) it also returns max |gpu - oracle| /
+    rms(oracle) per output over the same sequences, outside the timed region."""
     import oracle
     from threadpoolctl import threadpool_info
     wl = bt.wl
     pairs = workload_pairs(bt)
     DV = wl.head_dim_v or wl.head_dim
-    with_bwd = not wl.fp8_qk and DV == wl.head_dim
+    with_bwd = not wl.fp8_qk and DV == wl.head_dim and bt.do is not None
     dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
     if wl.fp8_qk:
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
@@ -81,23 +90,43 @@ def cpu_baseline(bt: gi.Batch, budget_s: float):
     do = dec(bt.do) if with_bwd else None
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
     t_total, flops, nseq = 0.0, 0, 0
+    err = {}  # output -> [max |diff|, sum of ref^2, element count]
     for b in range(wl.batch):
         sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
         lcq, lck = [0, cq[b + 1] - cq[b]], [0, ck[b + 1] - ck[b]]
         kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
         t0 = time.perf_counter()
-        oracle.gdpa_forward(q[sq], k[sk], v[sk], lcq, lck, wl.scale, wl.act, **kw)
+        refs = {"o": oracle.gdpa_forward(q[sq], k[sk], v[sk], lcq, lck, wl.scale, wl.act, **kw)}
         if with_bwd:
-            oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck, wl.scale, wl.act, **kw)
+            refs["dq"], refs["dk"], refs["dv"] = oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck,
+                                                                     wl.scale, wl.act, **kw)
         t_total += time.perf_counter() - t0
+        if gpu is not None:
+            for name, ref in refs.items():
+                got = gpu[name][sq if name in ("o", "dq") else sk]
+                e = err.setdefault(name, [0.0, 0.0, 0])
+                if ref.size:
+                    e[0] = max(e[0], float(np.abs(got.astype(np.float64) - ref).max()))
+                    e[1] += float((ref * ref).sum())
+                    e[2] += ref.size
         flops += (14 * wl.head_dim if with_bwd else 2 * (wl.head_dim + DV)) * int(pairs[b])
         nseq += 1
         if t_total >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of the first {nseq} of {wl.batch} sequences "
+    sample = f"the first {nseq} of {wl.batch} sequences"
+    base = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of {sample} "
                       f"({flops / 1e9:.1f} GFLOP algorithmic) in {t_total:.1f} s"}
+    if gpu is None:
+        return base, None
+    tol = {n: (TOL_FP8 if wl.fp8_qk else t) for n, t in TOL.items()}
+    err_rms = {n: e[0] / np.sqrt(e[1] / e[2]) if e[2] and e[1] > 0 else 0.0 for n, e in err.items()}
+    parity = {"sample": sample + " against the fp64 oracle, all elements",
+              "err_rms": {n: float(f"{x:.3g}") for n, x in err_rms.items()},
+              "tol": {n: tol[n] for n in err_rms},
+              "pass": bool(all(err_rms[n] <= tol[n] for n in err_rms))}
+    return base, parity
 
 
 def calibrate_copy(mib: int, reps: int):
@@ -126,6 +155,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for per-kernel timing")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each kernel after evicting L2 / MALL (512 MiB write before every launch)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
 
@@ -207,15 +238,32 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel average launch durations (HIP events on the stream the kernels run on)
-    def avg_ms(fn, reps):
+    # per-kernel launch durations (HIP events on the stream the kernels run on):
+    # back to back (inputs may stay in L2 / MALL between launches), and with
+    # --cold also with a 512 MiB buffer written before every launch, so that
+    # the inputs come from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
+    stats = {}
+
+    def launch_ms(fn, reps, cold=False):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in evs:
+        for i, (a, b) in enumerate(evs):
+            if cold:
+                flush.fill_(i & 0xFF)
             a.record()
             fn()
             b.record()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    def avg_ms(fn, reps, name):
+        warm = launch_ms(fn, reps)
+        stats[name] = {"mean": round(float(warm.mean()), 4), "median": round(float(np.median(warm)), 4),
+                       "min": round(float(warm.min()), 4)}
+        if args.cold:
+            cold = launch_ms(fn, reps, cold=True)
+            stats[name].update(cold_median=round(float(np.median(cold)), 4), cold_min=round(float(cold.min()), 4))
+        return float(warm.mean())
 
     # algorithmic work per launch: flops of the products the gradient needs
     # (S, dP, dV, dK in the dK/dV kernel, dQ in the dQ kernel; the dQ kernel's
@@ -225,12 +273,14 @@ def main():
     tq, tk = q.shape[0], k.shape[0]
     nq, nkv = tq * wl.heads_q * D, tk * wl.heads_kv * D
     nqv, nkvv = tq * wl.heads_q * DV, tk * wl.heads_kv * DV  # V- and O-shaped tensors
-    kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps), 2 * (D + DV) * P,
+    kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps, "gdpa_fwd_kernel"), 2 * (D + DV) * P,
                                 nq * isz["q"] + nkv * isz["k"] + nkvv * isz["v"] + nqv * isz["out"])}
     if with_bwd:
-        kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps), 8 * D * P,
+        kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps, "gdpa_bwd_dkdv_kernel"),
+                                        8 * D * P,
                                         nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + 2 * nkv * isz["out"])
-        kern["gdpa_bwd_dq_kernel"] = (avg_ms(lambda: bwd(True, False), args.kernel_reps), 2 * D * P,
+        kern["gdpa_bwd_dq_kernel"] = (avg_ms(lambda: bwd(True, False), args.kernel_reps, "gdpa_bwd_dq_kernel"),
+                                      2 * D * P,
                                       nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])
     dom = max(kern, key=lambda n: kern[n][0])
     dom_ms, dom_flops, dom_bytes = kern[dom]
@@ -274,12 +324,18 @@ def main():
         "bwd_tflops": (round(bwd_flops / ((kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]) * 1e-3)
                              / 1e12, 2) if with_bwd else None),
         "kernel_ms": {n: round(t[0], 4) for n, t in kern.items()},
+        "kernel_ms_stats": stats,
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
+        # the outputs the timed launches wrote (every launch computes the same values)
+        torch.cuda.synchronize()
+        gpu = {"o": o.cpu().numpy()}
+        if with_bwd:
+            gpu.update(dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(bt, args.cpu_budget)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(bt, args.cpu_budget, gpu)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

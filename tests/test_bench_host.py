@@ -1,0 +1,49 @@
+"""Host-side logic of bench.py (CPU): the allowed-pair count behind the flop
+figures, and the parity record that the oracle leg attaches to a bench line."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import bench
+import gdpa_inputs as gi
+import oracle
+
+
+@pytest.mark.parametrize("lq,lk,wl,wr", [(7, 7, -1, -1), (7, 7, -1, 0), (5, 9, -1, 0), (9, 5, -1, 0),
+                                         (12, 12, 3, 0), (6, 10, 2, 1), (10, 6, 0, 0), (0, 4, -1, -1)])
+def test_allowed_pairs_matches_mask(lq, lk, wl, wr):
+    # the bench's closed-form count equals the oracle's mask summed element by element
+    mask = "none" if wl < 0 and wr < 0 else ("causal" if wl < 0 else "window")
+    want = int(oracle.allowed_mask(lq, lk, mask, wl, wr).sum()) if lq and lk else 0
+    assert bench.allowed_pairs(lq, lk, wl, wr) == want
+
+
+def _oracle_outputs(bt):
+    wl = bt.wl
+    q, k, v, do = (oracle.decode_bf16(x) for x in (bt.q, bt.k, bt.v, bt.do))
+    kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
+    cu = (bt.cu_seqlens_q, bt.cu_seqlens_k)
+    o = oracle.gdpa_forward(q, k, v, *cu, wl.scale, wl.act, **kw)
+    dq, dk, dv = oracle.gdpa_backward(q, k, v, do, *cu, wl.scale, wl.act, **kw)
+    return {n: x.astype(np.float32) for n, x in dict(o=o, dq=dq, dk=dk, dv=dv).items()}
+
+
+def test_parity_record_passes_on_oracle_outputs_and_flags_a_wrong_one():
+    wl = dataclasses.replace(gi.WORKLOADS["tiny"], backward=True)
+    bt = gi.make_batch(wl)
+    out = _oracle_outputs(bt)
+    base, parity = bench.cpu_baseline(bt, 1.0, out)
+    assert base["kind"] == "oracle" and base["value"] > 0
+    assert parity["pass"] and set(parity["err_rms"]) == {"o", "dq", "dk", "dv"}
+    assert max(parity["err_rms"].values()) < 1e-6  # fp32 storage of the fp64 result
+    out["dv"] = out["dv"].copy()
+    out["dv"][3, 1, 5] += 0.5 * np.sqrt(np.mean(out["dv"].astype(np.float64) ** 2)) / 0.01  # one element off
+    _, bad = bench.cpu_baseline(bt, 1.0, out)
+    assert not bad["pass"] and bad["err_rms"]["dv"] > bad["tol"]["dv"]
+
+
+def test_cpu_baseline_without_outputs_has_no_parity():
+    bt = gi.make_batch(gi.WORKLOADS["tiny"])
+    base, parity = bench.cpu_baseline(bt, 0.5)
+    assert parity is None and base["unit"] == "TFLOP/s"
