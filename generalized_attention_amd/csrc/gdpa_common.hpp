@@ -36,6 +36,19 @@ __device__ __forceinline__ f32x16 mfma_fp8(const u32x2& a, const u32x2& b, const
                                                     __builtin_bit_cast(long, b), c, 0, 0, 0);
 }
 
+// FP8 E4M3 x E4M3 over 64 k-values per MFMA (gfx950's K = 64 form, twice the
+// FP8 rate of the K = 16 form): each lane supplies 32 bytes of A (a0, a1) and of
+// B (b0, b1).  The sum runs over every byte position, so any assignment of
+// k-values to (lane half, byte) works if A and B use the same one.  No block
+// scaling: the scale operands are 0, which selects the unscaled instruction.
+__device__ __forceinline__ f32x16 mfma_fp8_k64(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                               const f32x16& c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -47,10 +47,14 @@ struct FwdKernel {
   static constexpr int NDB = DV / 32;     // 32-row blocks of O^T
   static constexpr int KROWB = FP8 ? DPK : 2 * DPK;
   static constexpr int VROWB = 2 * DPV;
-  static constexpr int NQR = FP8 ? 1 : KS;   // 16-bit Q registers
-  static constexpr int NQR8 = FP8 ? KS : 1;  // FP8 Q registers
+  // FP8 Q K^T on the K = 64 MFMA where the head dim is a multiple of 64:
+  // lane half h of a unit s holds bytes [64 s + 32 h, +32) of its K row and of
+  // its Q row (two 16-byte pieces each)
+  static constexpr bool F8W = FP8 && D % 64 == 0;
+  static constexpr int NQR = FP8 ? (F8W ? 2 * (D / 64) : 1) : KS;  // 16-byte Q registers
+  static constexpr int NQR8 = FP8 && !F8W ? KS : 1;               // 8-byte FP8 Q registers (K = 16 form)
   static constexpr int NP = PSPLIT ? 2 : 1;  // 16-bit words per P element (hi, lo)
-  static constexpr int NA = KS;              // S units per key block (1 MFMA each)
+  static constexpr int NA = F8W ? D / 64 : KS;  // S units per key block (1 MFMA each)
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;             // units of operand prefetch
@@ -78,10 +82,14 @@ struct FwdKernel {
   // u / NA, k-step u % NA (A operand: K rows); else P V of block
   // (u - 2 NA) / NB, key-row half t, head-dim block db (A operand: V^T).
   static __device__ __forceinline__ u32x4 load_unit(int u, int kb0, const uint8_t* kl, const uint8_t* vl,
-                                                    const KOffs& lo, const VOffs& vo, int lane) {
+                                                    const KOffs& lo, const VOffs& vo, int lane, u32x4& hi) {
     if (u < 2 * NA) {
       const int kb = kb0 + u / NA, s = u % NA;
-      if constexpr (FP8) {
+      if constexpr (F8W) {
+        const int row = kb * 32 + (lane & 31), c = 4 * s + 2 * (lane >> 5);
+        hi = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c + 1));
+        return *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c));
+      } else if constexpr (FP8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(kb * 32 + (lane & 31), s) +
                                                          (lane >> 5) * 8);
         return u32x4{v[0], v[1], 0u, 0u};
@@ -105,17 +113,21 @@ struct FwdKernel {
                                                     const int* mlo, const int* mhi, const ActConsts& k) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     u32x4 p[2][NP][2];
-    u32x4 ring[PREF + 1];
+    u32x4 ring[PREF + 1], ring_hi[PREF + 1];  // ring_hi: second 16 bytes of K = 64 FP8 units
 #pragma unroll
-    for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, vo, lane);
+    for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, vo, lane, ring_hi[u]);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       __builtin_amdgcn_sched_barrier(0);
-      if (u + PREF < NU) ring[(u + PREF) % (PREF + 1)] = load_unit(u + PREF, kb0, kl, vl, lo, vo, lane);
+      if (u + PREF < NU)
+        ring[(u + PREF) % (PREF + 1)] =
+            load_unit(u + PREF, kb0, kl, vl, lo, vo, lane, ring_hi[(u + PREF) % (PREF + 1)]);
       const u32x4& op = ring[u % (PREF + 1)];
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
-        if constexpr (FP8)
+        if constexpr (F8W)
+          sacc[j] = mfma_fp8_k64(op, ring_hi[u % (PREF + 1)], qreg[2 * s], qreg[2 * s + 1], sacc[j]);
+        else if constexpr (FP8)
           sacc[j] = mfma_fp8(u32x2{op[0], op[1]}, qreg8[s], sacc[j]);
         else
           sacc[j] = mfma16<EL>(op, qreg[s], sacc[j]);
@@ -185,13 +197,21 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
   const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step.
+  // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step
+  // (K = 64 FP8 form: 32 bytes per unit, [64 s + 32 hf, +32)).
   const long q_ld = (long)a.hq * D;
   u32x4 qreg[K::NQR];
   u32x2 qreg8[K::NQR8];
   {
     const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
-    if constexpr (FP8) {
+    if constexpr (K::F8W) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8 + hf * 32);
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s) {
+        qreg[2 * s] = load16_or_zero(qp + 64 * s, qi < lq);
+        qreg[2 * s + 1] = load16_or_zero(qp + 64 * s + 16, qi < lq);
+      }
+    } else if constexpr (FP8) {
       const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qreg8[s] = load8_or_zero(qp + s * 16, qi < lq);
