@@ -53,17 +53,35 @@ def _kw(wl):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(g, name):
+    _check_workload(g, gi.WORKLOADS[name], None, N_ROWS)
+
+
+# Robustness sweep: the same full-size check on other draws of the workloads
+# whose structure the seed changes (jagged lengths, short-KV query lengths,
+# windowed FP8 lengths), with fewer sampled rows each.
+SWEEP_SEEDS = [101, 102, 103, 104, 105, 201, 202, 203, 204, 205]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("seed", SWEEP_SEEDS)
+@pytest.mark.parametrize("name", ["jagged_self", "short_kv_cross", "window_gqa_fp8"])
+def test_full_size_seed_sweep(g, name, seed):
+    _check_workload(g, gi.WORKLOADS[name], seed, 32)
+
+
+def _check_workload(g, wl, seed, n_rows):
     import torch
-    wl = gi.WORKLOADS[name]
+    name = wl.name if seed is None else f"{wl.name} seed {seed}"
     print(f"[fullsize] {name}: drawing inputs", flush=True)
-    bt = gi.make_batch(wl)
+    bt = gi.make_batch(wl, seed=seed)
+    base_seed = wl.seed if seed is None else seed
     dev = device_batch(bt)
     print(f"[fullsize] {name}: forward", flush=True)
     o = run_forward(g, bt, dev)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any(), "forward left unwritten (NaN-poisoned) outputs"
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
-    rows = sample_rows(cq, wl.heads_q, N_ROWS, seed=1000 + wl.seed)
+    rows = sample_rows(cq, wl.heads_q, n_rows, seed=1000 + base_seed)
     idx_t = torch.tensor([t for t, _ in rows], device="cuda")
     idx_h = torch.tensor([h for _, h in rows], device="cuda")
     got = o[idx_t, idx_h].double().cpu().numpy()
@@ -93,7 +111,7 @@ def test_full_size_workload(g, name):
         q, k, v, do = _seq(bt, b)
         ref_q[r] = oracle.gdpa_backward_q_rows(q, k, v, do, [0, q.shape[0]], [0, k.shape[0]], wl.scale, wl.act,
                                                [(t - cq[b], h)], **_kw(wl))[0]
-    krows = sample_rows(ck, wl.heads_kv, N_ROWS, seed=2000 + wl.seed)
+    krows = sample_rows(ck, wl.heads_kv, n_rows, seed=2000 + base_seed)
     kt = torch.tensor([t for t, _ in krows], device="cuda")
     kg = torch.tensor([h for _, h in krows], device="cuda")
     got_k = dk[kt, kg].double().cpu().numpy()
