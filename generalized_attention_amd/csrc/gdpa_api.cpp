@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <algorithm>
+#include <vector>
 
 #include "gdpa_kernels.hpp"
 
@@ -163,6 +164,37 @@ size_t schedule_bytes(int64_t batch) {
   return (size_t)(((batch + gdpa::kNumCounters) * 4 + 255) / 256 * 256);
 }
 
+// GDPA_DEBUG_CHECKS=1 (read at every call): jagged calls copy cu_seqlens to the
+// host, synchronising the caller's stream, and reject device data that the
+// kernels would otherwise take on trust.
+bool debug_checks() {
+  const char* e = std::getenv("GDPA_DEBUG_CHECKS");
+  return e != nullptr && e[0] != '\0' && e[0] != '0';
+}
+
+// cu[0] = 0, non-decreasing, cu[batch] = total, every length <= max_len.
+gdpa_status_t check_cu_on_host(const int32_t* cu, int32_t batch, int32_t max_len, int64_t total, void* stream) {
+  std::vector<int32_t> h((size_t)batch + 1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "cu_seqlens check copy");
+  if (h[0] != 0 || (int64_t)h[batch] != total) return GDPA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)h[b + 1] - h[b];
+    if (len < 0 || len > max_len) return GDPA_ERR_INVALID_ARG;
+  }
+  return GDPA_OK;
+}
+
+gdpa_status_t debug_check_jagged(const int32_t* cu_q, const int32_t* cu_k, const Common& c, void* stream) {
+  if (cu_q == nullptr || !debug_checks()) return GDPA_OK;
+  gdpa_status_t st = check_cu_on_host(cu_q, c.batch, c.max_lq, c.total_q, stream);
+  if (st == GDPA_OK) st = check_cu_on_host(cu_k, c.batch, c.max_lk, c.total_k, stream);
+  if (st == GDPA_ERR_INVALID_ARG && debug_log()) std::fprintf(stderr, "[gdpa] invalid cu_seqlens\n");
+  return st;
+}
+
 // Compute units of the current device (0 if unknown), cached per device.
 int device_cu_count() {
   int dev = 0;
@@ -252,8 +284,9 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   if ((int64_t)c.max_lk * c.hkv * std::max(c.d, c.dv) * 2 > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   int32_t* counters = nullptr;  // the forward keeps one workgroup per item
   int32_t ncu = 0;
-  gdpa_status_t sst =
-      build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
+  gdpa_status_t sst = debug_check_jagged(cu_q, cu_k, c, stream);
+  if (sst != GDPA_OK) return sst;
+  sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d in=%d wl=%d wr=%d psplit=%d grid=%lld\n",
@@ -313,8 +346,9 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.out_kind = out_kind;
   a.dsplit = !f16 && few_terms(c.max_lk, 1, c) ? 1 : 0;
   a.kvsplit = !f16 && few_terms(c.max_lq, a.group, c) ? 1 : 0;
-  gdpa_status_t sst =
-      build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &a.counters, &a.ncu);
+  gdpa_status_t sst = debug_check_jagged(cu_q, cu_k, c, stream);
+  if (sst != GDPA_OK) return sst;
+  sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &a.counters, &a.ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,

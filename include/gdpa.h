@@ -43,7 +43,11 @@
  *  - Errors are returned as gdpa_status_t, never thrown.  Argument checks run
  *    on the host before any HIP call.  Invalid device data (e.g. a
  *    non-monotone cu_seqlens or a length above max_seqlen) is undefined
- *    behaviour.
+ *    behaviour, unless the environment variable GDPA_DEBUG_CHECKS is set to a
+ *    value other than 0 at the call: jagged calls then copy cu_seqlens_q/k to
+ *    the host (synchronising `stream`) and return GDPA_ERR_INVALID_ARG, with
+ *    nothing queued, if cu[0] != 0, cu[B] != total, an entry decreases or a
+ *    length exceeds max_seqlen.
  *  - Results are bitwise deterministic for a given input and launch.
  */
 #ifndef GDPA_H_
