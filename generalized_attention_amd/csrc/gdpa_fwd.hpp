@@ -47,14 +47,16 @@ struct FwdKernel {
   static constexpr int NDB = DV / 32;     // 32-row blocks of O^T
   static constexpr int KROWB = FP8 ? DPK : 2 * DPK;
   static constexpr int VROWB = 2 * DPV;
-  // FP8 Q K^T on the K = 64 MFMA where the head dim is a multiple of 64:
-  // lane half h of a unit s holds bytes [64 s + 32 h, +32) of its K row and of
-  // its Q row (two 16-byte pieces each)
-  static constexpr bool F8W = FP8 && D % 64 == 0;
-  static constexpr int NQR = FP8 ? (F8W ? 2 * (D / 64) : 1) : KS;  // 16-byte Q registers
-  static constexpr int NQR8 = FP8 && !F8W ? KS : 1;               // 8-byte FP8 Q registers (K = 16 form)
+  // FP8 Q K^T: the first 64 * NK64 head-dim bytes on the K = 64 MFMA (lane
+  // half h of unit s < NK64 holds bytes [64 s + 32 h, +32) of its K row and of
+  // its Q row, two 16-byte pieces each), the remaining 16 * NK16 bytes on the
+  // K = 16 MFMA (8 bytes per lane half, as for 16-bit inputs)
+  static constexpr int NK64 = FP8 ? D / 64 : 0;
+  static constexpr int NK16 = FP8 ? (D % 64) / 16 : 0;
+  static constexpr int NQR = FP8 ? (NK64 > 0 ? 2 * NK64 : 1) : KS;  // 16-byte Q registers
+  static constexpr int NQR8 = NK16 > 0 ? NK16 : 1;                  // 8-byte FP8 Q registers
   static constexpr int NP = PSPLIT ? 2 : 1;  // 16-bit words per P element (hi, lo)
-  static constexpr int NA = F8W ? D / 64 : KS;  // S units per key block (1 MFMA each)
+  static constexpr int NA = FP8 ? NK64 + NK16 : KS;  // S units per key block (1 MFMA each)
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;             // units of operand prefetch
@@ -85,12 +87,14 @@ struct FwdKernel {
                                                     const KOffs& lo, const VOffs& vo, int lane, u32x4& hi) {
     if (u < 2 * NA) {
       const int kb = kb0 + u / NA, s = u % NA;
-      if constexpr (F8W) {
-        const int row = kb * 32 + (lane & 31), c = 4 * s + 2 * (lane >> 5);
-        hi = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c + 1));
-        return *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c));
-      } else if constexpr (FP8) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(kb * 32 + (lane & 31), s) +
+      if constexpr (FP8) {
+        const int row = kb * 32 + (lane & 31);
+        if (s < NK64) {
+          const int c = 4 * s + 2 * (lane >> 5);
+          hi = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c + 1));
+          return *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c));
+        }
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(row, 4 * NK64 + s - NK64) +
                                                          (lane >> 5) * 8);
         return u32x4{v[0], v[1], 0u, 0u};
       } else {
@@ -125,10 +129,12 @@ struct FwdKernel {
       const u32x4& op = ring[u % (PREF + 1)];
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
-        if constexpr (F8W)
-          sacc[j] = mfma_fp8_k64(op, ring_hi[u % (PREF + 1)], qreg[2 * s], qreg[2 * s + 1], sacc[j]);
-        else if constexpr (FP8)
-          sacc[j] = mfma_fp8(u32x2{op[0], op[1]}, qreg8[s], sacc[j]);
+        if constexpr (FP8) {
+          if (s < NK64)
+            sacc[j] = mfma_fp8_k64(op, ring_hi[u % (PREF + 1)], qreg[2 * s], qreg[2 * s + 1], sacc[j]);
+          else
+            sacc[j] = mfma_fp8(u32x2{op[0], op[1]}, qreg8[s - NK64], sacc[j]);
+        }
         else
           sacc[j] = mfma16<EL>(op, qreg[s], sacc[j]);
       } else {
@@ -198,23 +204,21 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query qi, 8 head-dim values per k-step
-  // (K = 64 FP8 form: 32 bytes per unit, [64 s + 32 hf, +32)).
+  // (FP8: 32 bytes [64 s + 32 hf, +32) per K = 64 unit, then 8 bytes per K = 16 unit).
   const long q_ld = (long)a.hq * D;
   u32x4 qreg[K::NQR];
   u32x2 qreg8[K::NQR8];
   {
     const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
-    if constexpr (K::F8W) {
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8 + hf * 32);
+    if constexpr (FP8) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8);
 #pragma unroll
-      for (int s = 0; s < D / 64; ++s) {
-        qreg[2 * s] = load16_or_zero(qp + 64 * s, qi < lq);
-        qreg[2 * s + 1] = load16_or_zero(qp + 64 * s + 16, qi < lq);
+      for (int s = 0; s < K::NK64; ++s) {
+        qreg[2 * s] = load16_or_zero(qp + 64 * s + 32 * hf, qi < lq);
+        qreg[2 * s + 1] = load16_or_zero(qp + 64 * s + 32 * hf + 16, qi < lq);
       }
-    } else if constexpr (FP8) {
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qreg8[s] = load8_or_zero(qp + s * 16, qi < lq);
+      for (int t = 0; t < K::NK16; ++t) qreg8[t] = load8_or_zero(qp + 64 * K::NK64 + 16 * t + 8 * hf, qi < lq);
     } else {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow;
 #pragma unroll

@@ -129,10 +129,11 @@ def test_fp8_forward(g, D):
 
 @pytest.mark.parametrize("mask", ["none", "causal"])
 @pytest.mark.parametrize("act", ["silu", "gelu_tanh", "relu2", "identity"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 def test_fp8_forward_activations_masks(g, D, act, mask):
-    # Q K^T on the K = 64 FP8 MFMA (head dims 64, 128): every activation path and the
-    # unmasked / causal tile kinds, with ragged lengths (tail tiles) and MQA
+    # Q K^T on the K = 64 FP8 MFMA (at 96 followed by two K = 16 MFMAs): every
+    # activation path and the unmasked / causal tile kinds, with ragged lengths
+    # (tail tiles) and MQA
     wl = _wl(head_dim=D, fp8_qk=True, act=act, mask=mask, heads_q=4, heads_kv=1, backward=False)
     bt = gi.make_batch(wl, seqlens_q=[129, 1, 64, 250], seqlens_k=[129, 7, 64, 250])
     check_forward(g, bt)
