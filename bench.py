@@ -129,6 +129,49 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None):
     return base, parity
 
 
+def measured_peaks(torch):
+    """Sustained dense MFMA rates (bf16 32x32x16, FP8 32x32x64) over the whole
+    chip from the probe kernels in generalized_attention_amd/probe, and the
+    device-copy bandwidth (bytes read + written) of a 1 GiB torch copy; best
+    of 5 runs each."""
+    import ctypes
+    path = os.path.join(ROOT, "generalized_attention_amd", "libgdpa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.gdpa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gdpa_probe_mfma.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus  # two 4-wave workgroups per CU: two waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for kind, name, iters in ((0, "bf16_tflops", 20000), (1, "fp8_tflops", 10000)):
+        best = 0.0
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            flops = lib.gdpa_probe_mfma(kind, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if flops <= 0:
+                raise RuntimeError("probe launch failed")
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[name] = round(best, 1)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    res["copy_gbs"] = round(best, 1)
+    del src, dst
+    return res
+
+
 def calibrate_copy(mib: int, reps: int):
     import torch
     n = mib * (1 << 20)
@@ -328,6 +371,11 @@ def main():
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
     }
+    # sustained peaks on this GPU, measured after the timed work (context for the
+    # published peaks the roofline uses)
+    peaks = measured_peaks(torch)
+    result["measured_peak"] = peaks
+    result["pct_of_measured_bf16_peak"] = round(100 * value / peaks["bf16_tflops"], 2)
     if not args.no_cpu_baseline:
         # the outputs the timed launches wrote (every launch computes the same values)
         torch.cuda.synchronize()

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdpa.so")
+PROBE_LIB = os.path.join(HERE, "libgdpa_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip", "gdpa_sched.hip",
            "gdpa_api.cpp"]
@@ -67,8 +68,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # throughput probes for bench.py's measured peaks (not part of the GDPA ABI)
+    cmd = [_hipcc()] + _flags() + ["-shared", "-o", PROBE_LIB + ".tmp", os.path.join(HERE, "probe", "gdpa_peak.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
