@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     if (!wave_active) return;
     const int m0 = step_m0(i), mhi = m0 + BQ - 1;
     // wave-level classification of (queries m0..mhi, keys k0w..kmax_w)
-    bool empty = false, full = mhi < lq;
+    bool empty = false, full = true;  // Q / dO rows past the last query are zeros
     if (a.wr >= 0) {
       empty |= k0w > min(mhi, lq - 1) + off + a.wr;
       full &= kmax_w <= m0 + off + a.wr;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int b_lo = n0 + (kb0 + j) * 32, b_hi = b_lo + 31;  // keys of this 32-key block
-        bool empty = b_lo >= lk, full = b_hi < lk;
+        bool empty = b_lo >= lk, full = true;  // K / V rows past the last key are zeros
         if (a.wr >= 0) {
           empty |= b_lo > qmax_w + off + a.wr;
           full &= b_hi <= q0w + off + a.wr;

@@ -282,9 +282,14 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of 
 
 // Issue the HBM -> LDS copy of a [NROW x ROWB-byte] row tile with
 // buffer_load_dwordx4 ... lds.  rsrc covers the rows of one sequence (see
-// make_rsrc); row0_off is the byte offset of the tile's first row in it.  Rows
-// at or beyond nvalid (>= 1) are redirected to row nvalid-1; the kernel masks
-// the matching keys, so the duplicated rows never contribute.  (The FLAT form,
+// make_rsrc); row0_off is the byte offset of the tile's first row in it, and
+// nvalid (>= 1) the number of the sequence's rows from there on.  The resource
+// spans exactly the sequence's rows, so tile rows at or past nvalid are read
+// at row nvalid, the first row past the end: the range check turns those loads
+// into zeros, written to LDS, and no memory is read (offsets are computed
+// unsigned; the host keeps every span below 2^31 bytes).  Every activation maps
+// 0 to 0 with a finite derivative, so a zero K, V, Q or dO row adds nothing to
+// O, dV, dK or dQ, and tiles that run past a sequence's end need no mask.  (The FLAT form,
 // global_load_lds, would also work, but the compiler then treats LDS counters
 // as unordered and waits for lgkmcnt(0) before every later LDS read.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -308,9 +313,10 @@ __device__ __forceinline__ void stage_tile_buf(__amdgpu_buffer_rsrc_t rsrc, int 
     const int row = p / U, pc = p % U;
     int c = pc ^ chunk_swz<ROWB>(row);
     if constexpr (GCH < U) c = c < GCH ? c : c - (U - GCH);
-    const int voff = row0_off + min(row, nvalid - 1) * ld_bytes + c * 16;
+    const unsigned voff =
+        (unsigned)row0_off + (unsigned)min(row, nvalid) * (unsigned)ld_bytes + (unsigned)(c * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
-                                             voff, 0, 0, 0);
+                                             (int)voff, 0, 0, 0);
   }
 }
 

@@ -248,7 +248,8 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
     stage_tile_buf<BN, K::VROWB, NW, DV / 8>(vrs, n0 * (int)v_ld * 2, (int)v_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave, two 32-key blocks at a time; the mask is
-  // applied only where the window cuts a block or a block runs past the last key.
+  // applied only where the window cuts a block (K and V rows past the last key
+  // are staged as zeros and add nothing).
   auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
     if (!wave_active) return;
     const int n0 = nb * BN;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int b_lo = n0 + (kb0 + j) * 32, b_hi = b_lo + 31;  // keys of this 32-key block
-        bool empty = b_lo >= lk, full = b_hi < lk;
+        bool empty = b_lo >= lk, full = true;
         if (a.wr >= 0) {
           empty |= b_lo > qmax_w + off + a.wr;
           full &= b_hi <= q0w + off + a.wr;
