@@ -42,6 +42,16 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared_functions()) <= exported
 
 
+def test_probe_library_is_separate_and_exports_its_probe(lib):
+    # bench.py's peak probes live in their own library, outside the GDPA ABI
+    probe = os.path.join(ROOT, "generalized_attention_amd", "libgdpa_probe.so")
+    assert os.path.exists(probe)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True, check=True).stdout
+    assert re.search(r" T gdpa_probe_mfma$", out, re.M)
+    main = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    assert "gdpa_probe_mfma" not in main
+
+
 def test_abi_version_and_status_strings(lib):
     ver = int(re.search(r"#define GDPA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert lib.gdpa_abi_version() == ver
