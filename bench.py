@@ -130,10 +130,11 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None):
 
 
 def measured_peaks(torch):
-    """Sustained dense MFMA rates (bf16 32x32x16, FP8 32x32x64) over the whole
-    chip from the probe kernels in generalized_attention_amd/probe, and the
-    device-copy bandwidth (bytes read + written) of a 1 GiB torch copy; best
-    of 5 runs each."""
+    """Sustained dense MFMA rates (bf16 32x32x16, FP8 32x32x64, TFLOP/s) and
+    v_exp_f32 rate (lane results per second, in 1e12) over the whole chip from
+    the probe kernels in generalized_attention_amd/probe, and the device-copy
+    bandwidth (bytes read + written) of a 1 GiB torch copy; best of 5 runs
+    each."""
     import ctypes
     path = os.path.join(ROOT, "generalized_attention_amd", "libgdpa_probe.so")
     lib = ctypes.CDLL(path)
@@ -144,7 +145,7 @@ def measured_peaks(torch):
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {}
-    for kind, name, iters in ((0, "bf16_tflops", 20000), (1, "fp8_tflops", 10000)):
+    for kind, name, iters in ((0, "bf16_tflops", 20000), (1, "fp8_tflops", 10000), (2, "exp2_tops", 4000)):
         best = 0.0
         for _ in range(5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
