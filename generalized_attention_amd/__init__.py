@@ -122,10 +122,74 @@ def _out_dtype(t):
 
 
 def _grad_dtype(dq, dk, dv):
-    for t in (dq, dk, dv):
-        if t is not None:
-            return _out_dtype(t)
-    return DTYPE_FP32
+    given = [t for t in (dq, dk, dv) if t is not None]
+    if not given:
+        return DTYPE_FP32
+    kinds = {_out_dtype(t) for t in given}
+    if len(kinds) != 1:
+        raise TypeError(f"dq, dk and dv must share one dtype, got {[t.dtype for t in given]}")
+    return kinds.pop()
+
+
+def _expect(name, t, shape, device, dtypes=None):
+    """Checks that tensor `t` has the layout the C entry points assume
+    (contiguous, on `device`, of `shape`, of one of `dtypes`) before any call
+    into the library, which takes raw pointers on trust."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {tuple(dtypes)}")
+
+
+_IN16 = (torch.bfloat16, torch.float16)
+_QK = (torch.bfloat16, torch.float16, torch.float8_e4m3fn, torch.uint8)
+_OUT = (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _check_fwd_args(q, k, v, o, jagged):
+    dev = q.device
+    if jagged:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("jagged q/k/v are [total, heads, head_dim]")
+        _expect("k", k, (k.shape[0], k.shape[1], q.shape[2]), dev, _QK)
+        _expect("v", v, (k.shape[0], k.shape[1], v.shape[2]), dev, _IN16)
+        _expect("o", o, (q.shape[0], q.shape[1], v.shape[2]), dev, _OUT)
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("fixed-length q/k/v are [batch, seqlen, heads, head_dim]")
+        _expect("k", k, (q.shape[0], k.shape[1], k.shape[2], q.shape[3]), dev, _QK)
+        _expect("v", v, (q.shape[0], k.shape[1], k.shape[2], v.shape[3]), dev, _IN16)
+        _expect("o", o, (*q.shape[:3], v.shape[-1]), dev, _OUT)
+    _expect("q", q, q.shape, dev, _QK)
+    if _qk_dtype(q) != _qk_dtype(k):
+        raise TypeError(f"q and k must share one dtype, got {q.dtype} and {k.dtype}")
+
+
+def _check_bwd_args(q, k, v, dout, dq, dk, dv, jagged):
+    dev = q.device
+    _check_fwd_args(q, k, v, None, jagged)
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise TypeError(f"q, k, v and dout must share one dtype, got {q.dtype}, {k.dtype}, {v.dtype}, {dout.dtype}")
+    _expect("dout", dout, (*q.shape[:-1], v.shape[-1]), dev, _IN16)
+    _expect("dq", dq, q.shape, dev, _OUT)
+    _expect("dk", dk, k.shape, dev, _OUT)
+    _expect("dv", dv, v.shape, dev, _OUT)
+    if (dk is None) != (dv is None):
+        raise ValueError("dk and dv are requested together (both tensors or both None)")
+
+
+def _check_cu(cu_q, cu_k, device):
+    for name, t in (("cu_seqlens_q", cu_q), ("cu_seqlens_k", cu_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous int32 vector on {device}")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
 
 
 def _workspace(nbytes, device):
@@ -138,6 +202,7 @@ def _workspace(nbytes, device):
 def gdpa_fwd(q, k, v, o, scale, act="fast_gelu", act_param=0.01, mask="none", window_left=-1,
              window_right=-1, q_descale=1.0, k_descale=1.0):
     """Fixed-length forward: q/o [B, Lq, Hq, D], k/v [B, Lk, Hkv, D]; writes o."""
+    _check_fwd_args(q, k, v, o, jagged=False)
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     ws, nws = _workspace(_lib.gdpa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
@@ -153,6 +218,8 @@ def gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_se
                     act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1,
                     q_descale=1.0, k_descale=1.0):
     """Jagged forward: q/o [total_q, Hq, D], k/v [total_k, Hkv, D], cu_seqlens int32 [B+1]."""
+    _check_fwd_args(q, k, v, o, jagged=True)
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
     B = cu_seqlens_q.numel() - 1
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
@@ -169,6 +236,7 @@ def gdpa_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_se
 def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, mask="none",
              window_left=-1, window_right=-1):
     """Fixed-length backward; writes dq (may be None) and dk/dv (both may be None)."""
+    _check_bwd_args(q, k, v, dout, dq, dk, dv, jagged=False)
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
@@ -182,6 +250,8 @@ def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, 
 def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
                     act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1):
     """Jagged backward; writes dq (may be None) and dk/dv (both may be None)."""
+    _check_bwd_args(q, k, v, dout, dq, dk, dv, jagged=True)
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
     B = cu_seqlens_q.numel() - 1
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]

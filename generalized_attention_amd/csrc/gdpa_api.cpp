@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "gdpa_kernels.hpp"
@@ -86,6 +87,19 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
     return GDPA_ERR_UNSUPPORTED;
   *c = Common{batch, max_lq, max_lk, hq, hkv, d, dv, total_q, total_k, kind, wl, wr};
   return GDPA_OK;
+}
+
+// Kernels built per input element kind and (Q/K, V) head dims: 16-bit inputs
+// at (64, 64), (96, 96), (128, 128) and, forward only, (192, 128); FP8 Q/K
+// (forward only) at (64, 64), (96, 96) and (128, 128).  Every entry point
+// checks its combination here, before the schedule kernel or any other HIP
+// call is queued.
+bool fwd_built(int in_kind, int32_t d, int32_t dv) {
+  if (d == dv && (d == 64 || d == 96 || d == 128)) return true;
+  return in_kind != gdpa::EL_FP8 && d == 192 && dv == 128;
+}
+bool bwd_built(int in_kind, int32_t d, int32_t dv) {
+  return in_kind != gdpa::EL_FP8 && d == dv && (d == 64 || d == 96 || d == 128);
 }
 
 // Output dtype -> kernel output kind (-1: not an output type).
@@ -195,15 +209,20 @@ gdpa_status_t debug_check_jagged(const int32_t* cu_q, const int32_t* cu_k, const
   return st;
 }
 
-// Compute units of the current device (0 if unknown), cached per device.
+// Compute units of the current device (0 if unknown), cached per device.  The
+// cache entries are atomics: concurrent callers on other threads may both
+// query the attribute, and both store the same value.
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static int cache[64] = {};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  static std::atomic<int> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -250,6 +269,7 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   if (f16 != (qk_dtype == GDPA_DTYPE_FP16)) return GDPA_ERR_UNSUPPORTED;
   const int in_kind = fp8 ? gdpa::EL_FP8 : f16 ? gdpa::EL_F16 : gdpa::EL_BF16;
   if (fp8 && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
+  if (!fwd_built(in_kind, c.d, c.dv)) return GDPA_ERR_UNSUPPORTED;
   if (c.batch == 0 || c.total_q == 0) return GDPA_OK;
   if (q == nullptr || o == nullptr) return GDPA_ERR_INVALID_ARG;
   if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
@@ -300,9 +320,9 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
                       void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (in_dtype == GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_UNSUPPORTED;
-  if (c.dv != c.d) return GDPA_ERR_UNSUPPORTED;  // (192, 128): forward only
+  if (in_dtype == GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_UNSUPPORTED;  // FP8 is forward-only
   if (in_dtype != GDPA_DTYPE_BF16 && in_dtype != GDPA_DTYPE_FP16) return GDPA_ERR_INVALID_ARG;
+  if (!bwd_built(in_dtype == GDPA_DTYPE_FP16 ? gdpa::EL_F16 : gdpa::EL_BF16, c.d, c.dv)) return GDPA_ERR_UNSUPPORTED;
   const int out_kind = out_kind_of(grad_dtype);
   if (out_kind < 0) return GDPA_ERR_INVALID_ARG;
   const bool f16 = in_dtype == GDPA_DTYPE_FP16;

@@ -33,8 +33,9 @@
  *    have the layouts of q/k/v.
  *    cu_seqlens_{q,k}: device int32 [B+1], cu[0] = 0, non-decreasing,
  *    cu[B] = total.  Zero-length sequences are allowed.
- *  - Element types: inputs bf16 (or FP8 E4M3 codes for q/k in the forward,
- *    with fp32 per-tensor descales); outputs fp32 or bf16.
+ *  - Element types: inputs bf16 or fp16 (or, forward only, FP8 E4M3 codes
+ *    for q/k with fp32 per-tensor descales and bf16 v); outputs fp32, bf16
+ *    or fp16 (fp32 is the mode whose accuracy the tests bound most tightly).
  *  - Outputs are overwritten, never accumulated into.  Query rows with no
  *    allowed key get O = 0 and dQ = 0; keys no query attends get dK = dV = 0.
  *    dK/dV are summed over the query heads of each KV group.
@@ -112,7 +113,8 @@ typedef enum {
  *   q, k, v, o     : device tensors in the layouts above.
  *   head_dim, head_dim_v : head dims of Q/K and of V/O: (64, 64), (96, 96),
  *                    (128, 128), or (192, 128) (the README's "(192, 128)"; 16-bit
- *                    inputs, forward only).  Other pairs: GDPA_ERR_UNSUPPORTED.
+ *                    inputs only).  Other pairs, and FP8 q/k at (192, 128),
+ *                    return GDPA_ERR_UNSUPPORTED before anything is queued.
  *   scale          : multiplies Q K^T inside the activation (FA softmax_scale).
  *   qk_dtype, v_dtype : BF16 and BF16, FP16 and FP16, or FP8_E4M3 (q and k
  *                    codes) and BF16.  P is rounded to v's type for P V, so

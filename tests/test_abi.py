@@ -191,6 +191,22 @@ def test_workspace_queries(lib):
         assert f(0, 1024, 1024, 4, 4, 128) == 0
 
 
+@pytest.mark.parametrize("call", ["fixed", "jagged", "jagged_with_workspace"])
+def test_fp8_at_head_dims_192_128_is_unsupported_before_any_launch(lib, call):
+    # FP8 Q/K are built at head dims 64, 96 and 128 only; (192, 128) must be
+    # refused on the host, before the schedule kernel of a jagged call is queued
+    # (FAKE pointers: any HIP call on them would fail with GDPA_ERR_HIP instead)
+    kw = dict(D=192, Dv=128, qk=2, vd=0)
+    if call == "fixed":
+        assert fwd(lib, **kw) == UNSUPPORTED
+    elif call == "jagged":
+        assert varlen_fwd(lib, **kw) == UNSUPPORTED
+    else:
+        nws = lib.gdpa_varlen_fwd_workspace_size(2, 128, 128, 4, 4, 192)
+        assert nws > 0
+        assert varlen_fwd(lib, ws=FAKE, nws=nws, **kw) == UNSUPPORTED
+
+
 def test_jagged_calls_check_the_workspace_before_launching(lib):
     # valid arguments, no workspace: refused on the host, nothing launched
     assert varlen_fwd(lib) == WS_SMALL
@@ -226,3 +242,84 @@ def test_flash_attn_mask_arguments(causal, window, expect):
     # the README's call form (causal, window_size) -> the C ABI's mask arguments
     import generalized_attention_amd as g
     assert g._mask_args(causal, window) == expect
+
+
+# ------------------------------------------------ binding-side argument checks
+# The C entry points take raw pointers on trust; the binding checks dtypes,
+# shapes, contiguity and devices first.  Every case below is invalid, so it
+# must raise before any library call (the tensors live on the CPU).
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _bwd_case(name):
+    import torch
+    B, L, H, D = 2, 16, 2, 64
+    a = dict(q=_cpu((B, L, H, D)), k=_cpu((B, L, H, D)), v=_cpu((B, L, H, D)), dout=_cpu((B, L, H, D)),
+             dq=_cpu((B, L, H, D), torch.float32), dk=_cpu((B, L, H, D), torch.float32),
+             dv=_cpu((B, L, H, D), torch.float32))
+    if name == "mixed_grad_dtypes":
+        a["dk"] = _cpu((B, L, H, D), torch.bfloat16)
+    elif name == "dq_wrong_shape":
+        a["dq"] = _cpu((B, L, H, 2 * D), torch.float32)
+    elif name == "dv_not_contiguous":
+        a["dv"] = _cpu((B, L, H, 2 * D), torch.float32)[..., :D]
+    elif name == "dout_other_dtype":
+        a["dout"] = _cpu((B, L, H, D), torch.float16)
+    elif name == "k_other_dtype":
+        a["k"] = _cpu((B, L, H, D), torch.float16)
+    elif name == "dk_without_dv":
+        a["dv"] = None
+    elif name == "int_grads":
+        a["dq"] = a["dk"] = a["dv"] = _cpu((B, L, H, D), torch.int32)
+    return a
+
+
+@pytest.mark.parametrize("name,exc", [
+    ("mixed_grad_dtypes", TypeError), ("dq_wrong_shape", ValueError), ("dv_not_contiguous", ValueError),
+    ("dout_other_dtype", TypeError), ("k_other_dtype", TypeError), ("dk_without_dv", ValueError),
+    ("int_grads", TypeError),
+])
+def test_binding_rejects_bad_backward_tensors(lib, name, exc):
+    import generalized_attention_amd as g
+    a = _bwd_case(name)
+    with pytest.raises(exc):
+        g.gdpa_bwd(a["q"], a["k"], a["v"], a["dout"], a["dq"], a["dk"], a["dv"], 0.125)
+
+
+@pytest.mark.parametrize("name,exc", [
+    ("o_wrong_shape", ValueError), ("o_not_contiguous", ValueError), ("o_int", TypeError),
+    ("v_wrong_heads", ValueError), ("q_fp32", TypeError),
+])
+def test_binding_rejects_bad_forward_tensors(lib, name, exc):
+    import torch
+    import generalized_attention_amd as g
+    B, L, H, D = 2, 16, 2, 64
+    q, k, v = _cpu((B, L, H, D)), _cpu((B, L, H, D)), _cpu((B, L, H, D))
+    o = _cpu((B, L, H, D), torch.float32)
+    if name == "o_wrong_shape":
+        o = _cpu((B, L + 1, H, D), torch.float32)
+    elif name == "o_not_contiguous":
+        o = _cpu((B, L, H, 2 * D), torch.float32)[..., ::2]
+    elif name == "o_int":
+        o = _cpu((B, L, H, D), torch.int32)
+    elif name == "v_wrong_heads":
+        v = _cpu((B, L, H + 1, D))
+    elif name == "q_fp32":
+        q = _cpu((B, L, H, D), torch.float32)
+    with pytest.raises(exc):
+        g.gdpa_fwd(q, k, v, o, 0.125)
+
+
+def test_binding_rejects_bad_cu_seqlens(lib):
+    import torch
+    import generalized_attention_amd as g
+    q, k, v = _cpu((10, 2, 64)), _cpu((10, 2, 64)), _cpu((10, 2, 64))
+    o = _cpu((10, 2, 64), torch.float32)
+    cu64 = torch.tensor([0, 4, 10], dtype=torch.int64)
+    cu32 = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        g.gdpa_varlen_fwd(q, k, v, o, cu64, cu32, 6, 6, 0.125)
+    with pytest.raises(ValueError):
+        g.gdpa_varlen_fwd(q, k, v, o, cu32, cu32[:2], 6, 6, 0.125)
