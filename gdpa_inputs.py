@@ -146,6 +146,15 @@ def draw_lengths(rng, batch, rng_range):
     return rng.integers(lo, hi + 1, size=batch).astype(np.int64)
 
 
+def draw_seqlens(wl: Workload, seed: Optional[int] = None):
+    """The (Q lengths, KV lengths) that make_batch draws for `wl`, without the
+    tensors (same generator, same draw order)."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    lq = draw_lengths(rng, wl.batch, wl.lq_range)
+    lk = lq.copy() if wl.lk_range is None else draw_lengths(rng, wl.batch, wl.lk_range)
+    return lq, lk
+
+
 def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool] = None,
                seqlens_q=None, seqlens_k=None) -> Batch:
     """Draw one instance of `wl`.

@@ -31,7 +31,7 @@ ACT = {
 MASK = {"none": 0, "causal": 1, "window": 2, "sliding_window": 2}
 DTYPE_BF16, DTYPE_FP16, DTYPE_FP8_E4M3, DTYPE_FP32 = 0, 1, 2, 3
 STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_UNSUPPORTED",
-          3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP"}
+          3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP", 5: "GDPA_ERR_DEVICE_WAIT"}
 
 EXPORTED = (
     "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd",
@@ -63,10 +63,13 @@ def _load():
                                     I32, I32, I32, I32, F32, I32, I32, P, SZ, P]
     for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
         getattr(lib, n).restype = ctypes.c_int
-    for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
-              "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
+    for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size"):
         getattr(lib, n).argtypes = [I32] * 6
         getattr(lib, n).restype = SZ
+    lib.gdpa_bwd_workspace_size.argtypes = [I32] * 7
+    lib.gdpa_bwd_workspace_size.restype = SZ
+    lib.gdpa_varlen_bwd_workspace_size.argtypes = [I32, I32, I32, I64, I32, I32, I32, I32]
+    lib.gdpa_varlen_bwd_workspace_size.restype = SZ
     lib.gdpa_status_string.argtypes = [ctypes.c_int]
     lib.gdpa_status_string.restype = ctypes.c_char_p
     lib.gdpa_abi_version.restype = I32
@@ -239,10 +242,11 @@ def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, 
     _check_bwd_args(q, k, v, dout, dq, dk, dv, jagged=False)
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
-    ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D), q.device)
+    gd = _grad_dtype(dq, dk, dv)
+    ws, nws = _workspace(_lib.gdpa_bwd_workspace_size(B, Lq, Lk, Hq, Hkv, D, gd), q.device)
     st = _lib.gdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, Lq, Lk, Hq, Hkv,
                        D, v.shape[-1], float(scale), _mask(mask), window_left, window_right, _act(act), float(act_param),
-                       _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws), nws, _stream(q.device))
+                       _qk_dtype(q), gd, _ptr(ws), nws, _stream(q.device))
     _check(st, "gdpa_bwd")
     return dq, dk, dv
 
@@ -255,12 +259,14 @@ def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_s
     B = cu_seqlens_q.numel() - 1
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
-    ws, nws = _workspace(_lib.gdpa_varlen_bwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
+    gd = _grad_dtype(dq, dk, dv)
+    ws, nws = _workspace(_lib.gdpa_varlen_bwd_workspace_size(B, max_seqlen_q, max_seqlen_k, q.shape[0], Hq, Hkv, D, gd),
+                         q.device)
     st = _lib.gdpa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k),
                               q.shape[0], k.shape[0], Hq, Hkv, D, v.shape[-1], float(scale), _mask(mask),
                               window_left,
-                              window_right, _act(act), float(act_param), _qk_dtype(q), _grad_dtype(dq, dk, dv), _ptr(ws),
+                              window_right, _act(act), float(act_param), _qk_dtype(q), gd, _ptr(ws),
                               nws, _stream(q.device))
     _check(st, "gdpa_varlen_bwd")
     return dq, dk, dv

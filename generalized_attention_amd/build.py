@@ -16,8 +16,10 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdpa.so")
 PROBE_LIB = os.path.join(HERE, "libgdpa_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip", "gdpa_sched.hip",
-           "gdpa_api.cpp"]
+BWD_UNITS = [f"gdpa_bwd_{t}_{d}.hip" for t in ("bf16", "f16") for d in (64, 96, 128)]
+FUSED_UNITS = [f"gdpa_bwdf_{t}_{d}.hip" for t in ("bf16", "f16") for d in (64, 96, 128)]
+SOURCES = FUSED_UNITS + BWD_UNITS + ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_sched.hip",
+                                     "gdpa_api.cpp"]
 # Per-source code generation options.  The forward kernels keep their MFMA
 # accumulators in architectural VGPRs (the activation reads the S tile with
 # no accumulator-to-VGPR copies; the register file still fits two workgroups
@@ -26,9 +28,8 @@ SOURCES = ["gdpa_fwd.hip", "gdpa_fwd_f16.hip", "gdpa_bwd.hip", "gdpa_bwd_f16.hip
 # completely: a partly unrolled stream indexes its register arrays at run time
 # and the compiler moves them to scratch or LDS.
 EXTRA = {"gdpa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"],
-         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"],
-         "gdpa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "gdpa_bwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "gdpa_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"]}
+EXTRA.update({u: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for u in BWD_UNITS})
 ARCH = "gfx950"
 
 
@@ -60,7 +61,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every source and link libgdpa.so; always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs

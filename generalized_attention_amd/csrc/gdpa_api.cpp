@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <cstring>
 #include <algorithm>
 #include <atomic>
 #include <vector>
@@ -178,6 +179,35 @@ size_t schedule_bytes(int64_t batch) {
   return (size_t)(((batch + gdpa::kNumCounters) * 4 + 255) / 256 * 256);
 }
 
+// Backward workspace, each part 256-byte aligned:
+//   order  int32 [batch]        longest-first sequence order (jagged calls of up
+//                                to kSortMax sequences; index order otherwise)
+//   queues int32 [kQWords]      per-XCD queue heads and owners, then the flag a
+//                                dQ turn wait sets when it gives up
+//   turns  int32 [tiles * hq]   dQ turn counters per (64-row query tile, head):
+//                                tiles = total_q / 64 + batch + 1 (jagged) or
+//                                batch * ceil(seqlen_q / 64)
+//   acc    fp32 [total_q, hq, d] dQ accumulator, when dQ is stored in 16 bits
+struct BwdLayout {
+  size_t order, queues, turns, acc, bytes;
+  int64_t nturn;  // turn counters
+};
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+BwdLayout bwd_layout(int64_t batch, bool jagged, int64_t max_lq, int64_t total_q, int64_t hq, int64_t d,
+                     bool acc16) {
+  BwdLayout l{};
+  if (batch <= 0) return l;
+  const int64_t tiles = jagged ? total_q / gdpa::kDqTile + batch + 1
+                               : batch * ((max_lq + gdpa::kDqTile - 1) / gdpa::kDqTile);
+  l.nturn = tiles * hq;
+  l.order = 0;
+  l.queues = jagged && batch <= gdpa::kSortMax ? align256((size_t)batch * 4) : 0;
+  l.turns = l.queues + align256(gdpa::kQWords * 4);
+  l.acc = l.turns + align256((size_t)l.nturn * 4);
+  l.bytes = l.acc + (acc16 ? align256((size_t)total_q * hq * d * 4) : 0);
+  return l;
+}
+
 // GDPA_DEBUG_CHECKS=1 (read at every call): jagged calls copy cu_seqlens to the
 // host, synchronising the caller's stream, and reject device data that the
 // kernels would otherwise take on trust.
@@ -316,6 +346,17 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
                     "forward launch");
 }
 
+// Polls of a dQ turn wait before it gives up; GDPA_DEBUG_SPIN_LIMIT (read in
+// the debug mode only) overrides it, a negative value making every wait give
+// up at once (to exercise the error path).
+int32_t spin_limit() {
+  if (debug_checks()) {
+    const char* e = std::getenv("GDPA_DEBUG_SPIN_LIMIT");
+    if (e != nullptr && e[0] != '\0') return (int32_t)std::strtol(e, nullptr, 10);
+  }
+  return 1 << 21;
+}
+
 gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                       void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
@@ -337,10 +378,13 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   if ((int64_t)c.max_lq * c.hq * c.d * 2 > INT32_MAX || (int64_t)c.max_lk * c.hkv * c.d * 2 > INT32_MAX)
     return GDPA_ERR_UNSUPPORTED;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kBwdBM - 1) / gdpa::kBwdBM;
-  const int64_t nblocks = ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN;
+  const int64_t nblocks = std::max<int64_t>(1, ((int64_t)c.max_lk + gdpa::kBwdBN - 1) / gdpa::kBwdBN);
   if (gdpa::pair_grid(c.batch, c.hkv, (long)(c.hq / c.hkv) * mblocks) > kMaxGrid ||
       gdpa::pair_grid(c.batch, c.hkv, nblocks) > kMaxGrid)
     return GDPA_ERR_UNSUPPORTED;
+  const bool jagged = cu_q != nullptr;
+  const BwdLayout lay = bwd_layout(c.batch, jagged, c.max_lq, c.total_q, c.hq, c.d, out_kind != gdpa::OUT_F32);
+  if (workspace == nullptr || workspace_bytes < lay.bytes) return GDPA_ERR_WORKSPACE_TOO_SMALL;
 
   BwdArgs a{};
   a.q = q;
@@ -366,16 +410,59 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.out_kind = out_kind;
   a.dsplit = !f16 && few_terms(c.max_lk, 1, c) ? 1 : 0;
   a.kvsplit = !f16 && few_terms(c.max_lq, a.group, c) ? 1 : 0;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.qstate = reinterpret_cast<int32_t*>(ws + lay.queues);
+  a.turn = reinterpret_cast<int32_t*>(ws + lay.turns);
+  a.dq_acc = out_kind == gdpa::OUT_F32 ? static_cast<float*>(dq) : reinterpret_cast<float*>(ws + lay.acc);
+  a.mt_fixed = (int32_t)(((int64_t)c.max_lq + gdpa::kDqTile - 1) / gdpa::kDqTile);
+  a.spin_limit = spin_limit();
+  a.ncu = device_cu_count();
+  // dQ comes from the dK/dV pass (five products; partial sums of a query tile
+  // from several key blocks meet in an ordered fp32 reduction) or from a
+  // separate kernel that recomputes S and dP (seven products, no reduction).
+  // Each key block that reaches a query tile adds a read and a write of the
+  // tile's fp32 partial sums, which cost more than the recomputation once a
+  // tile has several contributors, so the fused pass is the default only when
+  // every sequence's keys fit one block; GDPA_BWD_DQ=fused|separate overrides.
+  // The fused pass also needs all three gradients, at most one of the two
+  // word splits and a sequence's fp32 dQ rows within 32-bit offsets.
+  const char* mode = std::getenv("GDPA_BWD_DQ");
+  const bool force_fused = mode != nullptr && std::strcmp(mode, "fused") == 0;
+  const bool force_separate = mode != nullptr && std::strcmp(mode, "separate") == 0;
+  const bool fused = want_dq && want_dkv && !(a.dsplit && a.kvsplit) && a.ncu > 0 && !force_separate &&
+                     (force_fused || c.max_lk <= gdpa::kBwdBN) &&
+                     ((int64_t)c.max_lq + gdpa::kDqTile) * c.hq * c.d * 4 <= INT32_MAX;
   gdpa_status_t sst = debug_check_jagged(cu_q, cu_k, c, stream);
   if (sst != GDPA_OK) return sst;
-  sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &a.counters, &a.ncu);
-  if (sst != GDPA_OK) return sst;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (jagged && c.batch <= gdpa::kSortMax) {
+    // longest-first order; also zeroes the first queue words
+    sst = hip_status(gdpa::launch_schedule(cu_q, cu_k, c.batch, reinterpret_cast<int32_t*>(ws + lay.order),
+                                           a.qstate, hs),
+                     "schedule launch");
+    if (sst != GDPA_OK) return sst;
+    a.perm = reinterpret_cast<const int32_t*>(ws + lay.order);
+  }
+  if (fused) {
+    // queue heads and owners, the error flag and the turn counters start at zero
+    sst = hip_status(gdpa::launch_zero(a.qstate, (long)((lay.acc - lay.queues) / 4), hs), "workspace clear");
+    if (sst != GDPA_OK) return sst;
+  } else if (a.perm != nullptr && a.ncu > 0) {
+    a.counters = a.qstate;  // the dK/dV kernel's work queues (zeroed by the schedule)
+  }
   if (debug_log())
-    std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d\n", c.batch,
-                 c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr);
-  return hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, f16 ? gdpa::EL_F16 : gdpa::EL_BF16, want_dq, want_dkv,
-                                     static_cast<hipStream_t>(stream)),
-                    "backward launch");
+    std::fprintf(stderr, "[gdpa] bwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d wl=%d wr=%d fused=%d\n", c.batch,
+                 c.max_lq, c.max_lk, c.hq, c.hkv, c.d, c.act_kind, c.wl, c.wr, (int)fused);
+  sst = hip_status(gdpa::launch_bwd(a, c.d, c.act_kind, f16 ? gdpa::EL_F16 : gdpa::EL_BF16, want_dq, want_dkv, fused,
+                                    hs),
+                   "backward launch");
+  if (sst != GDPA_OK || !fused || !debug_checks()) return sst;
+  // debug mode: wait for the kernel and report a dQ turn wait that gave up
+  int32_t flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, a.qstate + gdpa::kQErr, sizeof(flag), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_status(e, "wait-flag readback");
+  return flag != 0 ? GDPA_ERR_DEVICE_WAIT : GDPA_OK;
 }
 
 }  // namespace
@@ -450,9 +537,17 @@ size_t gdpa_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int3
 size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t, int32_t, int32_t, int32_t, int32_t) {
   return schedule_bytes(batch);
 }
-size_t gdpa_bwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
-size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t, int32_t, int32_t, int32_t, int32_t) {
-  return schedule_bytes(batch);
+size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t, int32_t num_heads_q, int32_t,
+                               int32_t head_dim, int32_t grad_dtype) {
+  if (batch <= 0 || seqlen_q < 0 || num_heads_q <= 0 || head_dim <= 0) return 0;
+  return bwd_layout(batch, false, seqlen_q, (int64_t)batch * seqlen_q, num_heads_q, head_dim,
+                    grad_dtype != GDPA_DTYPE_FP32)
+      .bytes;
+}
+size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t, int64_t total_q,
+                                      int32_t num_heads_q, int32_t, int32_t head_dim, int32_t grad_dtype) {
+  if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || num_heads_q <= 0 || head_dim <= 0) return 0;
+  return bwd_layout(batch, true, max_seqlen_q, total_q, num_heads_q, head_dim, grad_dtype != GDPA_DTYPE_FP32).bytes;
 }
 
 const char* gdpa_status_string(gdpa_status_t s) {
@@ -462,6 +557,7 @@ const char* gdpa_status_string(gdpa_status_t s) {
     case GDPA_ERR_UNSUPPORTED: return "GDPA_ERR_UNSUPPORTED";
     case GDPA_ERR_WORKSPACE_TOO_SMALL: return "GDPA_ERR_WORKSPACE_TOO_SMALL";
     case GDPA_ERR_HIP: return "GDPA_ERR_HIP";
+    case GDPA_ERR_DEVICE_WAIT: return "GDPA_ERR_DEVICE_WAIT";
     default: return "GDPA_ERR_UNKNOWN";
   }
 }

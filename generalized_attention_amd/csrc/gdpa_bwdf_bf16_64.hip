@@ -1,0 +1,8 @@
+// Fused backward kernels (dK, dV and dQ in one pass) for bf16 inputs at head dim 64.
+#include "gdpa_bwd.hpp"
+
+namespace gdpa {
+
+template hipError_t launch_bwd_fused_ed<EL_BF16, 64>(const BwdArgs&, int, hipStream_t);
+
+}  // namespace gdpa

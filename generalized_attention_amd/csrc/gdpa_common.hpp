@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdpa_kernels.hpp"
 
 namespace gdpa {
@@ -108,6 +110,19 @@ __device__ __forceinline__ void store4(void* base, long idx, float x0, float x1,
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack2<EL_BF16>(x0, x1), pack2<EL_BF16>(x2, x3)};
   else
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack2<EL_F16>(x0, x1), pack2<EL_F16>(x2, x3)};
+}
+
+// Calls f(std::integral_constant<int, i>) for i = I .. N-1 in order: a loop
+// whose index is a compile-time constant in the body, with no reliance on the
+// loop unroller (long unit streams exceed its default threshold, and a partly
+// unrolled stream indexes its register arrays at run time, which moves them
+// to scratch memory).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -347,6 +362,17 @@ struct TileOffs {
   static constexpr int NDB = ROWB / 64;  // 32-column head-dim blocks per row
   int row[KS];
   int tr[NDB][2];
+  // Transposed-read offsets of head-dim block db (db may be a run-time value:
+  // computed, not looked up, so no register array is indexed at run time).
+  static __device__ __forceinline__ void tr_of(int lane, int db, int (&o)[2]) {
+    const int g = lane >> 4, rr = lane & 15;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 8 * c + 4 * (g >> 1) + (rr >> 2);
+      const int col = 32 * db + 16 * (g & 1) + 4 * (rr & 3);
+      o[c] = row * ROWB + (((col >> 3) ^ chunk_swz<ROWB>(row)) << 4) + ((col & 4) << 1);
+    }
+  }
   static __device__ __forceinline__ TileOffs make(int lane) {
     TileOffs o;
     const int r = lane & 31, hf = lane >> 5;

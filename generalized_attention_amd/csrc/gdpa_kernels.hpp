@@ -91,6 +91,13 @@ struct BwdArgs {
   const int32_t* perm;  // sequences in processing order (longest first), or nullptr
   int32_t* counters;    // per-XCD dK/dV work-queue counters (zeroed by the schedule), or nullptr
   int32_t ncu;          // compute units of the device (sizes the work-queue launches)
+  // Fused backward (dQ accumulated inside the dK/dV kernel), all zeroed by
+  // the call before the kernel runs:
+  float* dq_acc;        // fp32 dQ accumulator [total_q, hq, D] (dq itself when dQ is fp32)
+  int32_t* turn;        // per (64-row query tile, query head) turn counters
+  int32_t* qstate;      // per queue: next item [8], owning XCD + 1 [8]; then the error flag
+  int32_t mt_fixed;     // fixed-length batches: 64-row query tiles per sequence
+  int32_t spin_limit;   // polls before a turn wait gives up and sets the error flag
 };
 
 // Forward workgroup: kFwdNW waves, each owning 32 query rows.
@@ -158,6 +165,16 @@ constexpr int kSortMax = 4096;
 constexpr int kNumCounters = kNumXcd;
 hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
                            hipStream_t stream);
+// Zeroes n int32 words at p (a kernel, not a memset, so the call stays
+// capturable in a graph).
+hipError_t launch_zero(int32_t* p, long n, hipStream_t stream);
+
+// Fused backward: queue state layout inside BwdArgs::qstate.
+constexpr int kQNext = 0, kQOwner = kNumXcd, kQErr = 2 * kNumXcd, kQWords = 2 * kNumXcd + 1;
+// Turn counters are indexed by (first tile of the sequence + tile) * hq + head
+// with a sequence's first tile at cu_q[b] / 64 + b (jagged) or b * mt_fixed:
+// fewer than total_q / 64 + batch tiles in all.
+constexpr int kDqTile = 64;
 
 // Work-queue execution (jagged batches with a schedule): a launch of as many
 // workgroups as the device holds at once.  Work is still grouped by (sequence,
@@ -191,10 +208,8 @@ constexpr int kBwdBM = 128;
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, int in_kind, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int act_kind, int in_kind, bool want_dq, bool want_dkv,
-                      hipStream_t stream);
-// fp16 instantiations (own translation units)
+                      bool fused, hipStream_t stream);
+// fp16 forward instantiations (own translation unit)
 hipError_t launch_fwd_f16(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream);
-hipError_t launch_bwd_f16(const BwdArgs& a, int head_dim, int act_kind, bool want_dq, bool want_dkv,
-                          hipStream_t stream);
 
 }  // namespace gdpa

@@ -66,6 +66,29 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
   for (int i = threadIdx.x; i < batch; i += blockDim.x) perm[i] = (int32_t)(uint32_t)key[i];
 }
 
+__global__ __launch_bounds__(256) void gdpa_zero_kernel(int32_t* p, long n) {
+  // 16-byte stores over the 16-byte-aligned body, words before and after it singly
+  const long head = (long)((16 - ((uintptr_t)p & 15)) & 15) / 4;
+  const long h = head < n ? head : n;
+  const long body = (n - h) / 4;
+  const long stride = (long)gridDim.x * blockDim.x;
+  const long t0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (long i = t0; i < h; i += stride) p[i] = 0;
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  i32x4* q = reinterpret_cast<i32x4*>(p + h);
+  for (long i = t0; i < body; i += stride) q[i] = i32x4{0, 0, 0, 0};
+  for (long i = h + 4 * body + t0; i < n; i += stride) p[i] = 0;
+}
+
+hipError_t launch_zero(int32_t* p, long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  long blocks = (n / 4 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(gdpa_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
                            hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;

@@ -61,14 +61,19 @@
 extern "C" {
 #endif
 
-#define GDPA_ABI_VERSION 2  /* 2: head_dim_v after head_dim in the four entry points */
+#define GDPA_ABI_VERSION 3  /* 2: head_dim_v after head_dim in the four entry points;
+                               3: backward workspace queries take the dQ storage type
+                               (and the jagged one total_q), fixed-length backward
+                               calls need a workspace, GDPA_ERR_DEVICE_WAIT */
 
 typedef enum {
   GDPA_OK = 0,
   GDPA_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0, bad enum */
   GDPA_ERR_UNSUPPORTED = 2,          /* valid but not implemented (head dim, dtype combination) */
   GDPA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the *_workspace_size() query */
-  GDPA_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
+  GDPA_ERR_HIP = 4,                  /* a HIP runtime call or kernel launch failed */
+  GDPA_ERR_DEVICE_WAIT = 5           /* debug mode only (GDPA_DEBUG_CHECKS): a wait of the
+                                        ordered dQ reduction gave up; gradients are invalid */
 } gdpa_status_t;
 
 /* Activation replacing softmax (README "Features": custom activations).
@@ -155,11 +160,17 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
  * the products (the README lists FP8 as forward-only, so an FP8 in_dtype
  * returns GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout;
  * all three are written in grad_dtype (GDPA_DTYPE_FP32, GDPA_DTYPE_BF16 or
- * GDPA_DTYPE_FP16).  The dQ
- * reduction over key blocks runs in a fixed order (deterministic).
+ * GDPA_DTYPE_FP16).  head_dim_v must equal head_dim (64, 96 or 128).
+ * dQ sums the partial products of all key blocks in a fixed order, so results
+ * are bitwise reproducible (an fp32 reduction inside the workspace, or inside
+ * dq itself when grad_dtype is FP32: dq is then written more than once
+ * during the call).
  * Partial gradients: dq == NULL skips dQ; dk == dv == NULL skips dK and dV
  * (e.g. frozen keys/values).  dk and dv must be both NULL or both non-NULL,
- * and at least one gradient must be requested (else GDPA_ERR_INVALID_ARG). */
+ * and at least one gradient must be requested (else GDPA_ERR_INVALID_ARG).
+ * The workspace (gdpa_*bwd_workspace_size with this grad_dtype) is required
+ * by every backward call that has work to do; it is cleared and written on
+ * the device by the call itself. */
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout,
                        void* dq, void* dk, void* dv,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
@@ -181,23 +192,31 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace each call needs, in bytes (0 = none; pass NULL then).  Arguments
- * mirror the shape arguments of the matching entry point.  Jagged calls of
- * 1..4096 sequences need 4 bytes per sequence plus 32, rounded up to 256: the
- * call first builds there, on the device, the order in which sequences are
- * processed (longest first) and the counters of the work queues its kernels
- * draw items from (see the README's load-balanced scheduling of jagged
- * batches).  Fixed-length calls and larger batches need none.  A call given
- * less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before launching
- * anything.  The workspace is caller-owned and only used on the call's
- * stream; calls that share one must be ordered on one stream. */
+ * mirror the shape arguments of the matching entry point.
+ * Forward: jagged calls of 1..4096 sequences need 4 bytes per sequence plus
+ * 32, rounded up to 256: the call first builds there, on the device, the
+ * order in which sequences are processed (longest first) and the counters of
+ * the work queues its kernels draw items from (see the README's load-balanced
+ * scheduling of jagged batches).  Fixed-length calls and larger batches need
+ * none.
+ * Backward: the sequence order (jagged calls of up to 4096 sequences), 17
+ * words of work-queue state and a failed-wait flag, one int32 turn counter
+ * per (64-row query tile, query head) of the ordered dQ reduction, and, when
+ * grad_dtype is 16-bit, an fp32 dQ accumulator of total_q * num_heads_q *
+ * head_dim values; each part rounded up to 256 bytes.
+ * A call given less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before
+ * launching anything.  The workspace is caller-owned and only used on the
+ * call's stream; calls that share one must be ordered on one stream. */
 size_t gdpa_fwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
 size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
 size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
-                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               int32_t grad_dtype);
 size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim);
+                                      int64_t total_q, int32_t num_heads_q, int32_t num_heads_kv,
+                                      int32_t head_dim, int32_t grad_dtype);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* gdpa_status_string(gdpa_status_t status);

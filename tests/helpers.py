@@ -129,3 +129,98 @@ def sample_rows(cu, heads, n, seed):
     while len(rows) < n and total > 0:
         rows.append((int(rng.integers(total)), int(rng.integers(heads))))
     return rows
+
+
+# ------------------------------------------------------------------ kinks
+# ReLU, LeakyReLU and HardSwish have derivatives that jump at kinks (0, and
+# +-3 for HardSwish).  A score S = scale * q.k computed in fp32 by any
+# implementation may land on the other side of a kink from the fp64 value
+# when it lies within the fp32 accumulation error of that kink; both one-sided
+# derivatives are then correct results of the method in the precision it is
+# computed in.  The backward comparisons therefore allow, for each output
+# element, the sum over such pairs of |jump| * |dP| times the other operand
+# (|K| for dQ, |Q| for dK); dV depends on the activation itself, which is
+# continuous, and gets no allowance.  The error bound of a length-D fp32 dot
+# product of exactly representable products is gamma_D * sum_d |q_d k_d| with
+# gamma_D = D u / (1 - D u), u = 2^-24 (Higham, Accuracy and Stability of
+# Numerical Algorithms, 2nd ed., section 3.1); it is doubled here, plus two
+# roundings of |S|, for the scaling and the activation's argument.
+U32 = 2.0 ** -24
+
+
+def kink_jumps(act, alpha):
+    """(kink, |act'(kink+) - act'(kink-)|) of the activations whose
+    derivative is discontinuous."""
+    if act == "relu":
+        return [(0.0, 1.0)]
+    if act == "leaky_relu":
+        return [(0.0, abs(1.0 - alpha))]
+    if act == "hardswish":
+        return [(-3.0, 0.5), (3.0, 0.5)]
+    return []
+
+
+def kink_allowance(bt, q, k, v, do):
+    """Per-element extra absolute error (dq, dk) allowed for pairs whose score
+    lies within fp32 rounding of a derivative kink (zeros for smooth
+    activations).  q, k, v, do: fp64 [tokens, heads, D] as the oracle sees them."""
+    wl = bt.wl
+    aq, ak = np.zeros(q.shape), np.zeros(k.shape)
+    jumps = kink_jumps(wl.act, wl.act_param)
+    if not jumps:
+        return aq, ak
+    D = q.shape[2]
+    gamma = D * U32 / (1.0 - D * U32)
+    group = wl.heads_q // wl.heads_kv
+    cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
+    for b in range(len(cq) - 1):
+        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        lq, lk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        if lq == 0 or lk == 0:
+            continue
+        allowed = oracle.allowed_mask(lq, lk, wl.mask, wl.window_left, wl.window_right)
+        for h in range(wl.heads_q):
+            g = h // group
+            Q, K, V, dO = q[sq, h], k[sk, g], v[sk, g], do[sq, h]
+            s = wl.scale * (Q @ K.T)
+            bound = 2.0 * wl.scale * gamma * (np.abs(Q) @ np.abs(K).T) + 2.0 * U32 * np.abs(s) + 1e-30
+            near = np.zeros_like(s)
+            for kink, jump in jumps:
+                near += np.where(np.abs(s - kink) <= bound, jump, 0.0)
+            w = np.where(allowed, near * np.abs(dO @ V.T), 0.0)   # |jump * dP| per ambiguous pair
+            if not w.any():
+                continue
+            aq[sq, h] += wl.scale * (w @ np.abs(K))
+            ak[sk, g] += wl.scale * (w.T @ np.abs(Q))
+    return aq, ak
+
+
+def err_ratio_allow(got, ref, allow):
+    """err_ratio with `allow` (absolute, per element) subtracted from each
+    element's error first."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.maximum(np.abs(got - ref) - allow, 0.0)))
+    if rms == 0.0:
+        return 0.0 if err == 0.0 else float("inf")
+    return err / rms
+
+
+def backward_ratios(bt, dq, dk, dv, refs=None):
+    """max|err| / rms(ref) of dQ, dK, dV against the oracle, with the kink
+    allowance above (dV none)."""
+    q, k, v, do = oracle_inputs(bt)
+    wl = bt.wl
+    if refs is None:
+        refs = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **mask_kw(wl))
+    aq, ak = kink_allowance(bt, q, k, v, do)
+    rq, rk, rv = refs
+    as_np = lambda t: t if isinstance(t, np.ndarray) else t.float().cpu().double().numpy()
+    return dict(dq=err_ratio_allow(as_np(dq).reshape(rq.shape), rq, aq),
+                dk=err_ratio_allow(as_np(dk).reshape(rk.shape), rk, ak),
+                dv=err_ratio(as_np(dv).reshape(rv.shape), rv))

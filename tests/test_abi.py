@@ -56,7 +56,8 @@ def test_abi_version_and_status_strings(lib):
     ver = int(re.search(r"#define GDPA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert lib.gdpa_abi_version() == ver
     for code, name in [(0, b"GDPA_OK"), (1, b"GDPA_ERR_INVALID_ARG"), (2, b"GDPA_ERR_UNSUPPORTED"),
-                       (3, b"GDPA_ERR_WORKSPACE_TOO_SMALL"), (4, b"GDPA_ERR_HIP"), (99, b"GDPA_ERR_UNKNOWN")]:
+                       (3, b"GDPA_ERR_WORKSPACE_TOO_SMALL"), (4, b"GDPA_ERR_HIP"), (5, b"GDPA_ERR_DEVICE_WAIT"),
+                       (99, b"GDPA_ERR_UNKNOWN")]:
         assert lib.gdpa_status_string(code) == name
 
 
@@ -174,37 +175,50 @@ def test_varlen_bwd_validation(lib, over, expect):
 
 
 def test_workspace_queries(lib):
-    for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
-              "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
-        assert getattr(lib, n)(64, 1024, 1024, 4, 4, 128) >= 0
-    # fixed-length calls need none; jagged calls of up to 4096 sequences hold
-    # the longest-first order (one int32 per sequence) and 8 work-queue
-    # counters, rounded up to 256 bytes
+    # forward: fixed-length calls need none; jagged calls of up to 4096
+    # sequences hold the longest-first order (one int32 per sequence) and 8
+    # work-queue counters, rounded up to 256 bytes
     assert lib.gdpa_fwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
-    assert lib.gdpa_bwd_workspace_size(64, 1024, 1024, 4, 4, 128) == 0
-    for n in ("gdpa_varlen_fwd_workspace_size", "gdpa_varlen_bwd_workspace_size"):
-        f = getattr(lib, n)
-        assert f(56, 1024, 1024, 4, 4, 128) == 256
-        assert f(57, 1024, 1024, 4, 4, 128) == 512
-        assert f(4096, 1024, 1024, 4, 4, 128) == 16640
-        assert f(4097, 1024, 1024, 4, 4, 128) == 0
-        assert f(0, 1024, 1024, 4, 4, 128) == 0
+    f = lib.gdpa_varlen_fwd_workspace_size
+    assert f(56, 1024, 1024, 4, 4, 128) == 256
+    assert f(57, 1024, 1024, 4, 4, 128) == 512
+    assert f(4096, 1024, 1024, 4, 4, 128) == 16640
+    assert f(4097, 1024, 1024, 4, 4, 128) == 0
+    assert f(0, 1024, 1024, 4, 4, 128) == 0
 
 
-@pytest.mark.parametrize("call", ["fixed", "jagged", "jagged_with_workspace"])
-def test_fp8_at_head_dims_192_128_is_unsupported_before_any_launch(lib, call):
-    # FP8 Q/K are built at head dims 64, 96 and 128 only; (192, 128) must be
-    # refused on the host, before the schedule kernel of a jagged call is queued
-    # (FAKE pointers: any HIP call on them would fail with GDPA_ERR_HIP instead)
-    kw = dict(D=192, Dv=128, qk=2, vd=0)
-    if call == "fixed":
-        assert fwd(lib, **kw) == UNSUPPORTED
-    elif call == "jagged":
-        assert varlen_fwd(lib, **kw) == UNSUPPORTED
-    else:
-        nws = lib.gdpa_varlen_fwd_workspace_size(2, 128, 128, 4, 4, 192)
-        assert nws > 0
-        assert varlen_fwd(lib, ws=FAKE, nws=nws, **kw) == UNSUPPORTED
+FP32, BF16, FP16 = 3, 0, 1
+
+
+def test_backward_workspace_layout(lib):
+    # fixed length: queue state (256 B) + one turn counter per (64-row query
+    # tile, head): 64 sequences x 16 tiles x 4 heads x 4 B = 16 KiB
+    fx = lib.gdpa_bwd_workspace_size
+    assert fx(64, 1024, 1024, 4, 4, 128, FP32) == 256 + 16384
+    assert fx(64, 1000, 1024, 4, 4, 128, FP32) == 256 + 16384       # 16 tiles of 64 rows
+    # 16-bit dQ adds an fp32 accumulator of total_q x Hq x D values
+    assert fx(64, 1024, 1024, 4, 4, 128, BF16) == 256 + 16384 + 64 * 1024 * 4 * 128 * 4
+    assert fx(64, 1024, 1024, 4, 4, 128, FP16) == fx(64, 1024, 1024, 4, 4, 128, BF16)
+    assert fx(0, 1024, 1024, 4, 4, 128, FP32) == 0
+    # jagged: sequence order (batch int32) + queue state + (total_q / 64 +
+    # batch + 1) tiles per head, each part rounded up to 256 bytes
+    vb = lib.gdpa_varlen_bwd_workspace_size
+    turns = (34868 // 64 + 64 + 1) * 4 * 4
+    assert vb(64, 1024, 1024, 34868, 4, 4, 128, FP32) == 256 + 256 + (turns + 255) // 256 * 256
+    assert (vb(64, 1024, 1024, 34868, 4, 4, 128, BF16) - vb(64, 1024, 1024, 34868, 4, 4, 128, FP32)
+            == (34868 * 4 * 128 * 4 + 255) // 256 * 256)
+    # beyond 4096 sequences no order is kept
+    assert vb(5000, 8, 8, 5000, 1, 1, 64, FP32) == 256 + ((5000 // 64 + 5001) * 4 + 255) // 256 * 256
+    for n in (vb(64, 1024, 1024, 34868, 4, 4, 128, FP32), fx(3, 77, 77, 2, 1, 96, FP32)):
+        assert n % 256 == 0
+
+
+def test_backward_needs_its_workspace(lib):
+    # every backward call with work to do needs the queried workspace
+    assert bwd(lib) == WS_SMALL
+    nws = lib.gdpa_bwd_workspace_size(2, 128, 128, 4, 2, 128, FP32)
+    assert bwd(lib, ws=FAKE, nws=nws - 1) == WS_SMALL
+    assert bwd(lib, B=0) == OK
 
 
 def test_jagged_calls_check_the_workspace_before_launching(lib):

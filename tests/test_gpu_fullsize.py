@@ -175,3 +175,54 @@ def test_tensors_beyond_2gib(g):
     print(f"[fullsize] beyond 2 GiB: err/rms {errs}", flush=True)
     assert errs["o"] <= TOL_FWD_BF16
     assert max(errs["dq"], errs["dk"], errs["dv"]) <= TOL_BWD
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+@pytest.mark.parametrize("name", ["jagged_self", "full_self"])
+def test_full_size_backward_is_bitwise_repeatable(g, monkeypatch, name, mode):
+    """Three backward calls at full size give bitwise the same dQ, dK and dV,
+    with dQ from the dK/dV pass (per-XCD work queues, the ordered dQ
+    reduction) and from the separate dQ kernel (the dK/dV work queue)."""
+    import torch
+    monkeypatch.setenv("GDPA_BWD_DQ", mode)
+    wl = gi.WORKLOADS[name]
+    print(f"[fullsize] {name}: drawing inputs (repeatability)", flush=True)
+    bt = gi.make_batch(wl)
+    dev = device_batch(bt)
+    first = run_backward(g, bt, dev)
+    for rep in range(2):
+        again = run_backward(g, bt, dev)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b), f"{name} ({mode}): backward run {rep + 2} differs"
+        del again
+    print(f"[fullsize] {name} ({mode}): backward repeatable", flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_full_self_whole_slice(g):
+    """Full-length workload (32 x 2048, 8 heads): every element of one whole
+    (sequence, head) slice of O, dQ, dK and dV against the fp64 oracle."""
+    import torch
+    wl = gi.WORKLOADS["full_self"]
+    print("[fullsize] full_self: drawing inputs (whole slice)", flush=True)
+    bt = gi.make_batch(wl)
+    dev = device_batch(bt)
+    o = run_forward(g, bt, dev)
+    dq, dk, dv = run_backward(g, bt, dev)
+    torch.cuda.synchronize()
+    b, h = 21, 5
+    q, k, v, do = _seq(bt, b)
+    L = q.shape[0]
+    sl = slice(int(bt.cu_seqlens_q[b]), int(bt.cu_seqlens_q[b + 1]))
+    qh, kh, vh, doh = q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], do[:, h:h + 1]
+    ref_o = oracle.gdpa_forward(qh, kh, vh, [0, L], [0, L], wl.scale, wl.act, **_kw(wl))
+    rq, rk, rv = oracle.gdpa_backward(qh, kh, vh, doh, [0, L], [0, L], wl.scale, wl.act, **_kw(wl))
+    errs = dict(o=err_ratio(o[sl, h:h + 1].double().cpu().numpy(), ref_o),
+                dq=err_ratio(dq[sl, h:h + 1].double().cpu().numpy(), rq),
+                dk=err_ratio(dk[sl, h:h + 1].double().cpu().numpy(), rk),
+                dv=err_ratio(dv[sl, h:h + 1].double().cpu().numpy(), rv))
+    print(f"[fullsize] full_self slice (b={b}, h={h}): err/rms {errs}", flush=True)
+    assert errs["o"] <= TOL_FWD_BF16
+    assert max(errs["dq"], errs["dk"], errs["dv"]) <= TOL_BWD

@@ -12,8 +12,8 @@ import pytest
 
 import gdpa_inputs as gi
 import oracle
-from helpers import (TOL_BWD, TOL_FWD_BF16, TOL_FWD_FP8, device_batch, err_ratio, mask_kw, oracle_inputs,
-                     run_backward, run_forward)
+from helpers import (TOL_BWD, TOL_FWD_BF16, TOL_FWD_FP8, backward_ratios, device_batch, err_ratio, mask_kw,
+                     oracle_inputs, run_backward, run_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,7 @@ def check_forward(g, bt, tol=None):
 def check_backward(g, bt, tol=TOL_BWD):
     wl = bt.wl
     dq, dk, dv = [t.cpu().double().numpy() for t in run_backward(g, bt)]
-    q, k, v, do = oracle_inputs(bt)
-    rq, rk, rv = oracle.gdpa_backward(q, k, v, do, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act,
-                                      **mask_kw(wl))
-    errs = dict(dq=err_ratio(dq, rq), dk=err_ratio(dk, rk), dv=err_ratio(dv, rv))
+    errs = backward_ratios(bt, dq, dk, dv)
     assert max(errs.values()) <= tol, f"{wl} backward {errs}"
     return errs
 
@@ -241,8 +238,14 @@ def test_fixed_length_equals_varlen(g):
         assert torch.equal(a, b)
 
 
-def test_partial_gradients(g):
+@pytest.mark.parametrize("mode", ["fused", "separate"])
+def test_partial_gradients(g, monkeypatch, mode):
+    # dq alone (separate dQ kernel) and dk/dv alone (dK/dV kernel) against the
+    # full call (fused: dQ reduced in another fixed order inside the dK/dV
+    # pass): dK and dV take the same products in the same order, bitwise; dQ
+    # matches the oracle
     import torch
+    monkeypatch.setenv("GDPA_BWD_DQ", mode)
     bt = gi.make_batch(_wl(act="silu", mask="causal"), seqlens_q=[200, 70], seqlens_k=[200, 70])
     dev = device_batch(bt)
     dq, dk, dv = run_backward(g, bt, dev)
@@ -253,7 +256,123 @@ def test_partial_gradients(g):
     g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], dq2, None, None, *common, **kw)
     dk2, dv2 = torch.full_like(dk, float("nan")), torch.full_like(dv, float("nan"))
     g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, dk2, dv2, *common, **kw)
-    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    for t in (dq, dq2):
+        assert backward_ratios(bt, t, dk, dv)["dq"] <= TOL_BWD
+
+
+# -------------------------------------------- fused backward (ordered dQ sums)
+FUSED_CASES = [
+    dict(act="silu"),
+    dict(act="gelu_tanh", mask="causal"),
+    dict(act="relu2", mask="window", window_left=130, window_right=70),
+    dict(act="leaky_relu", heads_q=8, heads_kv=2),                 # GQA 4:1: a step loop over the group's heads
+    dict(act="hardswish", heads_q=4, heads_kv=1, mask="causal"),   # MQA
+    dict(act="gelu"),
+]
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_fused_and_separate_dq_match_the_oracle(g, monkeypatch, case, D):
+    # long sequences (several key blocks per tile, up to 12 contributors per
+    # dQ tile), ragged tails, an empty sequence; dK/dV bitwise equal between
+    # the two paths, dQ within the bar for both
+    import torch
+    lens = [700, 1, 0, 1537, 64, 129]
+    bt = gi.make_batch(_wl(head_dim=D, batch=len(lens), act_param=0.05, **FUSED_CASES[case]), seqlens_q=lens,
+                       seqlens_k=lens)
+    dev = device_batch(bt)
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    fused = run_backward(g, bt, dev)
+    monkeypatch.setenv("GDPA_BWD_DQ", "separate")
+    sep = run_backward(g, bt, dev)
+    assert torch.equal(fused[1], sep[1]) and torch.equal(fused[2], sep[2])
+    errs = backward_ratios(bt, *fused)
+    assert max(errs.values()) <= TOL_BWD, errs
+    assert backward_ratios(bt, *sep)["dq"] <= TOL_BWD
+
+
+SHORT_KV_CASES = [
+    dict(act="relu2"),                                          # dS split into hi + lo words (few keys)
+    dict(act="gelu_tanh", mask="causal"),
+    dict(act="silu", heads_q=8, heads_kv=2),                    # GQA 4:1
+    dict(act="relu2", heads_q=2, heads_kv=1, fp16=True),        # fp16: one word
+]
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("case", range(len(SHORT_KV_CASES)))
+def test_short_kv_fused_and_separate_match_the_oracle(g, monkeypatch, case, D):
+    # keys fit one block (the fused pass is the default): each query tile has
+    # one contributor, so dQ is written directly; empty and one-key sequences,
+    # ragged query tails; dK/dV bitwise equal between the paths
+    import torch
+    lq, lk = [700, 1, 0, 300, 64, 129, 5], [64, 64, 64, 1, 0, 33, 128]
+    bt = gi.make_batch(_wl(head_dim=D, batch=len(lq), **SHORT_KV_CASES[case]), seqlens_q=lq, seqlens_k=lk)
+    dev = device_batch(bt)
+    default = run_backward(g, bt, dev)
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    fused = run_backward(g, bt, dev)
+    monkeypatch.setenv("GDPA_BWD_DQ", "separate")
+    sep = run_backward(g, bt, dev)
+    for a, b in zip(default, fused):
+        assert torch.equal(a, b)
+    assert torch.equal(fused[1], sep[1]) and torch.equal(fused[2], sep[2])
+    errs = backward_ratios(bt, *fused)
+    assert max(errs.values()) <= TOL_BWD, errs
+    assert backward_ratios(bt, *sep)["dq"] <= TOL_BWD
+
+
+def test_fused_cross_attention_lengths(g, monkeypatch):
+    # Lq != Lk in both directions, causal (bottom-right) and a window: query
+    # tiles no key block reaches are written as zeros by the first block item
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    lq, lk = [300, 40, 900, 129], [100, 600, 900, 1000]
+    for mask, wl_, wr_ in (("causal", -1, -1), ("window", 200, 10), ("none", -1, -1)):
+        bt = gi.make_batch(_wl(head_dim=128, batch=4, act="silu", mask=mask, window_left=wl_, window_right=wr_),
+                           seqlens_q=lq, seqlens_k=lk)
+        check_backward(g, bt)
+
+
+def test_fused_backward_16bit_gradients(g, monkeypatch):
+    # bf16 and fp16 dQ: fp32 sums in the workspace, the last contributor
+    # rounds; compared with fp32 dQ of the same call at the output's precision
+    import torch
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    lens = [700, 1537, 64]
+    for fp16 in (False, True):
+        bt = gi.make_batch(_wl(head_dim=128, batch=3, act="gelu_tanh", mask="causal", fp16=fp16), seqlens_q=lens,
+                           seqlens_k=lens)
+        dev = device_batch(bt)
+        ref = run_backward(g, bt, dev)
+        got = run_backward(g, bt, dev, grad_dtype=torch.float16 if fp16 else torch.bfloat16)
+        for a, b in zip(got, ref):
+            assert torch.isfinite(a).all()
+            err = (a.float() - b).abs().max().item()
+            assert err <= 2 ** -7 * b.abs().max().item(), err
+
+
+def test_fused_wait_flag_in_debug_mode(g, monkeypatch):
+    # GDPA_DEBUG_CHECKS makes the call wait for the kernel and report a dQ turn
+    # wait that gave up; the default limit never trips, and a negative limit
+    # (forced from the host) gives up every wait at once, so the error path is
+    # taken while every kernel still runs to its end
+    lens = [1537, 700]
+    bt = gi.make_batch(_wl(head_dim=128, batch=2, act="silu"), seqlens_q=lens, seqlens_k=lens)
+    dev = device_batch(bt)
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    monkeypatch.setenv("GDPA_DEBUG_CHECKS", "1")
+    check = run_backward(g, bt, dev)
+    monkeypatch.setenv("GDPA_DEBUG_SPIN_LIMIT", "-1")
+    with pytest.raises(g.GDPAError) as e:
+        run_backward(g, bt, dev)
+    assert e.value.status == 5
+    monkeypatch.delenv("GDPA_DEBUG_SPIN_LIMIT")
+    import torch
+    again = run_backward(g, bt, dev)
+    for a, b in zip(check, again):
+        assert torch.equal(a, b)
 
 
 # ------------------------------------------------------- longest-first schedule
