@@ -188,6 +188,23 @@ size_t schedule_bytes(int64_t batch) {
 //                                tiles = total_q / 64 + batch + 1 (jagged) or
 //                                batch * ceil(seqlen_q / 64)
 //   acc    fp32 [total_q, hq, d] dQ accumulator, when dQ is stored in 16 bits
+// How a backward call produces dQ: GDPA_BWD_DQ=fused|separate (read at every
+// call, also by the workspace queries) overrides the default choice.
+enum DqMode { DQ_AUTO, DQ_FUSED, DQ_SEPARATE };
+DqMode dq_mode() {
+  const char* m = std::getenv("GDPA_BWD_DQ");
+  if (m == nullptr) return DQ_AUTO;
+  if (std::strcmp(m, "fused") == 0) return DQ_FUSED;
+  if (std::strcmp(m, "separate") == 0) return DQ_SEPARATE;
+  return DQ_AUTO;
+}
+// A 16-bit dQ needs the fp32 accumulator only when the fused pass reduces
+// partial sums of several key blocks; by default that pass runs only when
+// every sequence's keys fit one block (dQ then written directly).
+bool bwd_acc16(bool grads16, int64_t max_lk) {
+  return grads16 && max_lk > gdpa::kBwdBN && dq_mode() == DQ_FUSED;
+}
+
 struct BwdLayout {
   size_t order, queues, turns, acc, bytes;
   int64_t nturn;  // turn counters
@@ -383,7 +400,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
       gdpa::pair_grid(c.batch, c.hkv, nblocks) > kMaxGrid)
     return GDPA_ERR_UNSUPPORTED;
   const bool jagged = cu_q != nullptr;
-  const BwdLayout lay = bwd_layout(c.batch, jagged, c.max_lq, c.total_q, c.hq, c.d, out_kind != gdpa::OUT_F32);
+  const BwdLayout lay =
+      bwd_layout(c.batch, jagged, c.max_lq, c.total_q, c.hq, c.d, bwd_acc16(out_kind != gdpa::OUT_F32, c.max_lk));
   if (workspace == nullptr || workspace_bytes < lay.bytes) return GDPA_ERR_WORKSPACE_TOO_SMALL;
 
   BwdArgs a{};
@@ -426,9 +444,9 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   // every sequence's keys fit one block; GDPA_BWD_DQ=fused|separate overrides.
   // The fused pass also needs all three gradients, at most one of the two
   // word splits and a sequence's fp32 dQ rows within 32-bit offsets.
-  const char* mode = std::getenv("GDPA_BWD_DQ");
-  const bool force_fused = mode != nullptr && std::strcmp(mode, "fused") == 0;
-  const bool force_separate = mode != nullptr && std::strcmp(mode, "separate") == 0;
+  const DqMode mode = dq_mode();
+  const bool force_fused = mode == DQ_FUSED;
+  const bool force_separate = mode == DQ_SEPARATE;
   const bool fused = want_dq && want_dkv && !(a.dsplit && a.kvsplit) && a.ncu > 0 && !force_separate &&
                      (force_fused || c.max_lk <= gdpa::kBwdBN) &&
                      ((int64_t)c.max_lq + gdpa::kDqTile) * c.hq * c.d * 4 <= INT32_MAX;
@@ -537,17 +555,19 @@ size_t gdpa_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int3
 size_t gdpa_varlen_fwd_workspace_size(int32_t batch, int32_t, int32_t, int32_t, int32_t, int32_t) {
   return schedule_bytes(batch);
 }
-size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t, int32_t num_heads_q, int32_t,
+size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q, int32_t,
                                int32_t head_dim, int32_t grad_dtype) {
   if (batch <= 0 || seqlen_q < 0 || num_heads_q <= 0 || head_dim <= 0) return 0;
   return bwd_layout(batch, false, seqlen_q, (int64_t)batch * seqlen_q, num_heads_q, head_dim,
-                    grad_dtype != GDPA_DTYPE_FP32)
+                    bwd_acc16(grad_dtype != GDPA_DTYPE_FP32, seqlen_k))
       .bytes;
 }
-size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t, int64_t total_q,
+size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
                                       int32_t num_heads_q, int32_t, int32_t head_dim, int32_t grad_dtype) {
   if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || num_heads_q <= 0 || head_dim <= 0) return 0;
-  return bwd_layout(batch, true, max_seqlen_q, total_q, num_heads_q, head_dim, grad_dtype != GDPA_DTYPE_FP32).bytes;
+  return bwd_layout(batch, true, max_seqlen_q, total_q, num_heads_q, head_dim,
+                    bwd_acc16(grad_dtype != GDPA_DTYPE_FP32, max_seqlen_k))
+      .bytes;
 }
 
 const char* gdpa_status_string(gdpa_status_t s) {

@@ -202,8 +202,10 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
  * Backward: the sequence order (jagged calls of up to 4096 sequences), 17
  * words of work-queue state and a failed-wait flag, one int32 turn counter
  * per (64-row query tile, query head) of the ordered dQ reduction, and, when
- * grad_dtype is 16-bit, an fp32 dQ accumulator of total_q * num_heads_q *
- * head_dim values; each part rounded up to 256 bytes.
+ * grad_dtype is 16-bit and dQ is reduced over several key blocks inside the
+ * dK/dV pass (max seqlen_k > 128 with GDPA_BWD_DQ=fused set), an fp32 dQ
+ * accumulator of total_q * num_heads_q * head_dim values; each part rounded
+ * up to 256 bytes.  The queries read GDPA_BWD_DQ as the calls do.
  * A call given less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before
  * launching anything.  The workspace is caller-owned and only used on the
  * call's stream; calls that share one must be ordered on one stream. */

@@ -196,21 +196,36 @@ def test_backward_workspace_layout(lib):
     fx = lib.gdpa_bwd_workspace_size
     assert fx(64, 1024, 1024, 4, 4, 128, FP32) == 256 + 16384
     assert fx(64, 1000, 1024, 4, 4, 128, FP32) == 256 + 16384       # 16 tiles of 64 rows
-    # 16-bit dQ adds an fp32 accumulator of total_q x Hq x D values
-    assert fx(64, 1024, 1024, 4, 4, 128, BF16) == 256 + 16384 + 64 * 1024 * 4 * 128 * 4
-    assert fx(64, 1024, 1024, 4, 4, 128, FP16) == fx(64, 1024, 1024, 4, 4, 128, BF16)
+    # 16-bit dQ adds an fp32 accumulator of total_q x Hq x D values only when
+    # the dK/dV pass reduces several key blocks' partial sums (forced with
+    # GDPA_BWD_DQ=fused; by default several key blocks take the separate dQ
+    # kernel, and one key block writes dQ directly)
+    assert fx(64, 1024, 1024, 4, 4, 128, BF16) == 256 + 16384
     assert fx(0, 1024, 1024, 4, 4, 128, FP32) == 0
     # jagged: sequence order (batch int32) + queue state + (total_q / 64 +
     # batch + 1) tiles per head, each part rounded up to 256 bytes
     vb = lib.gdpa_varlen_bwd_workspace_size
     turns = (34868 // 64 + 64 + 1) * 4 * 4
     assert vb(64, 1024, 1024, 34868, 4, 4, 128, FP32) == 256 + 256 + (turns + 255) // 256 * 256
-    assert (vb(64, 1024, 1024, 34868, 4, 4, 128, BF16) - vb(64, 1024, 1024, 34868, 4, 4, 128, FP32)
-            == (34868 * 4 * 128 * 4 + 255) // 256 * 256)
+    assert vb(64, 1024, 1024, 34868, 4, 4, 128, BF16) == vb(64, 1024, 1024, 34868, 4, 4, 128, FP32)
     # beyond 4096 sequences no order is kept
     assert vb(5000, 8, 8, 5000, 1, 1, 64, FP32) == 256 + ((5000 // 64 + 5001) * 4 + 255) // 256 * 256
     for n in (vb(64, 1024, 1024, 34868, 4, 4, 128, FP32), fx(3, 77, 77, 2, 1, 96, FP32)):
         assert n % 256 == 0
+
+
+def test_backward_accumulator_follows_the_dq_mode(lib, monkeypatch):
+    fx, vb = lib.gdpa_bwd_workspace_size, lib.gdpa_varlen_bwd_workspace_size
+    base = fx(64, 1024, 1024, 4, 4, 128, FP32)
+    monkeypatch.setenv("GDPA_BWD_DQ", "fused")
+    assert fx(64, 1024, 1024, 4, 4, 128, BF16) == base + 64 * 1024 * 4 * 128 * 4
+    assert fx(64, 1024, 1024, 4, 4, 128, FP16) == fx(64, 1024, 1024, 4, 4, 128, BF16)
+    assert fx(64, 1024, 1024, 4, 4, 128, FP32) == base
+    assert fx(64, 1024, 128, 4, 4, 128, BF16) == base        # one key block: no partial sums to keep
+    assert (vb(64, 1024, 1024, 34868, 4, 4, 128, BF16) - vb(64, 1024, 1024, 34868, 4, 4, 128, FP32)
+            == (34868 * 4 * 128 * 4 + 255) // 256 * 256)
+    monkeypatch.setenv("GDPA_BWD_DQ", "separate")
+    assert fx(64, 1024, 1024, 4, 4, 128, BF16) == base
 
 
 def test_backward_needs_its_workspace(lib):
