@@ -34,7 +34,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_UNSUPPORTED",
           3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP", 5: "GDPA_ERR_DEVICE_WAIT"}
 
 EXPORTED = (
-    "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd",
+    "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd", "gdpa_varlen_bwd_noalloc",
     "gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
     "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size",
     "gdpa_status_string", "gdpa_abi_version",
@@ -61,6 +61,8 @@ def _load():
                              I32, I32, P, SZ, P]
     lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, F32,
                                     I32, I32, I32, I32, F32, I32, I32, P, SZ, P]
+    lib.gdpa_varlen_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32,
+                                            F32, I32, I32, I32, I32, F32, I32, I32, P]
     for n in ("gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd"):
         getattr(lib, n).restype = ctypes.c_int
     for n in ("gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size"):
@@ -269,6 +271,23 @@ def gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_s
                               window_right, _act(act), float(act_param), _qk_dtype(q), gd, _ptr(ws),
                               nws, _stream(q.device))
     _check(st, "gdpa_varlen_bwd")
+    return dq, dk, dv
+
+
+def gdpa_varlen_bwd_noalloc(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                            scale, act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1):
+    """Jagged backward that allocates nothing (the library's per-GPU scratch
+    array replaces the workspace); same results as gdpa_varlen_bwd."""
+    _check_bwd_args(q, k, v, dout, dq, dk, dv, jagged=True)
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
+    B = cu_seqlens_q.numel() - 1
+    Hq, D = q.shape[1], q.shape[2]
+    st = _lib.gdpa_varlen_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q),
+                                      int(max_seqlen_k), q.shape[0], k.shape[0], Hq, k.shape[1], D, v.shape[-1],
+                                      float(scale), _mask(mask), window_left, window_right, _act(act),
+                                      float(act_param), _qk_dtype(q), _grad_dtype(dq, dk, dv), _stream(q.device))
+    _check(st, "gdpa_varlen_bwd_noalloc")
     return dq, dk, dv
 
 

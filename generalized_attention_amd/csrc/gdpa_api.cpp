@@ -485,6 +485,36 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
 
 }  // namespace
 
+// ------------------------------------------------ allocation-free backward
+// The backward's workspace for callers that cannot allocate device memory:
+// one copy of this array per GPU, alive until the process ends.  Host code
+// uses only the address looked up per device (the array's name on the host
+// is a stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[GDPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch array (looked up once per device,
+// with that device current).
+gdpa_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return GDPA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "scratch address");
+    if (p == nullptr) return GDPA_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return GDPA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o, int32_t batch, int32_t seqlen_q,
@@ -549,6 +579,31 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
   if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
   return run_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, in_dtype, grad_dtype,
                  workspace, workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                      void* dk, void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
+                                      int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                      int32_t head_dim_v, float scale, int32_t mask, int32_t window_left,
+                                      int32_t window_right, int32_t act, float act_param, int32_t in_dtype,
+                                      int32_t grad_dtype, void* stream) {
+  Common c;
+  gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                  head_dim, head_dim_v, scale, mask, window_left, window_right, act, act_param, &c);
+  if (st != GDPA_OK) return st;
+  const size_t need = gdpa_varlen_bwd_workspace_size(batch, max_seqlen_q, max_seqlen_k, total_q, num_heads_q,
+                                                     num_heads_kv, head_dim, grad_dtype);
+  if (need > GDPA_NOALLOC_SCRATCH_BYTES) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != GDPA_OK) return st;
+  }
+  return gdpa_varlen_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                         total_q, total_k, num_heads_q, num_heads_kv, head_dim, head_dim_v, scale, mask, window_left,
+                         window_right, act, act_param, in_dtype, grad_dtype, ws,
+                         need > 0 ? (size_t)GDPA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t gdpa_fwd_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }

@@ -191,6 +191,31 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
                               int32_t in_dtype, int32_t grad_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free jagged backward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as gdpa_varlen_bwd, without
+ * the workspace: the call uses a scratch array of
+ * GDPA_NOALLOC_SCRATCH_BYTES that the library keeps in every GPU's memory
+ * for the life of the process, and allocates nothing.  A call whose
+ * workspace query (gdpa_varlen_bwd_workspace_size) exceeds that size returns
+ * GDPA_ERR_WORKSPACE_TOO_SMALL before launching anything (an fp32 gradient
+ * never needs more than the sequence order, the queue state and one turn
+ * counter per (64-row query tile, query head)).  All calls on one GPU share
+ * its array and every call clears on the device what it needs cleared:
+ * calls that can overlap on one GPU (different streams, or threads without
+ * ordering) race and must be ordered by the caller. */
+#define GDPA_NOALLOC_SCRATCH_BYTES (8u << 20)
+gdpa_status_t gdpa_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const void* dout,
+                                      void* dq, void* dk, void* dv,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int64_t total_q, int64_t total_k,
+                                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                      int32_t head_dim_v,
+                                      float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                      int32_t act, float act_param,
+                                      int32_t in_dtype, int32_t grad_dtype, void* stream);
+
 /* Workspace each call needs, in bytes (0 = none; pass NULL then).  Arguments
  * mirror the shape arguments of the matching entry point.
  * Forward: jagged calls of 1..4096 sequences need 4 bytes per sequence plus
