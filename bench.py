@@ -11,7 +11,7 @@ Flops are algorithmic: only allowed (query, key) pairs count, 4*D per pair and
 query head for the forward (Q K^T and P V) and 10*D for the backward (the five
 products S, dP, dV, dK, dQ); activation math is not counted.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--cold]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--out-dtype fp32|bf16]
   python bench.py --calibrate-copy 1024     # plain 1 GiB device copy, for PMC scaling
 """
 from __future__ import annotations
@@ -67,18 +67,58 @@ TOL = {"o": 2e-2, "dq": 3e-2, "dk": 3e-2, "dv": 3e-2}
 TOL_FP8 = 6e-2
 
 
-def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None):
-    """Time the fp64 oracle (forward + backward) on leading sequences of the same
-    batch until about `budget_s` seconds of CPU work; report TFLOP/s on the
-    algorithmic flops of the sequences processed.
+def pool_size():
+    """Host cores for the oracle leg: this process's CPU affinity, capped at the
+    16-core share a one-GPU machine gives its GPU."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
 
-    With `gpu` (host copies of the outputs the timed kernels wrote: o, and dq,
-    dk, dv for a backward workload) it also returns max |gpu - oracle| /
-    rms(oracle) per output over the same sequences, outside the timed region."""
+
+# Decoded inputs of the batch under test, set before the worker processes are
+# forked (they inherit it and receive only (sequence, head) indices).
+_ORACLE_INPUTS = {}
+
+
+def _one_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def _oracle_task(task):
+    """Forward (and backward) of one (sequence b, query head h) in the fp64
+    oracle: per-sequence outputs, dK/dV as head h's share of its KV group."""
     import oracle
-    from threadpoolctl import threadpool_info
+    b, h = task
+    st = _ORACLE_INPUTS
+    wl = st["wl"]
+    cq, ck = st["cq"], st["ck"]
+    g = h // (wl.heads_q // wl.heads_kv)
+    sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+    lcq, lck = [0, cq[b + 1] - cq[b]], [0, ck[b + 1] - ck[b]]
+    kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
+    q, k, v = st["q"][sq, h:h + 1], st["k"][sk, g:g + 1], st["v"][sk, g:g + 1]
+    t0 = time.perf_counter()
+    out = {"o": oracle.gdpa_forward(q, k, v, lcq, lck, wl.scale, wl.act, **kw)}
+    t1 = time.perf_counter()
+    if st["with_bwd"]:
+        out["dq"], out["dk"], out["dv"] = oracle.gdpa_backward(q, k, v, st["do"][sq, h:h + 1], lcq, lck, wl.scale,
+                                                               wl.act, **kw)
+    return b, h, t1 - t0, time.perf_counter() - t1, out
+
+
+def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None, workers=None):
+    """Time the fp64 oracle (forward + backward) on the batch's leading
+    sequences, each (sequence, query head) a task in a pool of `workers`
+    single-threaded processes (default pool_size()), until about `budget_s`
+    seconds of wall time; report TFLOP/s on the algorithmic flops of the
+    sequences processed.
+
+    Returns (baseline record, oracle outputs of the sample).  parity_record()
+    compares them with the GPU's outputs."""
+    import multiprocessing
+    import oracle
     wl = bt.wl
-    pairs = workload_pairs(bt)
+    workers = workers or pool_size()
+    pairs = workload_pairs(bt) // max(wl.heads_q, 1)  # per sequence and head
     DV = wl.head_dim_v or wl.head_dim
     with_bwd = not wl.fp8_qk and DV == wl.head_dim and bt.do is not None
     dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
@@ -86,47 +126,70 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None):
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
     else:
         q, k = dec(bt.q), dec(bt.k)
-    v = dec(bt.v)
-    do = dec(bt.do) if with_bwd else None
+    _ORACLE_INPUTS.clear()
+    _ORACLE_INPUTS.update(wl=wl, q=q, k=k, v=dec(bt.v), do=dec(bt.do) if with_bwd else None,
+                          cq=bt.cu_seqlens_q, ck=bt.cu_seqlens_k, with_bwd=with_bwd)
+    per_pair = 14 * wl.head_dim if with_bwd else 2 * (wl.head_dim + DV)
+    wall, t_fwd, t_bwd, flops, nseq = 0.0, 0.0, 0.0, 0, 0
+    results = []
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers, initializer=_one_thread) as pool:
+        b = 0
+        while b < wl.batch and (wall < budget_s or nseq == 0):
+            # whole sequences, at least one task per worker
+            tasks = []
+            while b < wl.batch and len(tasks) < workers:
+                tasks += [(b, h) for h in range(wl.heads_q)]
+                flops += per_pair * int(pairs[b]) * wl.heads_q
+                b += 1
+                nseq += 1
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_task, tasks, chunksize=1)
+            wall += time.perf_counter() - t0
+            for _, _, tf, tb, _ in res:
+                t_fwd += tf
+                t_bwd += tb
+            results += res
+    _ORACLE_INPUTS.clear()
+    base = {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of the first {nseq} "
+                      f"of {wl.batch} sequences ({flops / 1e9:.1f} GFLOP algorithmic), one task per "
+                      f"(sequence, head) on {workers} single-threaded processes: {wall:.1f} s wall "
+                      f"(task time forward {t_fwd:.1f} s, backward {t_bwd:.1f} s)"}
+    return base, {"nseq": nseq, "results": results}
+
+
+def parity_record(bt: gi.Batch, sample, gpu):
+    """max |gpu - oracle| / rms(oracle) per output over the oracle leg's
+    sequences (all elements); gpu holds host copies of o (and dq, dk, dv)."""
+    wl = bt.wl
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
-    t_total, flops, nseq = 0.0, 0, 0
-    err = {}  # output -> [max |diff|, sum of ref^2, element count]
-    for b in range(wl.batch):
-        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
-        lcq, lck = [0, cq[b + 1] - cq[b]], [0, ck[b + 1] - ck[b]]
-        kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
-        t0 = time.perf_counter()
-        refs = {"o": oracle.gdpa_forward(q[sq], k[sk], v[sk], lcq, lck, wl.scale, wl.act, **kw)}
-        if with_bwd:
-            refs["dq"], refs["dk"], refs["dv"] = oracle.gdpa_backward(q[sq], k[sk], v[sk], do[sq], lcq, lck,
-                                                                     wl.scale, wl.act, **kw)
-        t_total += time.perf_counter() - t0
-        if gpu is not None:
-            for name, ref in refs.items():
-                got = gpu[name][sq if name in ("o", "dq") else sk]
-                e = err.setdefault(name, [0.0, 0.0, 0])
-                if ref.size:
-                    e[0] = max(e[0], float(np.abs(got.astype(np.float64) - ref).max()))
-                    e[1] += float((ref * ref).sum())
-                    e[2] += ref.size
-        flops += (14 * wl.head_dim if with_bwd else 2 * (wl.head_dim + DV)) * int(pairs[b])
-        nseq += 1
-        if t_total >= budget_s:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    sample = f"the first {nseq} of {wl.batch} sequences"
-    base = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of {sample} "
-                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {t_total:.1f} s"}
-    if gpu is None:
-        return base, None
+    group = wl.heads_q // wl.heads_kv
+    refs = {}
+    for b, h, _, _, out in sample["results"]:
+        for name, x in out.items():
+            if name in ("o", "dq"):
+                refs.setdefault(name, {})[(b, h)] = x[:, 0]
+            else:  # dK, dV: sum the group's query heads in head order
+                key = (b, h // group)
+                acc = refs.setdefault(name, {})
+                acc[key] = x[:, 0] if key not in acc else acc[key] + x[:, 0]
+    err_rms = {}
+    for name, parts in refs.items():
+        mx, ss, n = 0.0, 0.0, 0
+        for (b, j), ref in parts.items():
+            rows = slice(cq[b], cq[b + 1]) if name in ("o", "dq") else slice(ck[b], ck[b + 1])
+            got = gpu[name][rows, j].astype(np.float64)
+            if ref.size:
+                mx = max(mx, float(np.abs(got - ref).max()))
+                ss += float((ref * ref).sum())
+                n += ref.size
+        err_rms[name] = mx / np.sqrt(ss / n) if n and ss > 0 else 0.0
     tol = {n: (TOL_FP8 if wl.fp8_qk else t) for n, t in TOL.items()}
-    err_rms = {n: e[0] / np.sqrt(e[1] / e[2]) if e[2] and e[1] > 0 else 0.0 for n, e in err.items()}
-    parity = {"sample": sample + " against the fp64 oracle, all elements",
-              "err_rms": {n: float(f"{x:.3g}") for n, x in err_rms.items()},
-              "tol": {n: tol[n] for n in err_rms},
-              "pass": bool(all(err_rms[n] <= tol[n] for n in err_rms))}
-    return base, parity
+    return {"sample": f"the first {sample['nseq']} of {wl.batch} sequences against the fp64 oracle, all elements",
+            "err_rms": {n: float(f"{x:.3g}") for n, x in err_rms.items()},
+            "tol": {n: tol[n] for n in err_rms},
+            "pass": bool(all(err_rms[n] <= tol[n] for n in err_rms))}
 
 
 def measured_peaks(torch):
@@ -190,17 +253,26 @@ def calibrate_copy(mib: int, reps: int):
                       "GBps_read_plus_write": 2 * n / ms / 1e6}))
 
 
+def bwd_dq_path(max_seqlen_k):
+    """The backward kernels a call takes (the library's default choice, or
+    GDPA_BWD_DQ): dQ inside the dK/dV pass when every sequence's keys fit one
+    128-key block, else a separate dQ kernel."""
+    mode = os.environ.get("GDPA_BWD_DQ", "")
+    if mode == "fused" or (mode != "separate" and max_seqlen_k <= 128):
+        return "fused"
+    return "separate"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="jagged_self", choices=sorted(gi.WORKLOADS))
+    ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"], help="dtype of O, dQ, dK, dV")
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for per-kernel timing")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time each kernel after evicting L2 / MALL (512 MiB write before every launch)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
 
@@ -212,6 +284,23 @@ def main():
               "kernel on their own share with no collective.", file=sys.stderr)
         sys.exit(2)
 
+    wl = gi.WORKLOADS[args.workload]
+    DV = wl.head_dim_v or wl.head_dim
+    # FP8 Q/K and distinct V head dims are forward-only paths (the README's FP8
+    # support is inference); every other workload is timed forward + backward
+    with_bwd = not wl.fp8_qk and DV == wl.head_dim
+    if with_bwd and not wl.backward:
+        wl = gi.dataclasses.replace(wl, backward=True)
+    if not args.calibrate_copy:
+        print(f"[bench] drawing {wl.name} (seed {wl.seed})", file=sys.stderr, flush=True)
+        bt = gi.make_batch(wl)
+        oracle_sample = None
+        if not args.no_cpu_baseline:
+            # the oracle leg runs first, in forked worker processes, before
+            # this process touches the GPU
+            print(f"[bench] timing the CPU oracle baseline ({pool_size()} processes)", file=sys.stderr, flush=True)
+            base, oracle_sample = cpu_baseline(bt, args.cpu_budget)
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -222,15 +311,6 @@ def main():
 
     import generalized_attention_amd as g
 
-    wl = gi.WORKLOADS[args.workload]
-    DV = wl.head_dim_v or wl.head_dim
-    # FP8 Q/K and distinct V head dims are forward-only paths (the README's FP8
-    # support is inference); every other workload is timed forward + backward
-    with_bwd = not wl.fp8_qk and DV == wl.head_dim
-    if with_bwd and not wl.backward:
-        wl = gi.dataclasses.replace(wl, backward=True)
-    print(f"[bench] drawing {wl.name} (seed {wl.seed})", file=sys.stderr, flush=True)
-    bt = gi.make_batch(wl)
     pairs = workload_pairs(bt)
     P = int(pairs.sum())
     D = wl.head_dim
@@ -247,13 +327,15 @@ def main():
     q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, e16)
     do = dev(bt.do, e16) if with_bwd else None
     cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
-    o = torch.empty(q.shape[0], wl.heads_q, DV, dtype=torch.float32, device="cuda")
-    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
-    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    odt = torch.float32 if args.out_dtype == "fp32" else torch.bfloat16
+    o = torch.empty(q.shape[0], wl.heads_q, DV, dtype=odt, device="cuda")
+    dq = torch.empty(q.shape, dtype=odt, device="cuda")
+    dk = torch.empty(k.shape, dtype=odt, device="cuda")
+    dv = torch.empty(v.shape, dtype=odt, device="cuda")
     mq, mk = bt.max_seqlen_q, bt.max_seqlen_k
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
               window_right=wl.window_right)
+    path = bwd_dq_path(mk) if with_bwd else None
 
     def fwd():
         g.gdpa_varlen_fwd(q, k, v, o, cu_q, cu_k, mq, mk, wl.scale, q_descale=bt.q_scale, k_descale=bt.k_scale,
@@ -271,8 +353,22 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    # a 512 MiB write evicts the inputs from L2 and the 256 MB MALL, so that a
+    # flushed launch reads them from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    print(f"[bench] warmup done; timing {args.steps} steps, flushed and warm", file=sys.stderr, flush=True)
 
+    # flushed: the 512 MiB write before every step, outside the timed region
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        flush.fill_(i & 0xFF)
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    flushed = np.array([a.elapsed_time(b) for a, b in evs])
+    # warm: the same number of steps back to back
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -280,16 +376,14 @@ def main():
         step()
     e1.record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_warm = e0.elapsed_time(e1) / args.steps
+    ms_step = float(np.median(flushed))
 
-    # per-kernel launch durations (HIP events on the stream the kernels run on):
-    # back to back (inputs may stay in L2 / MALL between launches), and with
-    # --cold also with a 512 MiB buffer written before every launch, so that
-    # the inputs come from HBM
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
+    # per-kernel launch durations (HIP events on the stream the kernels run
+    # on), flushed like the steps and warm beside
     stats = {}
 
-    def launch_ms(fn, reps, cold=False):
+    def launch_ms(fn, reps, cold):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (a, b) in enumerate(evs):
             if cold:
@@ -301,31 +395,38 @@ def main():
         return np.array([a.elapsed_time(b) for a, b in evs])
 
     def avg_ms(fn, reps, name):
-        warm = launch_ms(fn, reps)
-        stats[name] = {"mean": round(float(warm.mean()), 4), "median": round(float(np.median(warm)), 4),
-                       "min": round(float(warm.min()), 4)}
-        if args.cold:
-            cold = launch_ms(fn, reps, cold=True)
-            stats[name].update(cold_median=round(float(np.median(cold)), 4), cold_min=round(float(cold.min()), 4))
-        return float(warm.mean())
+        cold = launch_ms(fn, reps, True)
+        warm = launch_ms(fn, reps, False)
+        stats[name] = {"mean": round(float(cold.mean()), 4), "median": round(float(np.median(cold)), 4),
+                       "min": round(float(cold.min()), 4), "warm_mean": round(float(warm.mean()), 4),
+                       "warm_median": round(float(np.median(warm)), 4)}
+        return float(cold.mean())
 
     # algorithmic work per launch: flops of the products the gradient needs
     # (S, dP, dV, dK in the dK/dV kernel, dQ in the dQ kernel; the dQ kernel's
     # recomputed S and dP are not counted) and the bytes each kernel must move
     # at least (every input read once, every output written once)
-    isz = {"q": q.element_size(), "k": k.element_size(), "v": 2, "do": 2, "out": 4}
+    osz = 4 if args.out_dtype == "fp32" else 2
+    isz = {"q": q.element_size(), "k": k.element_size(), "v": 2, "do": 2, "out": osz}
     tq, tk = q.shape[0], k.shape[0]
     nq, nkv = tq * wl.heads_q * D, tk * wl.heads_kv * D
     nqv, nkvv = tq * wl.heads_q * DV, tk * wl.heads_kv * DV  # V- and O-shaped tensors
     kern = {"gdpa_fwd_kernel": (avg_ms(fwd, args.kernel_reps, "gdpa_fwd_kernel"), 2 * (D + DV) * P,
                                 nq * isz["q"] + nkv * isz["k"] + nkvv * isz["v"] + nqv * isz["out"])}
-    if with_bwd:
+    if path == "fused":
+        # one kernel: dK, dV and dQ (the call's small schedule and clear kernels are inside the timing)
+        kern["gdpa_bwd_fused_kernel"] = (avg_ms(bwd, args.kernel_reps, "gdpa_bwd_fused_kernel"), 10 * D * P,
+                                         nq * (isz["q"] + isz["do"] + isz["out"])
+                                         + nkv * (isz["k"] + isz["v"] + 2 * isz["out"]))
+        bwd_ms = kern["gdpa_bwd_fused_kernel"][0]
+    elif path == "separate":
         kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps, "gdpa_bwd_dkdv_kernel"),
                                         8 * D * P,
                                         nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + 2 * nkv * isz["out"])
         kern["gdpa_bwd_dq_kernel"] = (avg_ms(lambda: bwd(True, False), args.kernel_reps, "gdpa_bwd_dq_kernel"),
                                       2 * D * P,
                                       nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])
+        bwd_ms = kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]
     dom = max(kern, key=lambda n: kern[n][0])
     dom_ms, dom_flops, dom_bytes = kern[dom]
     # the roof that binds: the larger of the MFMA and HBM fractions
@@ -335,13 +436,16 @@ def main():
         bound, achieved, peak, unit = "hbm", hbm_gbs, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", mfma_tf, BF16_PEAK_TFLOPS, "TFLOP/s"
-    traffic = None
+    traffic, traffic_source = None, None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
         ent = rec.get("kernels", {}).get(dom)
-        if ent and rec.get("source_hash") == kernel_source_hash() and rec.get("workload") == wl.name:
+        if (ent and rec.get("source_hash") == kernel_source_hash() and rec.get("workload") == wl.name
+                and rec.get("out_dtype", "fp32") == args.out_dtype):
             traffic = ent["hbm_bytes_per_launch"]
+            traffic_source = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE of the same command "
+                              "and sources, scaled by the counters of a plain device copy")
 
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
@@ -361,17 +465,27 @@ def main():
         "config": {"workload": f"{wl.name}: B={wl.batch} sequences, lengths U[{wl.lq_range[0]},{wl.lq_range[1]}] "
                                f"(drawn total {int(bt.seqlens_q.sum())} tokens), Hq={wl.heads_q}, "
                                f"Hkv={wl.heads_kv}, D={D}, act={wl.act}, mask={wl.mask}, "
-                               f"{'fwd+bwd' if with_bwd else 'fwd'}, fp32 outputs",
+                               f"{'fwd+bwd' if with_bwd else 'fwd'}, {args.out_dtype} outputs",
                    "global_batch": wl.batch, "seq_len": int(bt.max_seqlen_q), "parallelism": "none (1 GPU)"},
+        "timing": ("ms_per_step is the median over the timed steps, each after a 512 MiB write outside the "
+                   "timed region (inputs read from HBM); ms_per_step_warm runs the same steps back to back"),
+        "ms_per_step_warm": round(ms_warm, 4),
+        "value_warm": round(total_flops / (ms_warm * 1e-3) / 1e12, 2),
+        "ms_per_step_min": round(float(flushed.min()), 4),
         "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "fwd_tflops": round(fwd_flops / (kern["gdpa_fwd_kernel"][0] * 1e-3) / 1e12, 2),
-        "bwd_tflops": (round(bwd_flops / ((kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]) * 1e-3)
-                             / 1e12, 2) if with_bwd else None),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if with_bwd else None,
+        "bwd_dq_path": path,
         "kernel_ms": {n: round(t[0], 4) for n, t in kern.items()},
         "kernel_ms_stats": stats,
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "traffic_source": traffic_source,
+                     "achieved_from": f"algorithmic {'bytes' if bound == 'hbm' else 'flops'} per launch / mean "
+                                      f"flushed launch time ({args.kernel_reps} launches)"},
     }
+    if bound == "mfma" and hbm_gbs > 0:
+        result["roofline"]["hbm_gbs"] = round(hbm_gbs, 1)
     # sustained peaks on this GPU, measured after the timed work (context for the
     # published peaks the roofline uses)
     peaks = measured_peaks(torch)
@@ -380,11 +494,11 @@ def main():
     if not args.no_cpu_baseline:
         # the outputs the timed launches wrote (every launch computes the same values)
         torch.cuda.synchronize()
-        gpu = {"o": o.cpu().numpy()}
+        gpu = {"o": o.float().cpu().numpy()}
         if with_bwd:
-            gpu.update(dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"], result["parity"] = cpu_baseline(bt, args.cpu_budget, gpu)
+            gpu.update(dq=dq.float().cpu().numpy(), dk=dk.float().cpu().numpy(), dv=dv.float().cpu().numpy())
+        result["cpu_baseline"] = base
+        result["parity"] = parity_record(bt, oracle_sample, gpu)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -33,17 +33,24 @@ def test_parity_record_passes_on_oracle_outputs_and_flags_a_wrong_one():
     wl = dataclasses.replace(gi.WORKLOADS["tiny"], backward=True)
     bt = gi.make_batch(wl)
     out = _oracle_outputs(bt)
-    base, parity = bench.cpu_baseline(bt, 1.0, out)
-    assert base["kind"] == "oracle" and base["value"] > 0
+    base, sample = bench.cpu_baseline(bt, 1.0, workers=2)
+    assert base["kind"] == "oracle" and base["value"] > 0 and base["cores"] == 2
+    parity = bench.parity_record(bt, sample, out)
     assert parity["pass"] and set(parity["err_rms"]) == {"o", "dq", "dk", "dv"}
     assert max(parity["err_rms"].values()) < 1e-6  # fp32 storage of the fp64 result
     out["dv"] = out["dv"].copy()
     out["dv"][3, 1, 5] += 0.5 * np.sqrt(np.mean(out["dv"].astype(np.float64) ** 2)) / 0.01  # one element off
-    _, bad = bench.cpu_baseline(bt, 1.0, out)
+    bad = bench.parity_record(bt, sample, out)
     assert not bad["pass"] and bad["err_rms"]["dv"] > bad["tol"]["dv"]
 
 
-def test_cpu_baseline_without_outputs_has_no_parity():
-    bt = gi.make_batch(gi.WORKLOADS["tiny"])
-    base, parity = bench.cpu_baseline(bt, 0.5)
-    assert parity is None and base["unit"] == "TFLOP/s"
+def test_cpu_baseline_pool_size_and_gqa_sums():
+    # GQA: dK/dV of a KV head sum the group's query heads, computed as
+    # separate tasks; the pool record states its process count
+    wl = dataclasses.replace(gi.WORKLOADS["tiny"], heads_q=4, heads_kv=2, backward=True)
+    bt = gi.make_batch(wl)
+    out = _oracle_outputs(bt)
+    base, sample = bench.cpu_baseline(bt, 0.5, workers=3)
+    assert base["unit"] == "TFLOP/s" and base["cores"] == 3
+    assert bench.parity_record(bt, sample, out)["pass"]
+    assert 1 <= bench.pool_size() <= 16
