@@ -123,6 +123,12 @@ struct FwdKernel {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       __builtin_amdgcn_sched_barrier(0);
+      // the units with no activation work (S of block 0, P V of block 1) run
+      // at raised priority, so the other wave on the SIMD fills the vector
+      // ALU with its activation while these keep the matrix core busy
+      // (measured: 2-4 % shorter forwards at two waves per SIMD)
+      if (u == 0 || u == 2 * NA + NB) __builtin_amdgcn_s_setprio(3);
+      if (u == NA) __builtin_amdgcn_s_setprio(0);
       if (u + PREF < NU)
         ring[(u + PREF) % (PREF + 1)] =
             load_unit(u + PREF, kb0, kl, vl, lo, vo, lane, ring_hi[(u + PREF) % (PREF + 1)]);
@@ -152,6 +158,7 @@ struct FwdKernel {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 
