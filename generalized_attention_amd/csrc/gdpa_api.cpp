@@ -63,6 +63,9 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
                            int32_t mask, int32_t window_left, int32_t window_right, int32_t act,
                            float act_param, Common* c) {
   if (batch < 0 || max_lq < 0 || max_lk < 0 || total_q < 0 || total_k < 0) return GDPA_ERR_INVALID_ARG;
+  // no sequence is longer than its max_seqlen (an empty batch is an empty call)
+  if (batch > 0 && (total_q > (int64_t)batch * max_lq || total_k > (int64_t)batch * max_lk))
+    return GDPA_ERR_INVALID_ARG;
   if (total_q > INT32_MAX || total_k > INT32_MAX) return GDPA_ERR_UNSUPPORTED;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return GDPA_ERR_INVALID_ARG;
   if (d <= 0 || dv <= 0) return GDPA_ERR_INVALID_ARG;
@@ -210,18 +213,28 @@ struct BwdLayout {
   int64_t nturn;  // turn counters
 };
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+// Sizes past kMaxWorkspace (far beyond any GPU's memory) are reported as
+// SIZE_MAX: no call can be given that much, and the arithmetic stays in range
+// for any argument values.
+constexpr int64_t kMaxWorkspace = int64_t(1) << 60;
 BwdLayout bwd_layout(int64_t batch, bool jagged, int64_t max_lq, int64_t total_q, int64_t hq, int64_t d,
                      bool acc16) {
   BwdLayout l{};
   if (batch <= 0) return l;
-  const int64_t tiles = jagged ? total_q / gdpa::kDqTile + batch + 1
-                               : batch * ((max_lq + gdpa::kDqTile - 1) / gdpa::kDqTile);
-  l.nturn = tiles * hq;
+  const __int128 tiles = jagged ? (__int128)total_q / gdpa::kDqTile + batch + 1
+                                : (__int128)batch * ((max_lq + gdpa::kDqTile - 1) / gdpa::kDqTile);
+  const __int128 turn_bytes = tiles * hq * 4;
+  const __int128 acc_bytes = acc16 ? (__int128)total_q * hq * d * 4 : 0;
+  if (turn_bytes > kMaxWorkspace || acc_bytes > kMaxWorkspace) {
+    l.bytes = SIZE_MAX;
+    return l;
+  }
+  l.nturn = (int64_t)(tiles * hq);
   l.order = 0;
   l.queues = jagged && batch <= gdpa::kSortMax ? align256((size_t)batch * 4) : 0;
   l.turns = l.queues + align256(gdpa::kQWords * 4);
-  l.acc = l.turns + align256((size_t)l.nturn * 4);
-  l.bytes = l.acc + (acc16 ? align256((size_t)total_q * hq * d * 4) : 0);
+  l.acc = l.turns + align256((size_t)turn_bytes);
+  l.bytes = l.acc + (acc16 ? align256((size_t)acc_bytes) : 0);
   return l;
 }
 
@@ -626,7 +639,11 @@ size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32
 }
 
 const char* gdpa_status_string(gdpa_status_t s) {
-  switch (s) {
+  // read as the int the C caller passed (a value outside the enumeration
+  // would be undefined behaviour if loaded as the C++ enum type)
+  int code = 0;
+  std::memcpy(&code, &s, sizeof(code));
+  switch (code) {
     case GDPA_OK: return "GDPA_OK";
     case GDPA_ERR_INVALID_ARG: return "GDPA_ERR_INVALID_ARG";
     case GDPA_ERR_UNSUPPORTED: return "GDPA_ERR_UNSUPPORTED";

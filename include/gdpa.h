@@ -142,7 +142,8 @@ gdpa_status_t gdpa_fwd(const void* q, const void* k, const void* v, void* o,
 
 /* Jagged forward.  max_seqlen_q/k are host upper bounds of the per-sequence
  * lengths (used to size the launch; no device->host copy is made);
- * total_q/total_k are the packed token counts (cu[B]). */
+ * total_q/total_k are the packed token counts (cu[B]); a total above batch x
+ * max_seqlen returns GDPA_ERR_INVALID_ARG. */
 gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void* o,
                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                               int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -231,6 +232,8 @@ gdpa_status_t gdpa_varlen_bwd_noalloc(const void* q, const void* k, const void* 
  * dK/dV pass (max seqlen_k > 128 with GDPA_BWD_DQ=fused set), an fp32 dQ
  * accumulator of total_q * num_heads_q * head_dim values; each part rounded
  * up to 256 bytes.  The queries read GDPA_BWD_DQ as the calls do.
+ * A query whose answer would pass 2^60 bytes returns SIZE_MAX (no call can
+ * be given that much).
  * A call given less than its query returns GDPA_ERR_WORKSPACE_TOO_SMALL before
  * launching anything.  The workspace is caller-owned and only used on the
  * call's stream; calls that share one must be ordered on one stream. */

@@ -211,9 +211,23 @@ def err_ratio_allow(got, ref, allow):
     return err / rms
 
 
-def backward_ratios(bt, dq, dk, dv, refs=None):
+def seq_ratios(got, ref, cu, allow=None):
+    """Per sequence b: max|err| / rms(ref) over rows cu[b]:cu[b+1] (each
+    sequence against its own rms; empty sequences skipped), with an optional
+    per-element allowance."""
+    out = {}
+    for b in range(len(cu) - 1):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        if cu[b + 1] > cu[b]:
+            a = 0.0 if allow is None else allow[sl]
+            out[b] = err_ratio_allow(got[sl], ref[sl], a)
+    return out
+
+
+def backward_ratios(bt, dq, dk, dv, refs=None, per_seq=None):
     """max|err| / rms(ref) of dQ, dK, dV against the oracle, with the kink
-    allowance above (dV none)."""
+    allowance above (dV none).  per_seq (a dict) receives the per-sequence
+    ratios of each gradient."""
     q, k, v, do = oracle_inputs(bt)
     wl = bt.wl
     if refs is None:
@@ -221,6 +235,9 @@ def backward_ratios(bt, dq, dk, dv, refs=None):
     aq, ak = kink_allowance(bt, q, k, v, do)
     rq, rk, rv = refs
     as_np = lambda t: t if isinstance(t, np.ndarray) else t.float().cpu().double().numpy()
-    return dict(dq=err_ratio_allow(as_np(dq).reshape(rq.shape), rq, aq),
-                dk=err_ratio_allow(as_np(dk).reshape(rk.shape), rk, ak),
-                dv=err_ratio(as_np(dv).reshape(rv.shape), rv))
+    gq, gk, gv = as_np(dq).reshape(rq.shape), as_np(dk).reshape(rk.shape), as_np(dv).reshape(rv.shape)
+    if per_seq is not None:
+        per_seq["dq"] = seq_ratios(gq, rq, bt.cu_seqlens_q, aq)
+        per_seq["dk"] = seq_ratios(gk, rk, bt.cu_seqlens_k, ak)
+        per_seq["dv"] = seq_ratios(gv, rv, bt.cu_seqlens_k)
+    return dict(dq=err_ratio_allow(gq, rq, aq), dk=err_ratio_allow(gk, rk, ak), dv=err_ratio(gv, rv))

@@ -139,7 +139,9 @@ def test_fwd_validation(lib, over, expect):
 @pytest.mark.parametrize("over,expect", [
     (dict(cq=None), INVALID),
     (dict(tq=-1), INVALID),
-    (dict(tq=2 ** 31), UNSUPPORTED),
+    (dict(tq=2 ** 31, B=2 ** 24), UNSUPPORTED),   # rows past 32-bit token indices
+    (dict(tq=257), INVALID),                  # more tokens than batch x max_seqlen_q
+    (dict(tk=257), INVALID),
     (dict(B=0), OK),
     (dict(tq=0), OK),
     (dict(D=256), UNSUPPORTED),

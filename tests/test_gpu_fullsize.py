@@ -69,15 +69,26 @@ def test_full_size_seed_sweep(g, name, seed):
     _check_workload(g, gi.WORKLOADS[name], seed, 32)
 
 
-def _check_workload(g, wl, seed, n_rows):
+# bf16 outputs (O, dQ, dK, dV rounded to bf16 on the device) at the
+# jagged, full-length and short-KV workloads
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["jagged_self", "full_self", "short_kv_cross"])
+def test_full_size_bf16_outputs(g, name):
+    import torch
+    _check_workload(g, gi.WORKLOADS[name], None, 48, out_dtype=torch.bfloat16)
+
+
+def _check_workload(g, wl, seed, n_rows, out_dtype=None):
     import torch
     name = wl.name if seed is None else f"{wl.name} seed {seed}"
+    if out_dtype is not None:
+        name += f" ({str(out_dtype).replace('torch.', '')} outputs)"
     print(f"[fullsize] {name}: drawing inputs", flush=True)
     bt = gi.make_batch(wl, seed=seed)
     base_seed = wl.seed if seed is None else seed
     dev = device_batch(bt)
     print(f"[fullsize] {name}: forward", flush=True)
-    o = run_forward(g, bt, dev)
+    o = run_forward(g, bt, dev, out_dtype=out_dtype)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any(), "forward left unwritten (NaN-poisoned) outputs"
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
@@ -100,7 +111,7 @@ def _check_workload(g, wl, seed, n_rows):
         return
 
     print(f"[fullsize] {name}: backward", flush=True)
-    dq, dk, dv = run_backward(g, bt, dev)
+    dq, dk, dv = run_backward(g, bt, dev, grad_dtype=out_dtype)
     torch.cuda.synchronize()
     for t_ in (dq, dk, dv):
         assert not torch.isnan(t_).any(), "backward left unwritten (NaN-poisoned) outputs"
