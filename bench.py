@@ -120,7 +120,7 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None, workers=None):
     workers = workers or pool_size()
     pairs = workload_pairs(bt) // max(wl.heads_q, 1)  # per sequence and head
     DV = wl.head_dim_v or wl.head_dim
-    with_bwd = not wl.fp8_qk and DV == wl.head_dim and bt.do is not None
+    with_bwd = not wl.fp8_qk and bt.do is not None
     dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
     if wl.fp8_qk:
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
@@ -129,7 +129,8 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None, workers=None):
     _ORACLE_INPUTS.clear()
     _ORACLE_INPUTS.update(wl=wl, q=q, k=k, v=dec(bt.v), do=dec(bt.do) if with_bwd else None,
                           cq=bt.cu_seqlens_q, ck=bt.cu_seqlens_k, with_bwd=with_bwd)
-    per_pair = 14 * wl.head_dim if with_bwd else 2 * (wl.head_dim + DV)
+    D = wl.head_dim
+    per_pair = 2 * (D + DV) + (2 * (3 * D + 2 * DV) if with_bwd else 0)
     wall, t_fwd, t_bwd, flops, nseq = 0.0, 0.0, 0.0, 0, 0
     results = []
     ctx = multiprocessing.get_context("fork")
@@ -286,9 +287,9 @@ def main():
 
     wl = gi.WORKLOADS[args.workload]
     DV = wl.head_dim_v or wl.head_dim
-    # FP8 Q/K and distinct V head dims are forward-only paths (the README's FP8
-    # support is inference); every other workload is timed forward + backward
-    with_bwd = not wl.fp8_qk and DV == wl.head_dim
+    # FP8 Q/K is a forward-only path (the README's FP8 support is inference);
+    # every other workload is timed forward + backward
+    with_bwd = not wl.fp8_qk
     if with_bwd and not wl.backward:
         wl = gi.dataclasses.replace(wl, backward=True)
     if not args.calibrate_copy:
@@ -314,7 +315,8 @@ def main():
     pairs = workload_pairs(bt)
     P = int(pairs.sum())
     D = wl.head_dim
-    fwd_flops, bwd_flops = 2 * (D + DV) * P, (10 * D * P if with_bwd else 0)
+    # S and dK, dQ contract or produce Q/K's head dim D, dP and dV V's DV
+    fwd_flops, bwd_flops = 2 * (D + DV) * P, (2 * (3 * D + 2 * DV) * P if with_bwd else 0)
 
     def dev(a, kind):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -415,17 +417,19 @@ def main():
                                 nq * isz["q"] + nkv * isz["k"] + nkvv * isz["v"] + nqv * isz["out"])}
     if path == "fused":
         # one kernel: dK, dV and dQ (the call's small schedule and clear kernels are inside the timing)
-        kern["gdpa_bwd_fused_kernel"] = (avg_ms(bwd, args.kernel_reps, "gdpa_bwd_fused_kernel"), 10 * D * P,
-                                         nq * (isz["q"] + isz["do"] + isz["out"])
-                                         + nkv * (isz["k"] + isz["v"] + 2 * isz["out"]))
+        kern["gdpa_bwd_fused_kernel"] = (avg_ms(bwd, args.kernel_reps, "gdpa_bwd_fused_kernel"), bwd_flops,
+                                         nq * (isz["q"] + isz["out"]) + nqv * isz["do"]
+                                         + nkv * (isz["k"] + isz["out"]) + nkvv * (isz["v"] + isz["out"]))
         bwd_ms = kern["gdpa_bwd_fused_kernel"][0]
     elif path == "separate":
         kern["gdpa_bwd_dkdv_kernel"] = (avg_ms(lambda: bwd(False, True), args.kernel_reps, "gdpa_bwd_dkdv_kernel"),
-                                        8 * D * P,
-                                        nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + 2 * nkv * isz["out"])
+                                        2 * (2 * D + 2 * DV) * P,
+                                        nq * isz["q"] + nqv * isz["do"] + nkv * (isz["k"] + isz["out"])
+                                        + nkvv * (isz["v"] + isz["out"]))
         kern["gdpa_bwd_dq_kernel"] = (avg_ms(lambda: bwd(True, False), args.kernel_reps, "gdpa_bwd_dq_kernel"),
                                       2 * D * P,
-                                      nq * (isz["q"] + isz["do"]) + nkv * (isz["k"] + isz["v"]) + nq * isz["out"])
+                                      nq * (isz["q"] + isz["out"]) + nqv * isz["do"] + nkv * isz["k"]
+                                      + nkvv * isz["v"])
         bwd_ms = kern["gdpa_bwd_dkdv_kernel"][0] + kern["gdpa_bwd_dq_kernel"][0]
     dom = max(kern, key=lambda n: kern[n][0])
     dom_ms, dom_flops, dom_bytes = kern[dom]

@@ -73,7 +73,7 @@ WORKLOADS = {
     "jagged_self_d96": Workload("jagged_self_d96", 64, 4, 4, 96, (1, 1024), None,
                                 "fast_gelu", backward=True, seed=2),
     "jagged_self_d192": Workload("jagged_self_d192", 64, 4, 4, 192, (1, 1024), None,
-                                 "fast_gelu", head_dim_v=128, seed=2),
+                                 "fast_gelu", head_dim_v=128, backward=True, seed=2),
     "window_gqa_fp8": Workload("window_gqa_fp8", 16, 16, 4, 64, (1024, 4096),
                                None, "leaky_relu", act_param=0.01,
                                mask="window", window_left=511, window_right=0,

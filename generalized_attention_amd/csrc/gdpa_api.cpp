@@ -103,7 +103,7 @@ bool fwd_built(int in_kind, int32_t d, int32_t dv) {
   return in_kind != gdpa::EL_FP8 && d == 192 && dv == 128;
 }
 bool bwd_built(int in_kind, int32_t d, int32_t dv) {
-  return in_kind != gdpa::EL_FP8 && d == dv && (d == 64 || d == 96 || d == 128);
+  return in_kind != gdpa::EL_FP8 && ((d == dv && (d == 64 || d == 96 || d == 128)) || (d == 192 && dv == 128));
 }
 
 // Output dtype -> kernel output kind (-1: not an output type).
@@ -460,7 +460,7 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   const DqMode mode = dq_mode();
   const bool force_fused = mode == DQ_FUSED;
   const bool force_separate = mode == DQ_SEPARATE;
-  const bool fused = want_dq && want_dkv && !(a.dsplit && a.kvsplit) && a.ncu > 0 && !force_separate &&
+  const bool fused = want_dq && want_dkv && c.d == c.dv && !(a.dsplit && a.kvsplit) && a.ncu > 0 && !force_separate &&
                      (force_fused || c.max_lk <= gdpa::kBwdBN) &&
                      ((int64_t)c.max_lq + gdpa::kDqTile) * c.hq * c.d * 4 <= INT32_MAX;
   gdpa_status_t sst = debug_check_jagged(cu_q, cu_k, c, stream);

@@ -10,6 +10,7 @@ static hipError_t launch_bwd_el(const BwdArgs& a, int head_dim, int act_kind, bo
   if (head_dim == 64) return launch_bwd_ed<EL, 64>(a, act_kind, want_dq, want_dkv, fused, stream);
   if (head_dim == 96) return launch_bwd_ed<EL, 96>(a, act_kind, want_dq, want_dkv, fused, stream);
   if (head_dim == 128) return launch_bwd_ed<EL, 128>(a, act_kind, want_dq, want_dkv, fused, stream);
+  if (head_dim == 192) return launch_bwd_ed<EL, 192, 128>(a, act_kind, want_dq, want_dkv, fused, stream);
   return hipErrorInvalidValue;
 }
 

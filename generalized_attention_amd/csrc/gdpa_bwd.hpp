@@ -71,13 +71,22 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs& a, int b, int& qs, int
 // ALU evaluates the activation.  With DSPL (few keys per dQ row, where the
 // bf16 rounding of dS no longer averages out) dS is carried as hi + lo words
 // in two LDS tiles and each dQ product is taken twice.
-template <int D, int ACT, int EL, bool SPLIT, bool DQ = false, bool DSPL = false>
+// D is the head dim of Q and K (S, dK), DV that of V and dO (dP, dV); they
+// differ only at (192, 128), where the S units of k-steps >= DV / 16 carry no
+// dP product and the dK blocks >= DV / 32 no dV product.
+template <int D, int ACT, int EL, bool SPLIT, bool DQ = false, bool DSPL = false, int DV = D>
 struct DkdvKernel {
   static constexpr int BQ = 64;                      // query rows per step
-  static constexpr int KS = D / 16;
-  static constexpr int NDB = D / 32;
-  static constexpr int ROWB = 2 * lds_dim(D);        // LDS row bytes (96 padded to 128)
-  static constexpr int TB = BQ * ROWB;               // bytes of one Q (or dO) tile
+  static constexpr int KS = D / 16;                  // k-steps of S (Q, K head dim)
+  static constexpr int NDB = D / 32;                 // 32-column blocks of dK
+  static constexpr int KSV = DV / 16;                // k-steps of dP (dO, V head dim)
+  static constexpr int NDBV = DV / 32;               // 32-column blocks of dV
+  static constexpr int ROWB = 2 * lds_dim(D);        // LDS row bytes of a Q tile (96 padded to 128)
+  static constexpr int ROWBV = 2 * lds_dim(DV);      // LDS row bytes of a dO tile
+  static constexpr int TB = BQ * ROWB;               // bytes of one Q tile
+  static constexpr int TBV = BQ * ROWBV;             // bytes of one dO tile
+  static_assert(KSV <= KS && NDBV <= NDB, "V's head dim is at most Q's");
+  static_assert(!DQ || DV == D, "the fused pass is built for equal head dims");
   static constexpr int NP = SPLIT ? 2 : 1;           // 16-bit words per P / dS element (dV, dK)
   static constexpr int NPD = SPLIT || DSPL ? 2 : 1;  // 16-bit words per dS element kept
   static constexpr int NA = KS;                      // S/dP units per query block (2 MFMAs each)
@@ -99,6 +108,7 @@ struct DkdvKernel {
   static constexpr int DS_TILE = DS_BYTES * (DSPL ? 2 : 1);  // hi (and lo) tiles of one step
 
   using LaneOffs = TileOffs<ROWB>;
+  using LaneOffsV = TileOffs<ROWBV>;
   using DsOffs = TileOffs<DS_ROWB>;
   struct Words {  // packed P and dS of one 32-query block: [hi/lo][t] x 4 words
     u32x4 p[NP][2];
@@ -185,8 +195,8 @@ struct DkdvKernel {
   // Units q >= NQH read the lo tile.
   static __device__ __forceinline__ void load_dq(int qu, const uint8_t* dsl, const int* dsa, const int* dsb,
                                                  u32x4& o0, u32x4& o1) {
-    const int q = qu % NQH;
-    dsl += (qu / NQH) * DS_BYTES;
+    const int q = NQH > 0 ? qu % NQH : 0;  // (no dQ units without DQ)
+    dsl += (NQH > 0 ? qu / NQH : 0) * DS_BYTES;
     const int a2[2] = {dsa[0], dsa[1]};
     if constexpr (DQB == 2) {
       const int b2[2] = {dsb[0], dsb[1]};
@@ -199,7 +209,7 @@ struct DkdvKernel {
   }
   static __device__ __forceinline__ void mma_dq(int qu, const u32x4& o0, const u32x4& o1, const u32x4* ktr,
                                                 f32x16* dqacc) {
-    const int q = qu % NQH;
+    const int q = NQH > 0 ? qu % NQH : 0;
     if constexpr (DQB == 2) {
       dqacc[0] = mfma16<EL>(o0, ktr[q], dqacc[0]);
       dqacc[1] = mfma16<EL>(o1, ktr[q], dqacc[1]);
@@ -210,15 +220,16 @@ struct DkdvKernel {
   }
 
   static __device__ __forceinline__ void load_unit(int u, const uint8_t* ql, const uint8_t* dl, const LaneOffs& lo,
-                                                   const uint8_t* dsl, const int* dsa, const int* dsb,
-                                                   u32x4& o0, u32x4& o1) {
+                                                   const LaneOffsV& lov, const uint8_t* dsl, const int* dsa,
+                                                   const int* dsb, u32x4& o0, u32x4& o1) {
     const Unit x = unit(u);
     if (x.kind == U_SDP) {
       o0 = row_at(ql, lo.row[x.s] + x.qb * 32 * ROWB);
-      o1 = row_at(dl, lo.row[x.s] + x.qb * 32 * ROWB);
+      o1 = x.s < KSV ? row_at(dl, lov.row[x.s < KSV ? x.s : 0] + x.qb * 32 * ROWBV) : o0;
     } else if (x.kind == U_DVK) {
       const int base = (x.qb * 32 + 16 * x.t) * ROWB;
-      o0 = tr_at(dl, lo.tr[x.db], base);
+      o0 = x.db < NDBV ? tr_at(dl, lov.tr[x.db < NDBV ? x.db : 0], (x.qb * 32 + 16 * x.t) * ROWBV)
+                       : u32x4{0u, 0u, 0u, 0u};
       o1 = tr_at(ql, lo.tr[x.db], base);
     } else {
       load_dq(x.q, dsl, dsa, dsb, o0, o1);
@@ -230,11 +241,11 @@ struct DkdvKernel {
     const Unit x = unit(u);
     if (x.kind == U_SDP) {
       sacc[x.qb] = mfma16<EL>(o0, kreg[x.s], sacc[x.qb]);
-      dpacc[x.qb] = mfma16<EL>(o1, vreg[x.s], dpacc[x.qb]);
+      if (x.s < KSV) dpacc[x.qb] = mfma16<EL>(o1, vreg[x.s < KSV ? x.s : 0], dpacc[x.qb]);
     } else if (x.kind == U_DVK) {
 #pragma unroll
       for (int h = 0; h < NP; ++h) {
-        dvacc[x.db] = mfma16<EL>(o0, wd[x.qb].p[h][x.t], dvacc[x.db]);
+        if (x.db < NDBV) dvacc[x.db < NDBV ? x.db : 0] = mfma16<EL>(o0, wd[x.qb].p[h][x.t], dvacc[x.db < NDBV ? x.db : 0]);
         dkacc[x.db] = mfma16<EL>(o1, wd[x.qb].ds[h][x.t], dkacc[x.db]);
       }
     } else {
@@ -248,7 +259,7 @@ struct DkdvKernel {
   // previous step's dQ from dsr.
   template <bool MASK>
   static __device__ __forceinline__ void step(const uint8_t* ql, const uint8_t* dl, const LaneOffs& lo,
-                                              const u32x4* kreg, const u32x4* vreg, f32x16* dkacc, f32x16* dvacc,
+                                              const LaneOffsV& lov, const u32x4* kreg, const u32x4* vreg, f32x16* dkacc, f32x16* dvacc,
                                               const int* mlo, const int* mhi, const ActConsts& k,
                                               uint8_t* dsw = nullptr, const uint8_t* dsr = nullptr,
                                               const int* dsa = nullptr, const int* dsb = nullptr,
@@ -258,11 +269,11 @@ struct DkdvKernel {
     Words wd[2];
     u32x4 ring[PREF + 1][2];
 #pragma unroll
-    for (int u = 0; u < PREF; ++u) load_unit(u, ql, dl, lo, dsr, dsa, dsb, ring[u][0], ring[u][1]);
+    for (int u = 0; u < PREF; ++u) load_unit(u, ql, dl, lo, lov, dsr, dsa, dsb, ring[u][0], ring[u][1]);
     auto unit_body = [&](const int u) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       if (u + PREF < NU)
-        load_unit(u + PREF, ql, dl, lo, dsr, dsa, dsb, ring[(u + PREF) % (PREF + 1)][0],
+        load_unit(u + PREF, ql, dl, lo, lov, dsr, dsa, dsb, ring[(u + PREF) % (PREF + 1)][0],
                   ring[(u + PREF) % (PREF + 1)][1]);
       mma_unit(u, ring[u % (PREF + 1)][0], ring[u % (PREF + 1)][1], kreg, vreg, sacc, dpacc, wd, dkacc, dvacc, ktr,
                dqacc);
@@ -280,9 +291,9 @@ struct DkdvKernel {
         if (u == U3 - 1) write_ds(dsw, krow, hf, 1, wd[1]);
       }
     };
-    if constexpr (DQ) {
-      // the longer stream with dQ units exceeds the unroller's threshold:
-      // issue it with compile-time unit indices
+    if constexpr (DQ || D != DV) {
+      // the longer streams (dQ units; head dim 192) exceed the unroller's
+      // threshold: issue them with compile-time unit indices
       static_for<0, NU>([&](auto uc) __attribute__((always_inline)) { unit_body(decltype(uc)::value); });
     } else {
 #pragma unroll
@@ -320,15 +331,16 @@ constexpr int dkdv_occupancy() {
   return (D == 64 && !SPLIT && ACT != ACT_GELU) ? 2 : 1;
 }
 
-template <int D, int ACT, int EL, bool SPLIT>
+template <int D, int ACT, int EL, bool SPLIT, int DV = D>
 __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_bwd_dkdv_kernel(const BwdArgs a) {
-  using K = DkdvKernel<D, ACT, EL, SPLIT>;
+  using K = DkdvKernel<D, ACT, EL, SPLIT, false, false, DV>;
   constexpr int BNB = kBwdBN;  // keys per workgroup (32 per wave)
   constexpr int BQ = K::BQ, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB, TB = K::TB;
+  constexpr int KSV = K::KSV, NDBV = K::NDBV, ROWBV = K::ROWBV, TBV = K::TBV;
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_lds0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds0[TBV];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds1[TBV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -359,37 +371,36 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
   const int nsteps = (mb_end - mb_begin) * a.group;
 
   // K and V of this lane's key as B operands (column = key, 8 head-dim values per k-step)
-  const long kv_ld = (long)a.hkv * D;
-  u32x4 kreg[KS], vreg[KS];
+  const long kv_ld = (long)a.hkv * D, vv_ld = (long)a.hkv * DV;
+  u32x4 kreg[KS], vreg[KSV];
   {
-    const long krow = (long)(ks + min(kj, lk - 1)) * kv_ld + g * D + hf * 8;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + krow;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + krow;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (long)(ks + min(kj, lk - 1)) * kv_ld + g * D + hf * 8;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (long)(ks + min(kj, lk - 1)) * vv_ld + g * DV + hf * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kreg[s] = load16_or_zero(kp + s * 16, kj < lk);
-      vreg[s] = load16_or_zero(vp + s * 16, kj < lk);
-    }
-  }
-  f32x16 dkacc[NDB], dvacc[NDB];
+    for (int s = 0; s < KS; ++s) kreg[s] = load16_or_zero(kp + s * 16, kj < lk);
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dkacc[i] = f32x16{};
-    dvacc[i] = f32x16{};
+    for (int s = 0; s < KSV; ++s) vreg[s] = load16_or_zero(vp + s * 16, kj < lk);
   }
+  f32x16 dkacc[NDB], dvacc[NDBV];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dkacc[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NDBV; ++i) dvacc[i] = f32x16{};
   const TileOffs<ROWB> loffs = TileOffs<ROWB>::make(lane);
+  const TileOffs<ROWBV> loffsv = TileOffs<ROWBV>::make(lane);
 
-  const int q_ld_b = a.hq * D * 2;  // bytes per token row of q / dO
+  const int q_ld_b = a.hq * D * 2;    // bytes per token row of q
+  const int do_ld_b = a.hq * DV * 2;  // bytes per token row of dO
   // this sequence's q and dO rows (all heads); 32-bit offsets, bounded on the host
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(static_cast<const uint8_t*>(a.q) + (long)qs * q_ld_b, lq * q_ld_b);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(static_cast<const uint8_t*>(a.dout) + (long)qs * q_ld_b, lq * q_ld_b);
+  const __amdgpu_buffer_rsrc_t drs =
+      make_rsrc(static_cast<const uint8_t*>(a.dout) + (long)qs * do_ld_b, lq * do_ld_b);
   auto step_m0 = [&](int i) { return (mb_begin + i / a.group) * BQ; };
   auto stage = [&](int i, uint8_t* ql, uint8_t* dl) {
     const int h = g * a.group + i % a.group;
     const int m0 = step_m0(i);
-    const int o = m0 * q_ld_b + h * D * 2;
-    stage_tile_buf<BQ, ROWB, 4, D / 8>(qrs, o, q_ld_b, lq - m0, ql, wave, lane);
-    stage_tile_buf<BQ, ROWB, 4, D / 8>(drs, o, q_ld_b, lq - m0, dl, wave, lane);
+    stage_tile_buf<BQ, ROWB, 4, D / 8>(qrs, m0 * q_ld_b + h * D * 2, q_ld_b, lq - m0, ql, wave, lane);
+    stage_tile_buf<BQ, ROWBV, 4, DV / 8>(drs, m0 * do_ld_b + h * DV * 2, do_ld_b, lq - m0, dl, wave, lane);
   };
   auto compute = [&](int i, const uint8_t* ql, const uint8_t* dl) {
     if (!wave_active) return;
@@ -418,15 +429,17 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     // At D = 64 they fit among the arch VGPRs, and are left there.
     if constexpr (D > 64) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        asm volatile("" : "+a"(kreg[s]));
-        asm volatile("" : "+a"(vreg[s]));
-      }
+      for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(kreg[s]));
+#pragma unroll
+      for (int s = 0; s < KSV; ++s) asm volatile("" : "+a"(vreg[s]));
     }
+    const auto& lov = [&]() -> const auto& {
+      if constexpr (D == DV) return loffs; else return loffsv;
+    }();
     if (full)
-      K::template step<false>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
+      K::template step<false>(ql, dl, loffs, lov, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
     else
-      K::template step<true>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
+      K::template step<true>(ql, dl, loffs, lov, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act);
   };
 
   if (nsteps > 0) stage(0, q_lds0, do_lds0);
@@ -445,17 +458,19 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
   }
 
   if (wave_active && kj < lk) {
-    const long orow = ((long)(ks + kj) * a.hkv + g) * D;
+    const long orow = ((long)(ks + kj) * a.hkv + g) * D, vrow = ((long)(ks + kj) * a.hkv + g) * DV;
+    const float gs = a.act.gscale, ps = a.act.pscale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
-        const float gs = a.act.gscale, ps = a.act.pscale;
         store4(a.dk, orow + d, dkacc[db][4 * i4] * gs, dkacc[db][4 * i4 + 1] * gs, dkacc[db][4 * i4 + 2] * gs,
                dkacc[db][4 * i4 + 3] * gs, a.out_kind);
-        store4(a.dv, orow + d, dvacc[db][4 * i4] * ps, dvacc[db][4 * i4 + 1] * ps, dvacc[db][4 * i4 + 2] * ps,
-               dvacc[db][4 * i4 + 3] * ps, a.out_kind);
+        if (db < NDBV)
+          store4(a.dv, vrow + d, dvacc[db < NDBV ? db : 0][4 * i4] * ps, dvacc[db < NDBV ? db : 0][4 * i4 + 1] * ps,
+                 dvacc[db < NDBV ? db : 0][4 * i4 + 2] * ps, dvacc[db < NDBV ? db : 0][4 * i4 + 3] * ps,
+                 a.out_kind);
       }
     }
   }
@@ -842,11 +857,11 @@ __global__ __launch_bounds__(256, 1) void gdpa_bwd_fused_kernel(const BwdArgs a)
           }
         }
         if (full)
-          K::template step<false>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act, dsw, dsr, dsa, dsb, ktr,
-                                  dqacc, krow, hf);
+          K::template step<false>(ql, dl, loffs, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act, dsw, dsr, dsa,
+                                  dsb, ktr, dqacc, krow, hf);
         else
-          K::template step<true>(ql, dl, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act, dsw, dsr, dsa, dsb, ktr,
-                                 dqacc, krow, hf);
+          K::template step<true>(ql, dl, loffs, loffs, kreg, vreg, dkacc, dvacc, mlo, mhi2, a.act, dsw, dsr, dsa,
+                                 dsb, ktr, dqacc, krow, hf);
       };
       // one step over fixed LDS buffers: (ql, dl) this step's tiles, (qn, dn)
       // the next step's, dsw / dsr the dS tiles written / read
@@ -914,13 +929,18 @@ __global__ __launch_bounds__(256, 1) void gdpa_bwd_fused_kernel(const BwdArgs a)
 }
 
 // ----------------------------------------------------------------------- dQ
-template <int D, int ACT, int EL, bool SPLIT>
+// D: head dim of Q and K (S, dQ); DV: that of V and dO (dP), smaller only at
+// (192, 128).
+template <int D, int ACT, int EL, bool SPLIT, int DV = D>
 struct DqKernel {
-  static constexpr int BN = 8192 / lds_dim(D);  // keys per KV tile
+  static constexpr int BN = 8192 / lds_dim(D) < 64 ? 64 : 8192 / lds_dim(D);  // keys per KV tile
   static constexpr int NKB = BN / 32;
-  static constexpr int KS = D / 16;
+  static constexpr int KS = D / 16;              // k-steps of S
+  static constexpr int KSV = DV / 16;            // k-steps of dP
   static constexpr int NDB = D / 32;
-  static constexpr int ROWB = 2 * lds_dim(D);  // LDS row bytes (96 padded to 128)
+  static constexpr int ROWB = 2 * lds_dim(D);    // LDS row bytes of a K tile (96 padded to 128)
+  static constexpr int ROWBV = 2 * lds_dim(DV);  // LDS row bytes of a V tile
+  static_assert(KSV <= KS, "V's head dim is at most K's");
 
   static constexpr int NP = SPLIT ? 2 : 1;   // 16-bit words per dS element
   static constexpr int NA = KS;               // S/dP units per key block (2 MFMAs each)
@@ -928,6 +948,7 @@ struct DqKernel {
   static constexpr int NU = 2 * NA + 2 * NB;  // units of a pair of key blocks
   static constexpr int PREF = 2;              // units of operand prefetch
   using LaneOffs = TileOffs<ROWB>;
+  using LaneOffsV = TileOffs<ROWBV>;
 
   // One pair of accumulator elements (key rows 8t+2w, +1) -> dS words.
   template <bool MASK>
@@ -952,11 +973,11 @@ struct DqKernel {
   // block u / NA, k-step u % NA; else dQ of block (u - 2 NA) / NB, key-row half
   // t and head-dim block db.
   static __device__ __forceinline__ void load_unit(int u, int kb0, const uint8_t* kl, const uint8_t* vl,
-                                                   const LaneOffs& lo, u32x4& o0, u32x4& o1) {
+                                                   const LaneOffs& lo, const LaneOffsV& lov, u32x4& o0, u32x4& o1) {
     if (u < 2 * NA) {
       const int kb = kb0 + u / NA, s = u % NA;
       o0 = row_at(kl, lo.row[s] + kb * 32 * ROWB);
-      o1 = row_at(vl, lo.row[s] + kb * 32 * ROWB);
+      o1 = s < KSV ? row_at(vl, lov.row[s < KSV ? s : 0] + kb * 32 * ROWBV) : o0;
     } else {
       const int v = u - 2 * NA, kb = kb0 + v / NB, t = (v % NB) / NDB, db = v % NDB;
       o0 = tr_at(kl, lo.tr[db], (kb * 32 + 16 * t) * ROWB);
@@ -971,24 +992,25 @@ struct DqKernel {
   // relative to block j's accumulator base (used when MASK).
   template <bool MASK>
   static __device__ __forceinline__ void block_pair(const uint8_t* kl, const uint8_t* vl, int kb0, const LaneOffs& lo,
-                                                    const u32x4* qreg, const u32x4* doreg, f32x16* dqacc,
+                                                    const LaneOffsV& lov, const u32x4* qreg, const u32x4* doreg,
+                                                    f32x16* dqacc,
                                                     const int* mlo, const int* mhi, const ActConsts& k) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}}, dpacc[2] = {f32x16{}, f32x16{}};
     u32x4 ds[2][NP][2];
     u32x4 ring[PREF + 1][2];
 #pragma unroll
-    for (int u = 0; u < PREF; ++u) load_unit(u, kb0, kl, vl, lo, ring[u][0], ring[u][1]);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    for (int u = 0; u < PREF; ++u) load_unit(u, kb0, kl, vl, lo, lov, ring[u][0], ring[u][1]);
+    auto unit_body = [&](const int u) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       if (u + PREF < NU)
-        load_unit(u + PREF, kb0, kl, vl, lo, ring[(u + PREF) % (PREF + 1)][0], ring[(u + PREF) % (PREF + 1)][1]);
+        load_unit(u + PREF, kb0, kl, vl, lo, lov, ring[(u + PREF) % (PREF + 1)][0],
+                  ring[(u + PREF) % (PREF + 1)][1]);
       const u32x4& o0 = ring[u % (PREF + 1)][0];
       const u32x4& o1 = ring[u % (PREF + 1)][1];
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
         sacc[j] = mfma16<EL>(o0, qreg[s], sacc[j]);
-        dpacc[j] = mfma16<EL>(o1, doreg[s], dpacc[j]);
+        if (s < KSV) dpacc[j] = mfma16<EL>(o1, doreg[s < KSV ? s : 0], dpacc[j]);
       } else {
         const int v = u - 2 * NA, j = v / NB, t = (v % NB) / NDB, db = v % NDB;
 #pragma unroll
@@ -1002,6 +1024,14 @@ struct DqKernel {
         for (int q = 0; q < 8; ++q)
           if (pair_at(q, v, span)) pair<MASK>(sacc[j], dpacc[j], q >> 2, q & 3, mlo[j], mhi[j], ds[j], k);
       }
+    };
+    if constexpr (D != DV) {
+      // the 48-unit stream of head dim 192 exceeds the unroller's threshold:
+      // issue it with compile-time unit indices
+      static_for<0, NU>([&](auto uc) __attribute__((always_inline)) { unit_body(decltype(uc)::value); });
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) unit_body(u);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1012,19 +1042,20 @@ struct DqKernel {
 // with dS carried as a hi/lo pair).
 template <int D, int ACT, bool SPLIT>
 constexpr int dq_occupancy() {
-  return (D == 128 && (ACT == ACT_GELU || (SPLIT && ACT == ACT_SILU))) ? 1 : 2;
+  return D > 128 || (D == 128 && (ACT == ACT_GELU || (SPLIT && ACT == ACT_SILU))) ? 1 : 2;
 }
 
-template <int D, int ACT, int EL, bool SPLIT>
+template <int D, int ACT, int EL, bool SPLIT, int DV = D>
 __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd_dq_kernel(const BwdArgs a) {
-  using K = DqKernel<D, ACT, EL, SPLIT>;
+  using K = DqKernel<D, ACT, EL, SPLIT, DV>;
   constexpr int BM = kBwdBM;
-  constexpr int BN = K::BN, NKB = K::NKB, KS = K::KS, NDB = K::NDB, ROWB = K::ROWB;
-  constexpr int TB = BN * ROWB;
+  constexpr int BN = K::BN, NKB = K::NKB, KS = K::KS, KSV = K::KSV, NDB = K::NDB, ROWB = K::ROWB;
+  constexpr int ROWBV = K::ROWBV;
+  constexpr int TB = BN * ROWB, TBV = BN * ROWBV;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TBV];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TBV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1052,32 +1083,35 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
   const int jlo = a.wl >= 0 ? qi + off - a.wl : 0;
   const int jhi = min(lk - 1, a.wr >= 0 ? qi + off + a.wr : lk - 1);
 
-  const long q_ld = (long)a.hq * D;
-  u32x4 qreg[KS], doreg[KS];
+  const long q_ld = (long)a.hq * D, do_ld = (long)a.hq * DV;
+  u32x4 qreg[KS], doreg[KSV];
   {
-    const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow;
-    const uint16_t* dp = static_cast<const uint16_t*>(a.dout) + qrow;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
+    const uint16_t* dp =
+        static_cast<const uint16_t*>(a.dout) + (long)(qs + min(qi, lq - 1)) * do_ld + h * DV + hf * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
-      doreg[s] = load16_or_zero(dp + s * 16, qi < lq);
-    }
+    for (int s = 0; s < KS; ++s) qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
+#pragma unroll
+    for (int s = 0; s < KSV; ++s) doreg[s] = load16_or_zero(dp + s * 16, qi < lq);
   }
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
   const TileOffs<ROWB> loffs = TileOffs<ROWB>::make(lane);
+  const TileOffs<ROWBV> loffsv = TileOffs<ROWBV>::make(lane);
+  const auto& lov = [&]() -> const auto& {
+    if constexpr (D == DV) return loffs; else return loffsv;
+  }();
 
-  const long kv_ld_b = (long)a.hkv * D * 2;
+  const long kv_ld_b = (long)a.hkv * D * 2, vv_ld_b = (long)a.hkv * DV * 2;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (long)ks * kv_ld_b + (long)g * D * 2;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (long)ks * kv_ld_b + (long)g * D * 2;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (long)ks * vv_ld_b + (long)g * DV * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld_b);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)kv_ld_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)vv_ld_b);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
     stage_tile_buf<BN, ROWB, 4, D / 8>(krs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, kl, wave, lane);
-    stage_tile_buf<BN, ROWB, 4, D / 8>(vrs, n0 * (int)kv_ld_b, (int)kv_ld_b, lk - n0, vl, wave, lane);
+    stage_tile_buf<BN, ROWBV, 4, DV / 8>(vrs, n0 * (int)vv_ld_b, (int)vv_ld_b, lk - n0, vl, wave, lane);
   };
   auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
     if (!wave_active) return;
@@ -1107,9 +1141,9 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
       }
       if (!any) continue;
       if (all_full)
-        K::template block_pair<false>(kl, vl, kb0, loffs, qreg, doreg, dqacc, mlo, mhi, a.act);
+        K::template block_pair<false>(kl, vl, kb0, loffs, lov, qreg, doreg, dqacc, mlo, mhi, a.act);
       else
-        K::template block_pair<true>(kl, vl, kb0, loffs, qreg, doreg, dqacc, mlo, mhi, a.act);
+        K::template block_pair<true>(kl, vl, kb0, loffs, lov, qreg, doreg, dqacc, mlo, mhi, a.act);
     }
   };
 
@@ -1203,13 +1237,16 @@ GDPA_BWDF_EXTERN(EL_F16, 96)
 GDPA_BWDF_EXTERN(EL_F16, 128)
 #undef GDPA_BWDF_EXTERN
 
-template <int D, int EL, bool SPLIT_KV, bool SPLIT_Q>
+template <int D, int EL, bool SPLIT_KV, bool SPLIT_Q, int DV = D>
 static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, bool fused,
                                 hipStream_t stream) {
   if (fused) {
-    // dQ accumulated in the dK/dV pass
+    // dQ accumulated in the dK/dV pass (equal head dims only)
     if (!want_dq || !want_dkv) return hipErrorInvalidValue;
-    return launch_bwd_fused_ed<EL, D>(a, act_kind, stream);
+    if constexpr (D == DV)
+      return launch_bwd_fused_ed<EL, D>(a, act_kind, stream);
+    else
+      return hipErrorInvalidValue;
   }
   // dK/dV work queue: as many workgroups as are resident at once
   const bool queue = a.counters != nullptr;
@@ -1220,12 +1257,12 @@ static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bo
 #define GDPA_BWD_CASE(K)                                                                                       \
   case K:                                                                                                      \
     if (grid_kv != 0)                                                                                          \
-      hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K, EL, SPLIT_KV>),                                               \
+      hipLaunchKernelGGL((gdpa_bwd_dkdv_kernel<D, K, EL, SPLIT_KV, DV>),                                           \
                          dim3((unsigned)(grid_kv > 0 ? grid_kv                                                 \
                                                      : queue_grid(a.ncu, dkdv_occupancy<D, K, SPLIT_KV>()))), \
                          blk, 0, stream, a);                                                                   \
     if (grid_q > 0)                                                                                            \
-      hipLaunchKernelGGL((gdpa_bwd_dq_kernel<D, K, EL, SPLIT_Q>), dim3((unsigned)grid_q), blk, 0, stream, a);     \
+      hipLaunchKernelGGL((gdpa_bwd_dq_kernel<D, K, EL, SPLIT_Q, DV>), dim3((unsigned)grid_q), blk, 0, stream, a); \
     break;
     GDPA_BWD_CASE(ACT_IDENTITY)
     GDPA_BWD_CASE(ACT_GELU)
@@ -1242,37 +1279,39 @@ static hipError_t launch_bwd_ds(const BwdArgs& a, int act_kind, bool want_dq, bo
   return hipGetLastError();
 }
 
-template <int D, int EL>
+template <int D, int EL, int DV = D>
 static hipError_t launch_bwd_d(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, bool fused,
                                hipStream_t stream) {
   // fp16 never splits P or dS (the host keeps a single word within tolerance)
   if constexpr (EL == EL_F16) {
     if (a.kvsplit || a.dsplit) return hipErrorInvalidValue;
-    return launch_bwd_ds<D, EL, false, false>(a, act_kind, want_dq, want_dkv, fused, stream);
+    return launch_bwd_ds<D, EL, false, false, DV>(a, act_kind, want_dq, want_dkv, fused, stream);
   }
   if (a.kvsplit)
-    return a.dsplit ? launch_bwd_ds<D, EL, true, true>(a, act_kind, want_dq, want_dkv, fused, stream)
-                    : launch_bwd_ds<D, EL, true, false>(a, act_kind, want_dq, want_dkv, fused, stream);
-  return a.dsplit ? launch_bwd_ds<D, EL, false, true>(a, act_kind, want_dq, want_dkv, fused, stream)
-                  : launch_bwd_ds<D, EL, false, false>(a, act_kind, want_dq, want_dkv, fused, stream);
+    return a.dsplit ? launch_bwd_ds<D, EL, true, true, DV>(a, act_kind, want_dq, want_dkv, fused, stream)
+                    : launch_bwd_ds<D, EL, true, false, DV>(a, act_kind, want_dq, want_dkv, fused, stream);
+  return a.dsplit ? launch_bwd_ds<D, EL, false, true, DV>(a, act_kind, want_dq, want_dkv, fused, stream)
+                  : launch_bwd_ds<D, EL, false, false, DV>(a, act_kind, want_dq, want_dkv, fused, stream);
 }
 
-// Backward launches of one input element kind and head dim.  Each pair is
-// instantiated in its own translation unit (gdpa_bwd_<type>_<dim>.hip), so
+// Backward launches of one input element kind and (Q/K, V) head dims.  Each
+// is instantiated in its own translation unit (gdpa_bwd_<type>_<dim>.hip), so
 // the library's kernels compile in parallel; gdpa_bwd.hip dispatches.
-template <int EL, int D>
+template <int EL, int D, int DV = D>
 hipError_t launch_bwd_ed(const BwdArgs& a, int act_kind, bool want_dq, bool want_dkv, bool fused,
                          hipStream_t stream) {
-  return launch_bwd_d<D, EL>(a, act_kind, want_dq, want_dkv, fused, stream);
+  return launch_bwd_d<D, EL, DV>(a, act_kind, want_dq, want_dkv, fused, stream);
 }
-#define GDPA_BWD_EXTERN(EL, D)                                                                                \
-  extern template hipError_t launch_bwd_ed<EL, D>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
-GDPA_BWD_EXTERN(EL_BF16, 64)
-GDPA_BWD_EXTERN(EL_BF16, 96)
-GDPA_BWD_EXTERN(EL_BF16, 128)
-GDPA_BWD_EXTERN(EL_F16, 64)
-GDPA_BWD_EXTERN(EL_F16, 96)
-GDPA_BWD_EXTERN(EL_F16, 128)
+#define GDPA_BWD_EXTERN(EL, D, DV)                                                                            \
+  extern template hipError_t launch_bwd_ed<EL, D, DV>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
+GDPA_BWD_EXTERN(EL_BF16, 64, 64)
+GDPA_BWD_EXTERN(EL_BF16, 96, 96)
+GDPA_BWD_EXTERN(EL_BF16, 128, 128)
+GDPA_BWD_EXTERN(EL_BF16, 192, 128)
+GDPA_BWD_EXTERN(EL_F16, 64, 64)
+GDPA_BWD_EXTERN(EL_F16, 96, 96)
+GDPA_BWD_EXTERN(EL_F16, 128, 128)
+GDPA_BWD_EXTERN(EL_F16, 192, 128)
 #undef GDPA_BWD_EXTERN
 
 }  // namespace gdpa

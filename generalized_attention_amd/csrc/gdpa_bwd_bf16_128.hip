@@ -3,6 +3,6 @@
 
 namespace gdpa {
 
-template hipError_t launch_bwd_ed<EL_BF16, 128>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
+template hipError_t launch_bwd_ed<EL_BF16, 128, 128>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
 
 }  // namespace gdpa

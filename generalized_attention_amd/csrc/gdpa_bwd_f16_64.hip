@@ -3,6 +3,6 @@
 
 namespace gdpa {
 
-template hipError_t launch_bwd_ed<EL_F16, 64>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
+template hipError_t launch_bwd_ed<EL_F16, 64, 64>(const BwdArgs&, int, bool, bool, bool, hipStream_t);
 
 }  // namespace gdpa

@@ -161,7 +161,9 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
  * the products (the README lists FP8 as forward-only, so an FP8 in_dtype
  * returns GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout;
  * all three are written in grad_dtype (GDPA_DTYPE_FP32, GDPA_DTYPE_BF16 or
- * GDPA_DTYPE_FP16).  head_dim_v must equal head_dim (64, 96 or 128).
+ * GDPA_DTYPE_FP16).  Head dims as in the forward: (64, 64), (96, 96),
+ * (128, 128) or (192, 128) (dv then has v's 128 columns; dq and dk q's and
+ * k's 192).
  * dQ sums the partial products of all key blocks in a fixed order, so results
  * are bitwise reproducible (an fp32 reduction inside the workspace, or inside
  * dq itself when grad_dtype is FP32: dq is then written more than once

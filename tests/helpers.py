@@ -93,9 +93,10 @@ def run_backward(g, bt: gi.Batch, dev=None, grad_dtype=None, poison=True):
                           bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, **kw)
     else:
         B, H, G, D = wl.batch, wl.heads_q, wl.heads_kv, wl.head_dim
+        DV = bt.v.shape[2]
         Lq, Lk = int(bt.seqlens_q[0]), int(bt.seqlens_k[0])
-        g.gdpa_bwd(dev["q"].view(B, Lq, H, D), dev["k"].view(B, Lk, G, D), dev["v"].view(B, Lk, G, D),
-                   dev["do"].view(B, Lq, H, D), dq.view(B, Lq, H, D), dk.view(B, Lk, G, D), dv.view(B, Lk, G, D),
+        g.gdpa_bwd(dev["q"].view(B, Lq, H, D), dev["k"].view(B, Lk, G, D), dev["v"].view(B, Lk, G, DV),
+                   dev["do"].view(B, Lq, H, DV), dq.view(B, Lq, H, D), dk.view(B, Lk, G, D), dv.view(B, Lk, G, DV),
                    wl.scale, **kw)
     return dq, dk, dv
 

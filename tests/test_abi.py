@@ -153,7 +153,9 @@ def test_varlen_fwd_validation(lib, over, expect):
 @pytest.mark.parametrize("over,expect", [
     (dict(ind=2), UNSUPPORTED),              # FP8 is forward-only (README "Features")
     (dict(ind=1, B=0), OK),                  # fp16 inputs
-    (dict(D=192, Dv=128), UNSUPPORTED),      # (192, 128) is forward only
+    (dict(D=192, Dv=128, B=0), OK),          # the README's (192, 128)
+    (dict(D=192, Dv=192), UNSUPPORTED),
+    (dict(D=192, Dv=128, ind=2), UNSUPPORTED),   # FP8 is forward-only
     (dict(ind=3), INVALID),                  # fp32 inputs
     (dict(gd=1, B=0), OK),                   # fp16 gradients
     (dict(gd=2), INVALID),

@@ -537,11 +537,32 @@ def test_head_dims_192_128_fp16_and_fixed_length(g):
     check_forward(g, gi.make_batch(wl))
 
 
-def test_head_dims_192_128_backward_is_unsupported(g):
-    bt = gi.make_batch(_wl(act="silu", head_dim=192, head_dim_v=128), seqlens_q=[40], seqlens_k=[40])
-    with pytest.raises(g.GDPAError) as e:
-        run_backward(g, bt)
-    assert e.value.status == 2
+@pytest.mark.parametrize("act", ["identity", "fast_gelu", "silu", "relu2", "leaky_relu", "gelu", "hardswish"])
+def test_head_dims_192_128_backward(g, act):
+    # S and dK over the 192 head dims of Q and K, dP and dV over V's 128:
+    # jagged lengths with empty, one-token and ragged sequences, GQA 4:2
+    bt = gi.make_batch(_wl(act=act, head_dim=192, head_dim_v=128, act_param=0.05), seqlens_q=FP16_LENS,
+                       seqlens_k=FP16_LENS)
+    check_backward(g, bt)
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 4])
+def test_head_dims_192_128_backward_masks_gqa(g, case):
+    mask, wl_, wr_, lq, lk = MASK_CASES[case]
+    wl = _wl(act="silu", head_dim=192, head_dim_v=128, mask=mask, window_left=wl_, window_right=wr_,
+             batch=len(lq), heads_q=8, heads_kv=2)
+    check_backward(g, gi.make_batch(wl, seqlens_q=lq, seqlens_k=lk))
+
+
+def test_head_dims_192_128_backward_fp16_short_kv_and_fixed_length(g):
+    # fp16 inputs; few keys (dS carried as hi + lo for dQ, still the separate
+    # dQ kernel: the fused pass needs equal head dims); fixed-length entry point
+    check_backward(g, gi.make_batch(_wl(act="fast_gelu", head_dim=192, head_dim_v=128, fp16=True),
+                                    seqlens_q=[1100, 33], seqlens_k=[1100, 33]))
+    check_backward(g, gi.make_batch(_wl(act="relu2", head_dim=192, head_dim_v=128), seqlens_q=[300, 50, 7],
+                                    seqlens_k=[64, 100, 1]))
+    wl = _wl(act="silu", head_dim=192, head_dim_v=128, varlen=False, batch=2, lq_range=(300, 300))
+    check_backward(g, gi.make_batch(wl))
 
 
 # ---------------------------------------- short key/value: hi/lo-split dS and P

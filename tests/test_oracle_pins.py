@@ -412,6 +412,35 @@ def test_backward_matches_finite_differences(case, name):
         assert np.allclose(grad, fd, rtol=1e-6, atol=1e-6), (name, np.max(np.abs(grad - fd)))
 
 
+@pytest.mark.parametrize("name", ["silu", "fast_gelu", "relu2"])
+def test_backward_distinct_value_head_dim_matches_finite_differences(name):
+    # V and dO narrower than Q and K (the pages' head dims (192, 128)), here
+    # 5 and 3: dP contracts over V's head dim, S over Q's
+    rng = np.random.default_rng(321)
+    lq, lk, hq, hkv = [4, 2], [3, 5], 2, 1
+    q, k = _rand(rng, sum(lq), hq, 5), _rand(rng, sum(lk), hkv, 5)
+    v, G = _rand(rng, sum(lk), hkv, 3), _rand(rng, sum(lq), hq, 3)
+    cq, ck = _cu(lq), _cu(lk)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(gdpa_forward(qq, kk, vv, cq, ck, 0.7, name, act_param=0.05) * G))
+
+    dq, dk, dv = gdpa_backward(q, k, v, G, cq, ck, 0.7, name, act_param=0.05)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss(q, k, v)
+            arr[idx] = old - h
+            lm = loss(q, k, v)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(grad, fd, rtol=1e-6, atol=1e-6), (name, np.max(np.abs(grad - fd)))
+
+
 def test_backward_identity_closed_forms():
     # identity, no mask: dV = scale K (Q^T dO), dQ = scale dO (V^T K), dK = scale V (dO^T Q)
     rng = np.random.default_rng(16)
