@@ -45,6 +45,7 @@ class Workload:
     window_left: int = -1    # -1 = unbounded
     window_right: int = -1
     fp8_qk: bool = False
+    mx_qk: bool = False               # Q and K in MXFP8 (E4M3 elements, E8M0 scale per 32 head dims)
     fp16: bool = False       # fp16 Q/K/V/dO instead of bf16
     head_dim_v: Optional[int] = None  # of V and O (None: head_dim)
     backward: bool = False
@@ -115,6 +116,26 @@ def quantize_e4m3(x: np.ndarray):
     return codes, float(scale)
 
 
+def quantize_mxfp8(x: np.ndarray, block: int = 32):
+    """OCP MX quantisation to MXFP8 (E4M3 elements) along the last axis: for
+    every block of 32 elements, shared exponent e = floor(log2(max|x|)) - 8
+    (8 = the largest E4M3 exponent; 0 for an all-zero block), clamped to
+    [-127, 127], scale code e + 127 (E8M0), element code = RNE(x / 2^e)
+    saturated to +-448 (torch's float8_e4m3fn cast).
+
+    Returns (uint8 codes of x's shape, uint8 scale codes [..., D / block])."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    blocks = x.reshape(*x.shape[:-1], x.shape[-1] // block, block)
+    amax = np.max(np.abs(blocks), axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    y = blocks / np.exp2(e.astype(np.float64))[..., None]
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).clamp_(-448.0, 448.0)
+    codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(x.shape).copy()
+    return codes, (e + 127).astype(np.uint8)
+
+
 @dataclasses.dataclass
 class Batch:
     """One drawn problem instance.  Tensors are storage-format numpy arrays."""
@@ -129,6 +150,8 @@ class Batch:
     do: Optional[np.ndarray]  # uint16, same format as v                     [total_q, Hq, D]
     q_scale: float = 1.0      # per-tensor scale of q codes (fp8 only)
     k_scale: float = 1.0
+    q_mx: Optional[np.ndarray] = None  # uint8 E8M0 block scales of q codes [total_q, Hq, D / 32] (MXFP8)
+    k_mx: Optional[np.ndarray] = None  #                          of k codes [total_k, Hkv, D / 32]
 
     @property
     def max_seqlen_q(self) -> int:
@@ -185,15 +208,19 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool]
     want_do = wl.backward if with_do is None else with_do
     dof = rng.standard_normal((tq, H, DV), dtype=np.float32) if want_do else None
     qs = ks = 1.0
+    qmx = kmx = None
     enc = f32_to_f16_bits if wl.fp16 else f32_to_bf16_bits
-    if wl.fp8_qk:
+    if wl.mx_qk:
+        q, qmx = quantize_mxfp8(qf)
+        k, kmx = quantize_mxfp8(kf)
+    elif wl.fp8_qk:
         q, qs = quantize_e4m3(qf)
         k, ks = quantize_e4m3(kf)
     else:
         q, k = enc(qf), enc(kf)
     v = enc(vf)
     do = enc(dof) if dof is not None else None
-    return Batch(wl, lq, lk, cu_q, cu_k, q, k, v, do, qs, ks)
+    return Batch(wl, lq, lk, cu_q, cu_k, q, k, v, do, qs, ks, qmx, kmx)
 
 
 def small_variant(wl: Workload, batch: int, lq_range, lk_range=None, **kw) -> Workload:

@@ -20,7 +20,7 @@ Every function is pinned by tests under tests/ (test_oracle_*.py) against
 closed forms, library routines, brute force and finite differences.
 """
 from .activations import act, act_grad, ACT_NAMES
-from .formats import decode_bf16, decode_e4m3, decode_f16
+from .formats import decode_bf16, decode_e4m3, decode_e8m0, decode_f16, decode_mxfp8
 from .gdpa import (
     allowed_mask,
     gdpa_forward,
@@ -31,7 +31,8 @@ from .gdpa import (
 )
 
 __all__ = [
-    "act", "act_grad", "ACT_NAMES", "decode_bf16", "decode_e4m3", "decode_f16", "allowed_mask",
+    "act", "act_grad", "ACT_NAMES", "decode_bf16", "decode_e4m3", "decode_e8m0", "decode_f16", "decode_mxfp8",
+    "allowed_mask",
     "gdpa_forward", "gdpa_backward", "gdpa_forward_rows", "gdpa_backward_q_rows",
     "gdpa_backward_k_rows",
 ]

@@ -13,6 +13,13 @@ Test infrastructure (see the package docstring).
   The GDPA README ("Features": "FP8 (E4M3) forward") names the format; it does
   not state the scaling.  Reading: one fp32 scale per tensor, so the value a
   code stands for is decode(code) * scale.
+* E8M0: the scale type of the OCP Microscaling Formats (MX) specification:
+  8 exponent bits, no sign or mantissa, value 2^(code - 127); code 255 is NaN.
+* MXFP8 (E4M3): the OCP MX format built on E4M3 elements: every block of 32
+  consecutive elements shares one E8M0 scale, and an element stands for
+  decode_e4m3(code) * 2^(scale - 127).  The GDPA README ("Features") lists
+  MXFP8 among its coming formats without a layout; reading: blocks run along
+  the head dim (the contraction axis of Q K^T), scales stored [..., D / 32].
 """
 from __future__ import annotations
 
@@ -46,3 +53,18 @@ def decode_e4m3(codes, scale: float = 1.0) -> np.ndarray:
     mag = np.where(e == 0, sub, normal)
     mag = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
     return sign * mag * float(scale)
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """E8M0 scale codes -> 2^(code - 127) (fp64); code 255 -> NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c.astype(np.float64) - 127.0))
+
+
+def decode_mxfp8(codes, scales, block: int = 32) -> np.ndarray:
+    """MXFP8 E4M3 values (fp64): codes [..., D] (uint8 E4M3), scales
+    [..., D / block] (uint8 E8M0); element d takes the scale of block d // block."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    assert codes.shape[-1] == scales.shape[-1] * block and codes.shape[:-1] == scales.shape[:-1]
+    return decode_e4m3(codes) * np.repeat(decode_e8m0(scales), block, axis=-1)
