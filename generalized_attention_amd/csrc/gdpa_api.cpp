@@ -99,6 +99,7 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
 // checks its combination here, before the schedule kernel or any other HIP
 // call is queued.
 bool fwd_built(int in_kind, int32_t d, int32_t dv) {
+  if (in_kind == gdpa::EL_MX8) return d == dv && (d == 64 || d == 128);  // 32-wide blocks on the K = 64 MFMA
   if (d == dv && (d == 64 || d == 96 || d == 128)) return true;
   return in_kind != gdpa::EL_FP8 && d == 192 && dv == 128;
 }
@@ -316,23 +317,29 @@ gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, int32_t b
 gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_q,
                       const int32_t* cu_k, const Common& c, float scale, float act_param,
                       int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype, float q_descale,
-                      float k_descale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP16 && qk_dtype != GDPA_DTYPE_FP8_E4M3)
+                      float k_descale, void* workspace, size_t workspace_bytes, void* stream,
+                      const uint8_t* q_mx = nullptr, const uint8_t* k_mx = nullptr) {
+  if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP16 && qk_dtype != GDPA_DTYPE_FP8_E4M3 &&
+      qk_dtype != GDPA_DTYPE_MXFP8_E4M3)
     return GDPA_ERR_INVALID_ARG;
+  // MXFP8 Q/K carry their scales in q_mx / k_mx (and only they do)
+  const bool mx = qk_dtype == GDPA_DTYPE_MXFP8_E4M3;
+  if (mx != (q_mx != nullptr || k_mx != nullptr) && !(mx && c.batch == 0)) return GDPA_ERR_INVALID_ARG;
   if (v_dtype != GDPA_DTYPE_BF16 && v_dtype != GDPA_DTYPE_FP16)
     return v_dtype == GDPA_DTYPE_FP8_E4M3 ? GDPA_ERR_UNSUPPORTED : GDPA_ERR_INVALID_ARG;
   const int out_kind = out_kind_of(out_dtype);
   if (out_kind < 0) return GDPA_ERR_INVALID_ARG;
   // bf16 Q/K with bf16 V, fp16 with fp16, or FP8 Q/K with bf16 V (P takes V's type).
-  const bool fp8 = qk_dtype == GDPA_DTYPE_FP8_E4M3;
+  const bool fp8 = qk_dtype == GDPA_DTYPE_FP8_E4M3 || mx;
   const bool f16 = v_dtype == GDPA_DTYPE_FP16;
   if (f16 != (qk_dtype == GDPA_DTYPE_FP16)) return GDPA_ERR_UNSUPPORTED;
-  const int in_kind = fp8 ? gdpa::EL_FP8 : f16 ? gdpa::EL_F16 : gdpa::EL_BF16;
+  const int in_kind = mx ? gdpa::EL_MX8 : fp8 ? gdpa::EL_FP8 : f16 ? gdpa::EL_F16 : gdpa::EL_BF16;
   if (fp8 && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
   if (!fwd_built(in_kind, c.d, c.dv)) return GDPA_ERR_UNSUPPORTED;
   if (c.batch == 0 || c.total_q == 0) return GDPA_OK;
   if (q == nullptr || o == nullptr) return GDPA_ERR_INVALID_ARG;
   if (c.total_k > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (mx && (q_mx == nullptr || (c.total_k > 0 && k_mx == nullptr))) return GDPA_ERR_INVALID_ARG;
   const int64_t mblocks = ((int64_t)c.max_lq + gdpa::kFwdBM - 1) / gdpa::kFwdBM;
   if (mblocks == 0) return GDPA_OK;
 
@@ -354,6 +361,8 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   a.wl = c.wl;
   a.wr = c.wr;
   a.out_kind = out_kind;
+  a.q_mx = q_mx;
+  a.k_mx = k_mx;
   // When an output row sums at most kFewTerms products, the bf16 rounding of P
   // no longer averages out; P is then carried as hi + lo (such short rows are
   // bandwidth-bound, so the second MFMA is free).  fp16's 3 extra mantissa
@@ -560,6 +569,25 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
   if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
   return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, qk_dtype, v_dtype, out_dtype,
                  q_descale, k_descale, workspace, workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                    const void* v, void* o, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
+                                    int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                    int32_t act, float act_param, int32_t out_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Common c;
+  gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                  head_dim, head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+  if (st != GDPA_OK) return st;
+  if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (batch > 0 && total_q > 0 && (q_scale == nullptr || (total_k > 0 && k_scale == nullptr)))
+    return GDPA_ERR_INVALID_ARG;
+  return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, GDPA_DTYPE_MXFP8_E4M3,
+                 GDPA_DTYPE_BF16, out_dtype, 1.0f, 1.0f, workspace, workspace_bytes, stream,
+                 static_cast<const uint8_t*>(q_scale), static_cast<const uint8_t*>(k_scale));
 }
 
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,

@@ -51,6 +51,19 @@ __device__ __forceinline__ f32x16 mfma_fp8_k64(const u32x4& a0, const u32x4& a1,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same with E8M0 block scales (the OCP MX formats), sa and sb from byte 0
+// of the scale operands.  The 64 k-values of a row form two blocks of 32: the
+// first 16 bytes of lane halves 0 and 1 (scaled by 2^(s - 127) of the half-0
+// lane: lane i for A row i, lane j for B column j) and their last 16 bytes
+// (scaled by the half-1 lane's, i + 32 or j + 32); measured on gfx950.
+__device__ __forceinline__ f32x16 mfma_fp8_k64_scaled(const u32x4& a0, const u32x4& a1, const u32x4& b0,
+                                                      const u32x4& b1, const f32x16& c, uint32_t sa, uint32_t sb) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -33,11 +33,24 @@
 
 namespace gdpa {
 
+// The N E8M0 scale bytes of one MXFP8 row (N = 2 or 4; the row's scales start
+// at a multiple of N bytes), in one 32-bit value, byte b for head-dim block b.
+template <int N>
+__device__ __forceinline__ uint32_t load_scales(const uint8_t* p) {
+  static_assert(N == 2 || N == 4, "head dims 64 and 128");
+  if constexpr (N == 4)
+    return *reinterpret_cast<const uint32_t*>(p);
+  else
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
 // D: head dim of Q and K; DV: head dim of V and O.
 template <int D, int ACT, int IN, bool PSPLIT, int NW, int DV = D>
 struct FwdKernel {
-  static constexpr bool FP8 = IN == EL_FP8;
+  static constexpr bool MX = IN == EL_MX8;    // MXFP8 Q/K: E4M3 codes with an E8M0 scale per 32 head dims
+  static constexpr bool FP8 = IN == EL_FP8 || MX;
   static constexpr int EL = IN == EL_F16 ? EL_F16 : EL_BF16;  // V, P (and 16-bit Q, K)
+  static_assert(!MX || D % 64 == 0, "MXFP8: every head-dim block of 32 on the K = 64 MFMA");
   static constexpr int BM = 32 * NW;
   static constexpr int DPK = lds_dim(D);  // head dims of the LDS rows of K and V
   static constexpr int DPV = lds_dim(DV);
@@ -90,8 +103,14 @@ struct FwdKernel {
       if constexpr (FP8) {
         const int row = kb * 32 + (lane & 31);
         if (s < NK64) {
-          const int c = 4 * s + 2 * (lane >> 5);
-          hi = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c + 1));
+          // FP8: bytes [64 s + 32 h, +32) in lane half h.  MXFP8: the block
+          // scales apply per 32 k-values made of the first 16 bytes of both
+          // lane halves (block 2 s, scale from half 0) and their last 16 bytes
+          // (block 2 s + 1, from half 1), so half h holds head dims
+          // [64 s + 16 h, +16) and [64 s + 32 + 16 h, +16)
+          const int h = lane >> 5;
+          const int c = MX ? 4 * s + h : 4 * s + 2 * h;
+          hi = *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, MX ? c + 2 : c + 1));
           return *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(row, c));
         }
         const u32x2 v = *reinterpret_cast<const u32x2*>(kl + lds_off<KROWB>(row, 4 * NK64 + s - NK64) +
@@ -114,7 +133,8 @@ struct FwdKernel {
   template <bool MASK>
   static __device__ __forceinline__ void block_pair(const uint8_t* kl, const uint8_t* vl, int kb0, const KOffs& lo,
                                                     const VOffs& vo, int lane, const u32x4* qreg, const u32x2* qreg8, f32x16* oacc,
-                                                    const int* mlo, const int* mhi, const ActConsts& k) {
+                                                    const int* mlo, const int* mhi, const ActConsts& k,
+                                                    const uint32_t* ksc = nullptr, uint32_t qsc = 0) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     u32x4 p[2][NP][2];
     u32x4 ring[PREF + 1], ring_hi[PREF + 1];  // ring_hi: second 16 bytes of K = 64 FP8 units
@@ -136,7 +156,12 @@ struct FwdKernel {
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
         if constexpr (FP8) {
-          if (s < NK64)
+          if constexpr (MX) {
+            // lane half h supplies the scale of head-dim block 2 s + h (its key's / query's)
+            const int sh = 16 * s + 8 * (lane >> 5);
+            sacc[j] = mfma_fp8_k64_scaled(op, ring_hi[u % (PREF + 1)], qreg[2 * s], qreg[2 * s + 1], sacc[j],
+                                          (ksc[j] >> sh) & 0xffu, (qsc >> sh) & 0xffu);
+          } else if (s < NK64)
             sacc[j] = mfma_fp8_k64(op, ring_hi[u % (PREF + 1)], qreg[2 * s], qreg[2 * s + 1], sacc[j]);
           else
             sacc[j] = mfma_fp8(u32x2{op[0], op[1]}, qreg8[s - NK64], sacc[j]);
@@ -221,8 +246,10 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
       const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8);
 #pragma unroll
       for (int s = 0; s < K::NK64; ++s) {
-        qreg[2 * s] = load16_or_zero(qp + 64 * s + 32 * hf, qi < lq);
-        qreg[2 * s + 1] = load16_or_zero(qp + 64 * s + 32 * hf + 16, qi < lq);
+        // the same byte layout as the K operand (see load_unit)
+        const int o0 = K::MX ? 64 * s + 16 * hf : 64 * s + 32 * hf, o1 = K::MX ? o0 + 32 : o0 + 16;
+        qreg[2 * s] = load16_or_zero(qp + o0, qi < lq);
+        qreg[2 * s + 1] = load16_or_zero(qp + o1, qi < lq);
       }
 #pragma unroll
       for (int t = 0; t < K::NK16; ++t) qreg8[t] = load8_or_zero(qp + 64 * K::NK64 + 16 * t + 8 * hf, qi < lq);
@@ -232,6 +259,10 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
       for (int s = 0; s < KS; ++s) qreg[s] = load16_or_zero(qp + s * 16, qi < lq);
     }
   }
+
+  // MXFP8: the E8M0 scales of this lane's query (byte b: head-dim block b)
+  uint32_t qsc = 0;
+  if constexpr (K::MX) qsc = load_scales<D / 32>(a.q_mx + ((long)(qs + min(qi, lq - 1)) * a.hq + h) * (D / 32));
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -283,10 +314,19 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
         mhi[j] = jhi - (b_lo + hf * 4);
       }
       if (!any) continue;
+      // MXFP8: the E8M0 scales of this lane's key in each of the two blocks
+      uint32_t ksc[2] = {0u, 0u};
+      if constexpr (K::MX) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int key = min(n0 + (kb0 + j) * 32 + (lane & 31), lk - 1);
+          ksc[j] = load_scales<D / 32>(a.k_mx + ((long)(ks + key) * a.hkv + g) * (D / 32));
+        }
+      }
       if (all_full)
-        K::template block_pair<false>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
+        K::template block_pair<false>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act, ksc, qsc);
       else
-        K::template block_pair<true>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act);
+        K::template block_pair<true>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act, ksc, qsc);
     }
   };
 
@@ -360,14 +400,20 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
 // (128, 128), and (192, 128) for 16-bit inputs.
 template <int IN>
 static hipError_t launch_fwd_in(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream) {
-  if (head_dim == head_dim_v) {
-    if (head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
-    if (head_dim == 96) return launch_fwd_d<96, IN>(a, act_kind, stream);
-    if (head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
+  if constexpr (IN == EL_MX8) {
+    if (head_dim == head_dim_v && head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
+    if (head_dim == head_dim_v && head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
+    return hipErrorInvalidValue;
+  } else {
+    if (head_dim == head_dim_v) {
+      if (head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
+      if (head_dim == 96) return launch_fwd_d<96, IN>(a, act_kind, stream);
+      if (head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
+    }
+    if constexpr (IN != EL_FP8)
+      if (head_dim == 192 && head_dim_v == 128) return launch_fwd_d<192, IN, 128>(a, act_kind, stream);
+    return hipErrorInvalidValue;
   }
-  if constexpr (IN != EL_FP8)
-    if (head_dim == 192 && head_dim_v == 128) return launch_fwd_d<192, IN, 128>(a, act_kind, stream);
-  return hipErrorInvalidValue;
 }
 
 }  // namespace gdpa

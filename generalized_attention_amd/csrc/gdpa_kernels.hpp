@@ -10,7 +10,7 @@ namespace gdpa {
 // FAST_SILU -> SILU).  Values match gdpa_act_t.
 // Element types of the MFMA inputs: bf16 or fp16 Q, K, V (and dO), or FP8
 // E4M3 Q and K with bf16 V (forward only).
-enum ElemKind : int { EL_BF16 = 0, EL_F16 = 1, EL_FP8 = 2 };
+enum ElemKind : int { EL_BF16 = 0, EL_F16 = 1, EL_FP8 = 2, EL_MX8 = 3 };  // EL_MX8: MXFP8 (E4M3, E8M0 per 32)
 // Output element types.
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
@@ -61,6 +61,8 @@ struct FwdArgs {
   int32_t out_kind;   // OUT_F32, OUT_BF16 or OUT_F16
   int32_t psplit;     // 1: P carried as a 16-bit hi/lo pair (two MFMAs for P V)
   const int32_t* perm;  // sequences in processing order (longest first), or nullptr
+  const uint8_t* q_mx;  // MXFP8: E8M0 scales of q [total_q, Hq, D / 32] (else nullptr)
+  const uint8_t* k_mx;  //        and of k [total_k, Hkv, D / 32]
 };
 
 // One backward launch (both kernels take the same block).

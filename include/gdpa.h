@@ -110,7 +110,8 @@ typedef enum {
   GDPA_DTYPE_BF16 = 0,
   GDPA_DTYPE_FP16 = 1,      /* IEEE binary16 */
   GDPA_DTYPE_FP8_E4M3 = 2,  /* OCP E4M3 codes, forward q/k only */
-  GDPA_DTYPE_FP32 = 3       /* outputs only */
+  GDPA_DTYPE_FP32 = 3,      /* outputs only */
+  GDPA_DTYPE_MXFP8_E4M3 = 4 /* OCP MXFP8: E4M3 codes + E8M0 scales; gdpa_varlen_fwd_mxfp8 only */
 } gdpa_dtype_t;
 
 /* ------------------------------------------------------------------ forward
@@ -154,6 +155,27 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
                               int32_t qk_dtype, int32_t v_dtype, int32_t out_dtype,
                               float q_descale, float k_descale,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Jagged forward with MXFP8 Q and K (the README's "Features" list MXFP8 among
+ * its coming datatypes; the format is the OCP Microscaling Formats
+ * specification's MXFP8 E4M3).  q [total_q, Hq, D] and k [total_k, Hkv, D]
+ * hold E4M3 codes; q_scale [total_q, Hq, D/32] and k_scale [total_k, Hkv, D/32]
+ * hold the E8M0 scale of each block of 32 consecutive head-dim elements
+ * (value 2^(byte - 127); 255 is NaN), so element d of a row stands for
+ * e4m3(code) * 2^(scale[d / 32] - 127).  v is bf16 [total_k, Hkv, D], o as in
+ * gdpa_varlen_fwd.  head_dim is 64 or 128 (else GDPA_ERR_UNSUPPORTED); the
+ * other arguments, the workspace and the errors are those of gdpa_varlen_fwd
+ * (q_scale / k_scale NULL with work to do: GDPA_ERR_INVALID_ARG).  Both score
+ * operands enter gfx950's block-scaled MFMA with their scales. */
+gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                    const void* v, void* o,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int64_t total_q, int64_t total_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                    int32_t act, float act_param, int32_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- backward
  * Gradients of L = sum(O .* dO) for the forward above.  in_dtype (q, k, v and

@@ -25,9 +25,13 @@ def to_dev(arr, dtype_name):
 
 
 def oracle_inputs(bt: gi.Batch):
-    """fp64 values the kernels consume (decoded bf16 / fp16 / E4M3 codes x scale)."""
+    """fp64 values the kernels consume (decoded bf16 / fp16 / E4M3 codes x scale
+    / MXFP8 codes x block scale)."""
     dec = oracle.decode_f16 if bt.wl.fp16 else oracle.decode_bf16
-    if bt.wl.fp8_qk:
+    if bt.wl.mx_qk:
+        q = oracle.decode_mxfp8(bt.q, bt.q_mx)
+        k = oracle.decode_mxfp8(bt.k, bt.k_mx)
+    elif bt.wl.fp8_qk:
         q = oracle.decode_e4m3(bt.q, bt.q_scale)
         k = oracle.decode_e4m3(bt.k, bt.k_scale)
     else:
@@ -46,9 +50,12 @@ def device_batch(bt: gi.Batch):
     import torch
     wl = bt.wl
     e16 = "fp16" if wl.fp16 else "bf16"
-    qk = "fp8" if wl.fp8_qk else e16
+    qk = "fp8" if (wl.fp8_qk or wl.mx_qk) else e16
     d = dict(q=to_dev(bt.q, qk), k=to_dev(bt.k, qk), v=to_dev(bt.v, e16),
              cu_q=torch.from_numpy(bt.cu_seqlens_q).cuda(), cu_k=torch.from_numpy(bt.cu_seqlens_k).cuda())
+    if wl.mx_qk:
+        d["q_mx"] = torch.from_numpy(np.ascontiguousarray(bt.q_mx)).cuda()
+        d["k_mx"] = torch.from_numpy(np.ascontiguousarray(bt.k_mx)).cuda()
     if bt.do is not None:
         d["do"] = to_dev(bt.do, e16)
     return d
@@ -66,7 +73,11 @@ def run_forward(g, bt: gi.Batch, dev=None, out_dtype=None, poison=True):
         torch.empty((tq, H, DV), dtype=out_dtype, device="cuda")
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
               window_right=wl.window_right, q_descale=bt.q_scale, k_descale=bt.k_scale)
-    if wl.varlen:
+    if wl.mx_qk:
+        kw.pop("q_descale"), kw.pop("k_descale")
+        g.gdpa_varlen_fwd_mxfp8(dev["q"], dev["q_mx"], dev["k"], dev["k_mx"], dev["v"], o, dev["cu_q"], dev["cu_k"],
+                                bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, **kw)
+    elif wl.varlen:
         g.gdpa_varlen_fwd(dev["q"], dev["k"], dev["v"], o, dev["cu_q"], dev["cu_k"], bt.max_seqlen_q,
                           bt.max_seqlen_k, wl.scale, **kw)
     else:

@@ -45,7 +45,7 @@ def _wl(**kw):
 
 def check_forward(g, bt, tol=None):
     wl = bt.wl
-    tol = tol or (TOL_FWD_FP8 if wl.fp8_qk else TOL_FWD_BF16)
+    tol = tol or (TOL_FWD_FP8 if (wl.fp8_qk or wl.mx_qk) else TOL_FWD_BF16)
     o = run_forward(g, bt).cpu().double().numpy()
     q, k, v, _ = oracle_inputs(bt)
     ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **mask_kw(wl))
@@ -563,6 +563,62 @@ def test_head_dims_192_128_backward_fp16_short_kv_and_fixed_length(g):
                                     seqlens_k=[64, 100, 1]))
     wl = _wl(act="silu", head_dim=192, head_dim_v=128, varlen=False, batch=2, lq_range=(300, 300))
     check_backward(g, gi.make_batch(wl))
+
+
+# ------------------------------------------------ MXFP8 Q/K (E8M0 block scales)
+MX_CASES = [
+    dict(act="fast_gelu"),
+    dict(act="leaky_relu", act_param=0.01, mask="window", window_left=100, window_right=0, heads_q=8, heads_kv=2),
+    dict(act="silu", mask="causal"),
+    dict(act="relu2", heads_q=4, heads_kv=1),
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(MX_CASES)))
+def test_mxfp8_forward(g, case, D):
+    # per-block E8M0 scales of Q and K (the quantiser gives every 32-element
+    # block its own exponent) enter the block-scaled MFMA; jagged lengths with
+    # empty, one-token and ragged sequences over several KV tiles
+    lens = [700, 1, 0, 300, 64, 129]
+    bt = gi.make_batch(_wl(head_dim=D, batch=len(lens), mx_qk=True, backward=False, **MX_CASES[case]),
+                       seqlens_q=lens, seqlens_k=lens)
+    # spread the block scales (a seeded offset in [-3, 3] per block): any
+    # block taking another block's scale then fails by factors of up to 2^6
+    rng = np.random.default_rng(77 + case)
+    bt = dataclasses.replace(bt, q_mx=(bt.q_mx.astype(np.int64) + rng.integers(-3, 4, bt.q_mx.shape)).astype(np.uint8),
+                             k_mx=(bt.k_mx.astype(np.int64) + rng.integers(-3, 4, bt.k_mx.shape)).astype(np.uint8))
+    assert len(np.unique(bt.q_mx)) >= 7 and len(np.unique(bt.k_mx)) >= 7
+    check_forward(g, bt)
+
+
+def test_mxfp8_scales_are_applied(g):
+    # raising every q scale by 2 and every k scale by 1 multiplies the scores
+    # by 8; checked against the oracle on the changed scales, and the output
+    # differs from the unchanged one
+    import torch
+    lens = [200, 77]
+    bt = gi.make_batch(_wl(head_dim=128, batch=2, mx_qk=True, backward=False, act="silu"), seqlens_q=lens,
+                       seqlens_k=lens)
+    o1 = run_forward(g, bt)
+    bt2 = dataclasses.replace(bt, q_mx=(bt.q_mx + 2).astype(np.uint8), k_mx=(bt.k_mx + 1).astype(np.uint8))
+    check_forward(g, bt2)
+    assert not torch.equal(o1, run_forward(g, bt2))
+
+
+def test_mxfp8_unsupported_head_dim_and_missing_scales(g):
+    import torch
+    bt = gi.make_batch(_wl(head_dim=96, batch=1, mx_qk=True, backward=False), seqlens_q=[40], seqlens_k=[40])
+    with pytest.raises(g.GDPAError) as e:
+        run_forward(g, bt)
+    assert e.value.status == 2
+    bt = gi.make_batch(_wl(head_dim=64, batch=1, mx_qk=True, backward=False), seqlens_q=[40], seqlens_k=[40])
+    dev = device_batch(bt)
+    o = torch.empty(40, 4, 64, device="cuda")
+    with pytest.raises(g.GDPAError) as e:
+        g.gdpa_varlen_fwd_mxfp8(dev["q"], None, dev["k"], dev["k_mx"], dev["v"], o, dev["cu_q"], dev["cu_k"], 40, 40,
+                                0.1)
+    assert e.value.status == 1
 
 
 # ---------------------------------------- short key/value: hi/lo-split dS and P
