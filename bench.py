@@ -440,16 +440,19 @@ def main():
         bound, achieved, peak, unit = "hbm", hbm_gbs, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", mfma_tf, BF16_PEAK_TFLOPS, "TFLOP/s"
+    # HBM bytes the counters measured for this kernel, workload and output
+    # type with the same kernel sources (profiles/traffic.json); None otherwise
     traffic, traffic_source = None, None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        ent = rec.get("kernels", {}).get(dom)
-        if (ent and rec.get("source_hash") == kernel_source_hash() and rec.get("workload") == wl.name
-                and rec.get("out_dtype", "fp32") == args.out_dtype):
-            traffic = ent["hbm_bytes_per_launch"]
-            traffic_source = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE of the same command "
-                              "and sources, scaled by the counters of a plain device copy")
+        wrec = rec.get("workloads", {}).get(wl.name, {})
+        ent = wrec.get("kernels", {}).get(dom)
+        if ent and rec.get("source_hash") == kernel_source_hash() and wrec.get("out_dtype") == args.out_dtype:
+            traffic = round(ent["hbm_bytes_per_launch"])
+            traffic_source = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE per launch of this kernel "
+                              "(bench.py, this workload, the same kernel sources), scaled by the counters of a "
+                              "plain 1 GiB device copy")
 
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
