@@ -346,12 +346,14 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hf = lane >> 5;
-  // One work item: sequence b, KV head g, key block nblk.
-  auto process = [&](int b, int g, int nblk) __attribute__((always_inline)) {
+  // One work item: sequence b, KV head g, key block nblk.  In queue mode
+  // fetch (non-null) takes the next index as the last step starts; returns
+  // whether it did (there was a step).
+  auto process = [&](int b, int g, int nblk, QueueFetch* fetch) __attribute__((always_inline)) -> bool {
   int qs, lq, ks, lk;
   seq_bounds(a, b, qs, lq, ks, lk);
   const int n0 = nblk * BNB;
-  if (n0 >= lk) return;
+  if (n0 >= lk) return false;
   const int off = lk - lq;
   const int k0w = n0 + wave * 32;
   const bool wave_active = k0w < lk;
@@ -447,17 +449,32 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
   __syncthreads();
   for (int i = 0; i < nsteps; i += 2) {
     if (i + 1 < nsteps) stage(i + 1, q_lds1, do_lds1);
+    if (fetch != nullptr && i + 1 == nsteps) fetch->issue();  // (uniform)
     compute(i, q_lds0, do_lds0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (i + 1 >= nsteps) break;
     if (i + 2 < nsteps) stage(i + 2, q_lds0, do_lds0);
+    if (fetch != nullptr && i + 2 == nsteps) fetch->issue();
     compute(i + 1, q_lds1, do_lds1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  if (wave_active && kj < lk) {
+  // Each wave stores its 32 keys' dK and dV rows through one of the (now
+  // idle) tile buffers, rows in consecutive lanes.
+  constexpr int ST_BYTES = TileStore<NDB>::BYTES > TileStore<NDBV>::BYTES ? TileStore<NDB>::BYTES
+                                                                          : TileStore<NDBV>::BYTES;
+  if constexpr (ST_BYTES <= TB && ST_BYTES <= TBV) {
+    if (wave_active) {
+      uint8_t* sl = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
+      const int nrows = min(32, lk - k0w);
+      TileStore<NDB>::store(dkacc, a.act.gscale, sl, a.dk, ((long)(ks + k0w) * a.hkv + g) * D, (long)a.hkv * D,
+                            nrows, a.out_kind, lane);
+      TileStore<NDBV>::store(dvacc, a.act.pscale, sl, a.dv, ((long)(ks + k0w) * a.hkv + g) * DV, (long)a.hkv * DV,
+                             nrows, a.out_kind, lane);
+    }
+  } else if (wave_active && kj < lk) {
     const long orow = ((long)(ks + kj) * a.hkv + g) * D, vrow = ((long)(ks + kj) * a.hkv + g) * DV;
     const float gs = a.act.gscale, ps = a.act.pscale;
 #pragma unroll
@@ -474,6 +491,7 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
       }
     }
   }
+  return nsteps > 0;
   };
 
   if (a.counters == nullptr) {
@@ -481,16 +499,16 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     // sequences first; within a pair, key blocks run last-first.
     WorkItem w;
     if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
-    process(w.b, w.g, a.nblocks - 1 - w.rest);
+    process(w.b, w.g, a.nblocks - 1 - w.rest, nullptr);
   } else {
     // Per-XCD work queue over the same pairs, longest sequence first (one
     // workgroup per CU here, so the dispatcher's in-order hand-out of one
     // item per workgroup would leave CUs idle between items).
     run_queue(a.counters + (blockIdx.x & (kNumXcd - 1)), xcd_items(a.batch, a.hkv, a.nblocks),
-              [&](int j) __attribute__((always_inline)) {
+              [&](int j, QueueFetch& fetch) __attribute__((always_inline)) {
                 WorkItem w;
                 xcd_item(j, a.hkv, a.nblocks, a.perm, w);
-                process(w.b, w.g, a.nblocks - 1 - w.rest);
+                return process(w.b, w.g, a.nblocks - 1 - w.rest, &fetch);
               });
   }
 }
@@ -1162,7 +1180,15 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
     __syncthreads();
   }
 
-  if (wave_active && qi < lq) {
+  // Each wave stores its 32 query rows of dQ through one of the (now idle)
+  // tile buffers, rows in consecutive lanes.
+  if constexpr (TileStore<NDB>::BYTES <= TB && TileStore<NDB>::BYTES <= TBV) {
+    if (wave_active) {
+      uint8_t* sl = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+      TileStore<NDB>::store(dqacc, a.act.gscale, sl, a.dq, ((long)(qs + q0w) * a.hq + h) * D, (long)a.hq * D,
+                            min(32, lq - q0w), a.out_kind, lane);
+    }
+  } else if (wave_active && qi < lq) {
     const long orow = ((long)(qs + qi) * a.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

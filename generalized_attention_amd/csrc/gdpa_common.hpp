@@ -414,4 +414,98 @@ __device__ __forceinline__ u32x4 tr_at(const uint8_t* tile, const int (&o)[2], i
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// ------------------------------------------------------- coalesced tile store
+// A wave's 32-row result tile in the accumulator layout the kernels end with
+// (lane l owns output row l % 32; register 4 i + j of column block db holds
+// column 32 db + 4 (l / 32) + 8 i + j), written so that consecutive lanes
+// cover consecutive bytes of one row.  Stored straight from the accumulators,
+// each 16-byte-per-lane store instruction would touch 32 rows with 32 bytes
+// in each; the tile instead goes through a row-major LDS copy of itself, and
+// every store covers whole rows (two rows of 512 bytes for fp32 at head dim
+// 128).  LDS chunk c of row r sits at chunk position c ^ (r % 16) of a row
+// padded to a multiple of 16 chunks, so the 16 lanes of each write (16 rows,
+// one chunk) and of each read (one row, 16 chunks) hit 16 distinct bank
+// quads.  The stores go through a buffer resource that ends at row nrows, so
+// the hardware drops the rows past the end and no store needs a branch.  The
+// LDS region (BYTES) is the wave's own and must be free: callers pass a tile
+// buffer after the loop's last barrier.  A wave's LDS accesses complete in
+// issue order, so no wait separates the write from the read-back.
+template <int NDB>
+struct TileStore {
+  static constexpr int NC = NDB * 8;              // 16-byte chunks per fp32 row
+  static constexpr int RS = (NC + 15) / 16 * 16;  // LDS row stride in chunks
+  static constexpr int BYTES = 32 * RS * 16;      // LDS bytes per wave
+  static constexpr int NR = NC / 2;               // 16-byte reads per lane
+  static __device__ __forceinline__ int off(int r, int c) { return (r * RS + (c ^ (r & 15))) << 4; }
+  // out + base: element (row 0, column 0) of the tile; ld: elements between
+  // rows; rows at or past nrows are not written; kind: OUT_* element type.
+  static __device__ __forceinline__ void store(const f32x16 (&acc)[NDB], float scale, uint8_t* lds, void* out,
+                                               long base, long ld, int nrows, int kind, int lane) {
+    // (an opaque copy of the lane id keeps the compiler from computing the
+    // addresses below ahead of the kernel's main loop, where they would hold
+    // registers through it)
+    asm volatile("" : "+v"(lane));
+    lane &= 63;
+    const int r = lane & 31, hf = lane >> 5;
+    // chunk 8 db + 2 i4 + hf of row r: the XOR only touches the low 4 bits,
+    // so its position is 16 (db / 2) + ((8 (db % 2) + 2 i4) ^ (hf ^ r % 16))
+    const int wbase = (r * RS) << 4, wy = hf ^ (r & 15);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(lds + wbase + ((16 * (db >> 1) + ((8 * (db & 1) + 2 * i4) ^ wy)) << 4)) =
+            f32x4{acc[db][4 * i4] * scale, acc[db][4 * i4 + 1] * scale, acc[db][4 * i4 + 2] * scale,
+                  acc[db][4 * i4 + 3] * scale};
+    const int esz = kind == OUT_F32 ? 4 : 2;
+    // base and nrows are the same in every lane of the wave: moved to scalar
+    // registers, the resource needs no per-lane loop
+    const uint64_t tile = reinterpret_cast<uint64_t>(static_cast<uint8_t*>(out) + base * esz);
+    const uint64_t tile_s = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tile) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tile >> 32)) << 32);
+    const int nbytes = __builtin_amdgcn_readfirstlane(nrows > 0 ? nrows * (int)ld * esz : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(tile_s), nbytes);
+    // (all row offsets go into the per-lane offset, which the range check
+    // covers)
+    f32x4 v[NR];
+    int goff[NR];
+    if constexpr (64 % NC == 0) {
+      // read it covers rows RPI it + r0 (r0 = lane / NC), chunk c = lane % NC;
+      // (RPI it) % 16 is a multiple of RPI > r0, so the row's swizzle is
+      // (RPI it) % 16 + r0 and the chunk's position (c ^ r0) ^ ((RPI it) % 16)
+      constexpr int RPI = 64 / NC;
+      const int r0 = lane / NC, c = lane % NC, cx = c ^ r0;
+      const int rb = (r0 * RS) << 4;
+#pragma unroll
+      for (int it = 0; it < NR; ++it)
+        v[it] = *reinterpret_cast<const f32x4*>(lds + (it * RPI * RS * 16) + rb + ((cx ^ ((RPI * it) & 15)) << 4));
+      const int g0 = (r0 * (int)ld + c * 4) * esz;
+#pragma unroll
+      for (int it = 0; it < NR; ++it) goff[it] = g0 + it * RPI * (int)ld * esz;
+    } else {
+#pragma unroll
+      for (int it = 0; it < NR; ++it) {
+        const unsigned idx = (unsigned)(it * 64 + lane);
+        v[it] = *reinterpret_cast<const f32x4*>(lds + off((int)(idx / NC), (int)(idx % NC)));
+        goff[it] = ((int)(idx / NC) * (int)ld + (int)(idx % NC) * 4) * esz;
+      }
+    }
+    if (kind == OUT_F32) {
+#pragma unroll
+      for (int it = 0; it < NR; ++it)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[it]), rs, goff[it], 0, 0);
+    } else if (kind == OUT_BF16) {
+#pragma unroll
+      for (int it = 0; it < NR; ++it)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2<EL_BF16>(v[it][0], v[it][1]), pack2<EL_BF16>(v[it][2], v[it][3])},
+                                              rs, goff[it], 0, 0);
+    } else {
+#pragma unroll
+      for (int it = 0; it < NR; ++it)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2<EL_F16>(v[it][0], v[it][1]), pack2<EL_F16>(v[it][2], v[it][3])},
+                                              rs, goff[it], 0, 0);
+    }
+  }
+};
+
 }  // namespace gdpa

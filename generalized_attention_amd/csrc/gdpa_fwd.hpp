@@ -345,8 +345,17 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane stores 4 consecutive head-dim values per register group
-  if (!wave_active || qi >= lq) return;
+  // ---- epilogue: each wave stores its 32 rows of O through one of the (now
+  // idle) tile buffers, rows in consecutive lanes; where a tile buffer is too
+  // small (FP8 K), lanes store 4 consecutive head-dim values per register group
+  if (!wave_active) return;
+  if constexpr (NW == 4 && TileStore<NDB>::BYTES <= KBYTES && TileStore<NDB>::BYTES <= VBYTES) {
+    uint8_t* sl = wave == 0 ? v_lds0 : wave == 1 ? v_lds1 : wave == 2 ? k_lds0 : k_lds1;
+    TileStore<NDB>::store(oacc, a.act.pscale, sl, a.o, ((long)(qs + q0w) * a.hq + h) * DV, (long)a.hq * DV,
+                          min(32, lq - q0w), a.out_kind, lane);
+    return;
+  }
+  if (qi >= lq) return;
   const long orow = ((long)(qs + qi) * a.hq + h) * DV;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {

@@ -184,9 +184,25 @@ constexpr int kDqTile = 64;
 // the workgroups of an XCD take the next item of that XCD's list from an
 // atomic counter instead of being handed one item each by the dispatcher.
 // The lists run longest sequence first, so a free workgroup always picks the
-// heaviest remaining item of its XCD (list scheduling); the next index is
-// fetched while the current item runs.  Workgroup ids are dealt to the XCDs
-// in turn, so blockIdx % 8 names the XCD (only locality depends on that).
+// heaviest remaining item of its XCD (list scheduling).  The next index is
+// taken as the current item enters its last step (the body calls
+// fetch.issue() there; the counter's reply arrives while the step computes):
+// an index taken any earlier would reserve the heaviest remaining item for a
+// workgroup that stays busy for longer, while workgroups that free up in the
+// meantime take lighter ones, and the tail of the launch would lose the
+// longest-first order.  Workgroup ids are dealt to the XCDs in turn, so
+// blockIdx % 8 names the XCD (only locality depends on that).
+struct QueueFetch {
+  int32_t* counter;
+  int32_t* slot;  // LDS word that receives the next index
+  int32_t v;
+  __device__ __forceinline__ void issue() {
+    if (threadIdx.x == 0) v = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void publish() {
+    if (threadIdx.x == 0) *slot = v;
+  }
+};
 template <typename F>
 __device__ __forceinline__ void run_queue(int32_t* counter, long total, F&& body) {
   __shared__ int32_t nxt[2];
@@ -195,9 +211,12 @@ __device__ __forceinline__ void run_queue(int32_t* counter, long total, F&& body
   int item = nxt[0];
   int par = 0;
   while (item < total) {
-    if (threadIdx.x == 0)
-      nxt[par ^ 1] = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    body(item);
+    // the slot written during this item is read only after the barrier below;
+    // the other slot was read before the previous one
+    // body(item, fetch) calls fetch.issue() at most once and returns whether it did
+    QueueFetch fetch{counter, &nxt[par ^ 1], 0};
+    if (!body(item, fetch)) fetch.issue();
+    fetch.publish();
     __syncthreads();
     item = nxt[par ^ 1];
     par ^= 1;
