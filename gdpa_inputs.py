@@ -46,6 +46,7 @@ class Workload:
     window_right: int = -1
     fp8_qk: bool = False
     mx_qk: bool = False               # Q and K in MXFP8 (E4M3 elements, E8M0 scale per 32 head dims)
+    mx4_qk: bool = False              # Q and K in MXFP4 (E2M1 element pairs per byte, E8M0 scale per 32)
     fp16: bool = False       # fp16 Q/K/V/dO instead of bf16
     head_dim_v: Optional[int] = None  # of V and O (None: head_dim)
     backward: bool = False
@@ -136,6 +137,38 @@ def quantize_mxfp8(x: np.ndarray, block: int = 32):
     return codes, (e + 127).astype(np.uint8)
 
 
+# E2M1 magnitudes by code (OCP MX specification, FP4 E2M1)
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def quantize_mxfp4(x: np.ndarray, block: int = 32):
+    """OCP MX quantisation to MXFP4 (E2M1 elements) along the last axis: for
+    every block of 32 elements, shared exponent e = floor(log2(max|x|)) - 2
+    (2 = the largest E2M1 exponent; 0 for an all-zero block), clamped to
+    [-127, 127], scale code e + 127 (E8M0); element = the nearest E2M1 value
+    of x / 2^e (ties to the even code), saturated to +-6.
+
+    Returns (uint8 bytes [..., D / 2] holding element 2 i in the low nibble
+    of byte i and element 2 i + 1 in the high nibble, uint8 scale codes
+    [..., D / block])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    blocks = x.reshape(*x.shape[:-1], x.shape[-1] // block, block).astype(np.float64)
+    amax = np.max(np.abs(blocks), axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    y = np.minimum(np.abs(blocks / np.exp2(e.astype(np.float64))[..., None]), 6.0)
+    dist = np.abs(y[..., None] - _E2M1_GRID)
+    best = dist.min(-1, keepdims=True)
+    # among the nearest grid points take the even code (ties to even)
+    cand = np.where(dist == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(-1)
+    mag = np.where(even < 99, even, cand.min(-1)).astype(np.uint8)
+    codes = (mag | np.where(blocks < 0, 8, 0).astype(np.uint8)).reshape(x.shape)
+    codes[(codes & 0x7) == 0] = 0   # -0 stored as +0
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 @dataclasses.dataclass
 class Batch:
     """One drawn problem instance.  Tensors are storage-format numpy arrays."""
@@ -144,13 +177,13 @@ class Batch:
     seqlens_k: np.ndarray     # int64 [B]
     cu_seqlens_q: np.ndarray  # int32 [B+1]
     cu_seqlens_k: np.ndarray  # int32 [B+1]
-    q: np.ndarray             # uint16 bf16/fp16 bits, or uint8 E4M3 codes  [total_q, Hq, D]
+    q: np.ndarray             # uint16 bf16/fp16 bits, uint8 E4M3 codes [total_q, Hq, D], or MXFP4 bytes [.., D / 2]
     k: np.ndarray             # same format as q                             [total_k, Hkv, D]
     v: np.ndarray             # uint16 bf16/fp16 bits                        [total_k, Hkv, D]
     do: Optional[np.ndarray]  # uint16, same format as v                     [total_q, Hq, D]
     q_scale: float = 1.0      # per-tensor scale of q codes (fp8 only)
     k_scale: float = 1.0
-    q_mx: Optional[np.ndarray] = None  # uint8 E8M0 block scales of q codes [total_q, Hq, D / 32] (MXFP8)
+    q_mx: Optional[np.ndarray] = None  # uint8 E8M0 block scales of q codes [total_q, Hq, D / 32] (MXFP8, MXFP4)
     k_mx: Optional[np.ndarray] = None  #                          of k codes [total_k, Hkv, D / 32]
 
     @property
@@ -210,7 +243,10 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_do: Optional[bool]
     qs = ks = 1.0
     qmx = kmx = None
     enc = f32_to_f16_bits if wl.fp16 else f32_to_bf16_bits
-    if wl.mx_qk:
+    if wl.mx4_qk:
+        q, qmx = quantize_mxfp4(qf)
+        k, kmx = quantize_mxfp4(kf)
+    elif wl.mx_qk:
         q, qmx = quantize_mxfp8(qf)
         k, kmx = quantize_mxfp8(kf)
     elif wl.fp8_qk:

@@ -20,7 +20,8 @@ Every function is pinned by tests under tests/ (test_oracle_*.py) against
 closed forms, library routines, brute force and finite differences.
 """
 from .activations import act, act_grad, ACT_NAMES
-from .formats import decode_bf16, decode_e4m3, decode_e8m0, decode_f16, decode_mxfp8
+from .formats import (decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0, decode_f16, decode_mxfp4,
+                      decode_mxfp8, unpack_fp4)
 from .gdpa import (
     allowed_mask,
     gdpa_forward,

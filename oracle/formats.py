@@ -20,6 +20,13 @@ Test infrastructure (see the package docstring).
   decode_e4m3(code) * 2^(scale - 127).  The GDPA README ("Features") lists
   MXFP8 among its coming formats without a layout; reading: blocks run along
   the head dim (the contraction axis of Q K^T), scales stored [..., D / 32].
+* FP4 E2M1: the element type of the OCP MX specification's MXFP4: 1 sign bit,
+  2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 is subnormal
+  (m/2 * 2^0); no infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+* MXFP4: E2M1 elements, one E8M0 scale per block of 32.  Two elements share a
+  byte; reading (the pages give no layout): element 2 i sits in the low nibble
+  of byte i of a row, element 2 i + 1 in the high nibble, rows [..., D / 2]
+  bytes, scales [..., D / 32] as for MXFP8.
 """
 from __future__ import annotations
 
@@ -68,3 +75,33 @@ def decode_mxfp8(codes, scales, block: int = 32) -> np.ndarray:
     scales = np.asarray(scales, dtype=np.uint8)
     assert codes.shape[-1] == scales.shape[-1] * block and codes.shape[:-1] == scales.shape[:-1]
     return decode_e4m3(codes) * np.repeat(decode_e8m0(scales), block, axis=-1)
+
+
+def decode_e2m1(codes) -> np.ndarray:
+    """FP4 E2M1 codes (low 4 bits of each value) -> fp64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    normal = (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    sub = m / 2.0
+    return sign * np.where(e == 0, sub, normal)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """Bytes [..., D / 2] -> E2M1 codes [..., D]: element 2 i from the low
+    nibble of byte i, element 2 i + 1 from its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def decode_mxfp4(packed, scales, block: int = 32) -> np.ndarray:
+    """MXFP4 values (fp64): packed [..., D / 2] bytes of E2M1 pairs, scales
+    [..., D / block] (uint8 E8M0); element d takes the scale of block d // block."""
+    codes = unpack_fp4(packed)
+    scales = np.asarray(scales, dtype=np.uint8)
+    assert codes.shape[-1] == scales.shape[-1] * block and codes.shape[:-1] == scales.shape[:-1]
+    return decode_e2m1(codes) * np.repeat(decode_e8m0(scales), block, axis=-1)

@@ -28,7 +28,10 @@ def oracle_inputs(bt: gi.Batch):
     """fp64 values the kernels consume (decoded bf16 / fp16 / E4M3 codes x scale
     / MXFP8 codes x block scale)."""
     dec = oracle.decode_f16 if bt.wl.fp16 else oracle.decode_bf16
-    if bt.wl.mx_qk:
+    if bt.wl.mx4_qk:
+        q = oracle.decode_mxfp4(bt.q, bt.q_mx)
+        k = oracle.decode_mxfp4(bt.k, bt.k_mx)
+    elif bt.wl.mx_qk:
         q = oracle.decode_mxfp8(bt.q, bt.q_mx)
         k = oracle.decode_mxfp8(bt.k, bt.k_mx)
     elif bt.wl.fp8_qk:
@@ -50,10 +53,10 @@ def device_batch(bt: gi.Batch):
     import torch
     wl = bt.wl
     e16 = "fp16" if wl.fp16 else "bf16"
-    qk = "fp8" if (wl.fp8_qk or wl.mx_qk) else e16
+    qk = "fp8" if (wl.fp8_qk or wl.mx_qk) else "u8" if wl.mx4_qk else e16
     d = dict(q=to_dev(bt.q, qk), k=to_dev(bt.k, qk), v=to_dev(bt.v, e16),
              cu_q=torch.from_numpy(bt.cu_seqlens_q).cuda(), cu_k=torch.from_numpy(bt.cu_seqlens_k).cuda())
-    if wl.mx_qk:
+    if wl.mx_qk or wl.mx4_qk:
         d["q_mx"] = torch.from_numpy(np.ascontiguousarray(bt.q_mx)).cuda()
         d["k_mx"] = torch.from_numpy(np.ascontiguousarray(bt.k_mx)).cuda()
     if bt.do is not None:
