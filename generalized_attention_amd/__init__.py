@@ -35,6 +35,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_UNSUPPORTED",
 
 EXPORTED = (
     "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd", "gdpa_varlen_bwd_noalloc", "gdpa_varlen_fwd_mxfp8",
+    "gdpa_varlen_fwd_mxfp4",
     "gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
     "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size",
     "gdpa_status_string", "gdpa_abi_version",
@@ -59,6 +60,7 @@ def _load():
                                     I32, I32, F32, I32, I32, I32, F32, F32, P, SZ, P]
     lib.gdpa_varlen_fwd_mxfp8.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32,
                                           I32, I32, I32, F32, I32, P, SZ, P]
+    lib.gdpa_varlen_fwd_mxfp4.argtypes = lib.gdpa_varlen_fwd_mxfp8.argtypes
     lib.gdpa_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
                              I32, I32, P, SZ, P]
     lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, F32,
@@ -264,6 +266,33 @@ def gdpa_varlen_fwd_mxfp8(q, q_scale, k, k_scale, v, o, cu_seqlens_q, cu_seqlens
                                     window_right, _act(act), float(act_param), _out_dtype(o), _ptr(ws), nws,
                                     _stream(q.device))
     _check(st, "gdpa_varlen_fwd_mxfp8")
+    return o
+
+
+def gdpa_varlen_fwd_mxfp4(q, q_scale, k, k_scale, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          scale, act="fast_gelu", act_param=0.01, mask="none", window_left=-1, window_right=-1):
+    """Jagged forward with MXFP4 q/k: uint8 [total, heads, D / 2], two E2M1
+    elements per byte (element 2 i in the low nibble of byte i), E8M0 scales
+    [total, heads, D / 32] (uint8 or float8_e8m0fnu), v bf16 [total, heads_kv, D]."""
+    _check_fwd_args(q, k, v, o, jagged=True)
+    _check_cu(cu_seqlens_q, cu_seqlens_k, q.device)
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8:
+        raise TypeError(f"MXFP4 q/k are uint8 bytes of E2M1 pairs, got {q.dtype} and {k.dtype}")
+    D = 2 * q.shape[2]
+    if D != v.shape[2] or D % 32:
+        raise ValueError("MXFP4: 2 * q.shape[2] is the head dim, equal to v's and a multiple of 32")
+    _SC = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+    _expect("q_scale", q_scale, (q.shape[0], q.shape[1], D // 32), q.device, _SC)
+    _expect("k_scale", k_scale, (k.shape[0], k.shape[1], D // 32), q.device, _SC)
+    B = cu_seqlens_q.numel() - 1
+    Hq, Hkv = q.shape[1], k.shape[1]
+    ws, nws = _workspace(_lib.gdpa_varlen_fwd_workspace_size(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, D), q.device)
+    st = _lib.gdpa_varlen_fwd_mxfp4(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(o),
+                                    _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k),
+                                    q.shape[0], k.shape[0], Hq, Hkv, D, float(scale), _mask(mask), window_left,
+                                    window_right, _act(act), float(act_param), _out_dtype(o), _ptr(ws), nws,
+                                    _stream(q.device))
+    _check(st, "gdpa_varlen_fwd_mxfp4")
     return o
 
 

@@ -99,7 +99,8 @@ gdpa_status_t check_common(int32_t batch, int32_t max_lq, int32_t max_lk, int64_
 // checks its combination here, before the schedule kernel or any other HIP
 // call is queued.
 bool fwd_built(int in_kind, int32_t d, int32_t dv) {
-  if (in_kind == gdpa::EL_MX8) return d == dv && (d == 64 || d == 128);  // 32-wide blocks on the K = 64 MFMA
+  if (in_kind == gdpa::EL_MX8 || in_kind == gdpa::EL_MX4)
+    return d == dv && (d == 64 || d == 128);  // 32-wide blocks on the K = 64 MFMA
   if (d == dv && (d == 64 || d == 96 || d == 128)) return true;
   return in_kind != gdpa::EL_FP8 && d == 192 && dv == 128;
 }
@@ -320,10 +321,11 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
                       float k_descale, void* workspace, size_t workspace_bytes, void* stream,
                       const uint8_t* q_mx = nullptr, const uint8_t* k_mx = nullptr) {
   if (qk_dtype != GDPA_DTYPE_BF16 && qk_dtype != GDPA_DTYPE_FP16 && qk_dtype != GDPA_DTYPE_FP8_E4M3 &&
-      qk_dtype != GDPA_DTYPE_MXFP8_E4M3)
+      qk_dtype != GDPA_DTYPE_MXFP8_E4M3 && qk_dtype != GDPA_DTYPE_MXFP4_E2M1)
     return GDPA_ERR_INVALID_ARG;
-  // MXFP8 Q/K carry their scales in q_mx / k_mx (and only they do)
-  const bool mx = qk_dtype == GDPA_DTYPE_MXFP8_E4M3;
+  // MXFP8 / MXFP4 Q/K carry their scales in q_mx / k_mx (and only they do)
+  const bool mx4 = qk_dtype == GDPA_DTYPE_MXFP4_E2M1;
+  const bool mx = qk_dtype == GDPA_DTYPE_MXFP8_E4M3 || mx4;
   if (mx != (q_mx != nullptr || k_mx != nullptr) && !(mx && c.batch == 0)) return GDPA_ERR_INVALID_ARG;
   if (v_dtype != GDPA_DTYPE_BF16 && v_dtype != GDPA_DTYPE_FP16)
     return v_dtype == GDPA_DTYPE_FP8_E4M3 ? GDPA_ERR_UNSUPPORTED : GDPA_ERR_INVALID_ARG;
@@ -333,7 +335,11 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   const bool fp8 = qk_dtype == GDPA_DTYPE_FP8_E4M3 || mx;
   const bool f16 = v_dtype == GDPA_DTYPE_FP16;
   if (f16 != (qk_dtype == GDPA_DTYPE_FP16)) return GDPA_ERR_UNSUPPORTED;
-  const int in_kind = mx ? gdpa::EL_MX8 : fp8 ? gdpa::EL_FP8 : f16 ? gdpa::EL_F16 : gdpa::EL_BF16;
+  const int in_kind = mx4  ? gdpa::EL_MX4
+                      : mx ? gdpa::EL_MX8
+                      : fp8 ? gdpa::EL_FP8
+                      : f16 ? gdpa::EL_F16
+                            : gdpa::EL_BF16;
   if (fp8 && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
   if (!fwd_built(in_kind, c.d, c.dv)) return GDPA_ERR_UNSUPPORTED;
   if (c.batch == 0 || c.total_q == 0) return GDPA_OK;
@@ -571,13 +577,14 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
                  q_descale, k_descale, workspace, workspace_bytes, stream);
 }
 
-gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
-                                    const void* v, void* o, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
-                                    int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
-                                    int32_t act, float act_param, int32_t out_dtype, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+namespace {
+gdpa_status_t varlen_fwd_mx(int32_t qk_dtype, const void* q, const void* q_scale, const void* k,
+                            const void* k_scale, const void* v, void* o, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int64_t total_q, int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv,
+                            int32_t head_dim, float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                            int32_t act, float act_param, int32_t out_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   Common c;
   gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
                                   head_dim, head_dim, scale, mask, window_left, window_right, act, act_param, &c);
@@ -585,9 +592,34 @@ gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const vo
   if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
   if (batch > 0 && total_q > 0 && (q_scale == nullptr || (total_k > 0 && k_scale == nullptr)))
     return GDPA_ERR_INVALID_ARG;
-  return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, GDPA_DTYPE_MXFP8_E4M3,
-                 GDPA_DTYPE_BF16, out_dtype, 1.0f, 1.0f, workspace, workspace_bytes, stream,
-                 static_cast<const uint8_t*>(q_scale), static_cast<const uint8_t*>(k_scale));
+  return run_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, qk_dtype, GDPA_DTYPE_BF16,
+                 out_dtype, 1.0f, 1.0f, workspace, workspace_bytes, stream, static_cast<const uint8_t*>(q_scale),
+                 static_cast<const uint8_t*>(k_scale));
+}
+}  // namespace
+
+gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                    const void* v, void* o, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
+                                    int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                    int32_t act, float act_param, int32_t out_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return varlen_fwd_mx(GDPA_DTYPE_MXFP8_E4M3, q, q_scale, k, k_scale, v, o, cu_seqlens_q, cu_seqlens_k, batch,
+                       max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv, head_dim, scale,
+                       mask, window_left, window_right, act, act_param, out_dtype, workspace, workspace_bytes, stream);
+}
+
+gdpa_status_t gdpa_varlen_fwd_mxfp4(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                    const void* v, void* o, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q,
+                                    int64_t total_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                    int32_t act, float act_param, int32_t out_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return varlen_fwd_mx(GDPA_DTYPE_MXFP4_E2M1, q, q_scale, k, k_scale, v, o, cu_seqlens_q, cu_seqlens_k, batch,
+                       max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv, head_dim, scale,
+                       mask, window_left, window_right, act, act_param, out_dtype, workspace, workspace_bytes, stream);
 }
 
 gdpa_status_t gdpa_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,

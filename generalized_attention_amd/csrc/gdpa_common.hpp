@@ -64,6 +64,21 @@ __device__ __forceinline__ f32x16 mfma_fp8_k64_scaled(const u32x4& a0, const u32
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
 }
 
+// FP4 E2M1 x E2M1 over 64 k-values with E8M0 block scales (the OCP MXFP4
+// format): each lane supplies 16 bytes of A and of B, 32 elements, two per
+// byte, element 2 i in the low nibble of byte i.  Measured on gfx950: the
+// instruction reads 4 registers per operand, nibble i of lane l pairs with
+// nibble i of the same lane of the other operand, and all 32 elements of a
+// lane form one scale block, scaled by that lane's own scale byte (lane half
+// h of a row therefore holds head-dim block 2 s + h of unit s).
+__device__ __forceinline__ f32x16 mfma_fp4_k64_scaled(const u32x4& a, const u32x4& b, const f32x16& c, uint32_t sa,
+                                                      uint32_t sb) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -301,7 +316,8 @@ template <int ROWB>
 __device__ __forceinline__ int chunk_swz(int row) {
   if constexpr (ROWB >= 256) return ((row & 3) << 2) | ((row >> 2) & 3);
   else if constexpr (ROWB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  else return (row >> 2) & 3;
+  else if constexpr (ROWB == 64) return (row >> 2) & 3;
+  else return (row >> 2) & 1;  // 32-byte rows (MXFP4 K at head dim 64): two chunks
 }
 template <int ROWB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk

@@ -9,6 +9,7 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int head_dim_v, int act_ki
     case EL_BF16: return launch_fwd_in<EL_BF16>(a, head_dim, head_dim_v, act_kind, stream);
     case EL_FP8: return launch_fwd_in<EL_FP8>(a, head_dim, head_dim_v, act_kind, stream);
     case EL_MX8: return launch_fwd_in<EL_MX8>(a, head_dim, head_dim_v, act_kind, stream);
+    case EL_MX4: return launch_fwd_in<EL_MX4>(a, head_dim, head_dim_v, act_kind, stream);
     case EL_F16: return launch_fwd_f16(a, head_dim, head_dim_v, act_kind, stream);
     default: return hipErrorInvalidValue;
   }

@@ -47,10 +47,12 @@ __device__ __forceinline__ uint32_t load_scales(const uint8_t* p) {
 // D: head dim of Q and K; DV: head dim of V and O.
 template <int D, int ACT, int IN, bool PSPLIT, int NW, int DV = D>
 struct FwdKernel {
-  static constexpr bool MX = IN == EL_MX8;    // MXFP8 Q/K: E4M3 codes with an E8M0 scale per 32 head dims
-  static constexpr bool FP8 = IN == EL_FP8 || MX;
+  static constexpr bool MX4 = IN == EL_MX4;   // MXFP4 Q/K: E2M1 pairs per byte with an E8M0 scale per 32 head dims
+  static constexpr bool MX = IN == EL_MX8 || MX4;  // block-scaled (MXFP8: E4M3 codes with an E8M0 scale per 32)
+  static constexpr bool FP8 = IN == EL_FP8 || IN == EL_MX8;  // one byte per Q/K element
+  static constexpr bool NARROW = FP8 || MX4;                // Q K^T on the K = 64 MFMA
   static constexpr int EL = IN == EL_F16 ? EL_F16 : EL_BF16;  // V, P (and 16-bit Q, K)
-  static_assert(!MX || D % 64 == 0, "MXFP8: every head-dim block of 32 on the K = 64 MFMA");
+  static_assert(!MX || D % 64 == 0, "MX formats: every head-dim block of 32 on the K = 64 MFMA");
   static constexpr int BM = 32 * NW;
   static constexpr int DPK = lds_dim(D);  // head dims of the LDS rows of K and V
   static constexpr int DPV = lds_dim(DV);
@@ -58,22 +60,23 @@ struct FwdKernel {
   static constexpr int NKB = BN / 32;     // 32-key blocks per tile
   static constexpr int KS = D / 16;       // k-steps of Q K^T
   static constexpr int NDB = DV / 32;     // 32-row blocks of O^T
-  static constexpr int KROWB = FP8 ? DPK : 2 * DPK;
+  static constexpr int KROWB = MX4 ? DPK / 2 : FP8 ? DPK : 2 * DPK;
   static constexpr int VROWB = 2 * DPV;
   // FP8 Q K^T: the first 64 * NK64 head-dim bytes on the K = 64 MFMA (lane
   // half h of unit s < NK64 holds bytes [64 s + 32 h, +32) of its K row and of
   // its Q row, two 16-byte pieces each), the remaining 16 * NK16 bytes on the
   // K = 16 MFMA (8 bytes per lane half, as for 16-bit inputs)
-  static constexpr int NK64 = FP8 ? D / 64 : 0;
+  // (MXFP4: unit s on the K = 64 MFMA takes bytes [32 s + 16 h, +16) in lane half h)
+  static constexpr int NK64 = NARROW ? D / 64 : 0;
   static constexpr int NK16 = FP8 ? (D % 64) / 16 : 0;
-  static constexpr int NQR = FP8 ? (NK64 > 0 ? 2 * NK64 : 1) : KS;  // 16-byte Q registers
+  static constexpr int NQR = MX4 ? NK64 : FP8 ? (NK64 > 0 ? 2 * NK64 : 1) : KS;  // 16-byte Q registers
   static constexpr int NQR8 = NK16 > 0 ? NK16 : 1;                  // 8-byte FP8 Q registers
   static constexpr int NP = PSPLIT ? 2 : 1;  // 16-bit words per P element (hi, lo)
-  static constexpr int NA = FP8 ? NK64 + NK16 : KS;  // S units per key block (1 MFMA each)
+  static constexpr int NA = NARROW ? NK64 + NK16 : KS;  // S units per key block (1 MFMA each)
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
   static constexpr int PREF = 2;             // units of operand prefetch
-  using KOffs = TileOffs<FP8 ? VROWB : KROWB>;  // row reads of 16-bit K (unused for FP8 K)
+  using KOffs = TileOffs<NARROW ? VROWB : KROWB>;  // row reads of 16-bit K (unused for 8- and 4-bit K)
   using VOffs = TileOffs<VROWB>;                 // transposed reads of V
 
   // One pair of accumulator elements (key rows 8t+2w, +1) -> packed P words.
@@ -100,7 +103,11 @@ struct FwdKernel {
                                                     const KOffs& lo, const VOffs& vo, int lane, u32x4& hi) {
     if (u < 2 * NA) {
       const int kb = kb0 + u / NA, s = u % NA;
-      if constexpr (FP8) {
+      if constexpr (MX4) {
+        // head-dim block 2 s + h: bytes [32 s + 16 h, +16) of the K row
+        hi = u32x4{0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4*>(kl + lds_off<KROWB>(kb * 32 + (lane & 31), 2 * s + (lane >> 5)));
+      } else if constexpr (FP8) {
         const int row = kb * 32 + (lane & 31);
         if (s < NK64) {
           // FP8: bytes [64 s + 32 h, +32) in lane half h.  MXFP8: the block
@@ -155,7 +162,10 @@ struct FwdKernel {
       const u32x4& op = ring[u % (PREF + 1)];
       if (u < 2 * NA) {
         const int j = u / NA, s = u % NA;
-        if constexpr (FP8) {
+        if constexpr (MX4) {
+          const int sh = 16 * s + 8 * (lane >> 5);
+          sacc[j] = mfma_fp4_k64_scaled(op, qreg[s], sacc[j], (ksc[j] >> sh) & 0xffu, (qsc >> sh) & 0xffu);
+        } else if constexpr (FP8) {
           if constexpr (MX) {
             // lane half h supplies the scale of head-dim block 2 s + h (its key's / query's)
             const int sh = 16 * s + 8 * (lane >> 5);
@@ -242,7 +252,12 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   u32x2 qreg8[K::NQR8];
   {
     const long qrow = (long)(qs + min(qi, lq - 1)) * q_ld + h * D + hf * 8;
-    if constexpr (FP8) {
+    if constexpr (K::MX4) {
+      // MXFP4 (two elements per byte): bytes [32 s + 16 hf, +16) of the row, as for K
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8) / 2;
+#pragma unroll
+      for (int s = 0; s < K::NK64; ++s) qreg[s] = load16_or_zero(qp + 32 * s + 16 * hf, qi < lq);
+    } else if constexpr (FP8) {
       const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow - hf * 8);
 #pragma unroll
       for (int s = 0; s < K::NK64; ++s) {
@@ -270,19 +285,19 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   const typename K::KOffs loffs = K::KOffs::make(lane);
   const typename K::VOffs voffs = K::VOffs::make(lane);
 
-  const int esz = FP8 ? 1 : 2;
+  const int esz2 = K::MX4 ? 1 : FP8 ? 2 : 4;  // bytes per two K elements
   const long kv_ld = (long)a.hkv * D, v_ld = (long)a.hkv * DV;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)ks * kv_ld + g * D) * esz;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)ks * kv_ld + g * D) * esz2 / 2;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)ks * v_ld + g * DV) * 2;
 
   // Byte ranges of this sequence's K and V rows (all KV heads), addressed by
   // 32-bit offsets; the host keeps them below 2^31.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld * esz);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, lk * (int)kv_ld * esz2 / 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, lk * (int)v_ld * 2);
   auto stage = [&](int nb, uint8_t* kl, uint8_t* vl) {
     const int n0 = nb * BN;
-    stage_tile_buf<BN, K::KROWB, NW, D * (FP8 ? 1 : 2) / 16>(krs, n0 * (int)kv_ld * esz, (int)kv_ld * esz, lk - n0,
-                                                             kl, wave, lane);
+    stage_tile_buf<BN, K::KROWB, NW, D * esz2 / 32>(krs, n0 * (int)kv_ld * esz2 / 2, (int)kv_ld * esz2 / 2,
+                                                   lk - n0, kl, wave, lane);
     stage_tile_buf<BN, K::VROWB, NW, DV / 8>(vrs, n0 * (int)v_ld * 2, (int)v_ld * 2, lk - n0, vl, wave, lane);
   };
   // One tile of math for this wave, two 32-key blocks at a time; the mask is
@@ -409,7 +424,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int act_kind, hipStream_t strea
 // (128, 128), and (192, 128) for 16-bit inputs.
 template <int IN>
 static hipError_t launch_fwd_in(const FwdArgs& a, int head_dim, int head_dim_v, int act_kind, hipStream_t stream) {
-  if constexpr (IN == EL_MX8) {
+  if constexpr (IN == EL_MX8 || IN == EL_MX4) {
     if (head_dim == head_dim_v && head_dim == 64) return launch_fwd_d<64, IN>(a, act_kind, stream);
     if (head_dim == head_dim_v && head_dim == 128) return launch_fwd_d<128, IN>(a, act_kind, stream);
     return hipErrorInvalidValue;

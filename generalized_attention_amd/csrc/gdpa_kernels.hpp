@@ -10,7 +10,8 @@ namespace gdpa {
 // FAST_SILU -> SILU).  Values match gdpa_act_t.
 // Element types of the MFMA inputs: bf16 or fp16 Q, K, V (and dO), or FP8
 // E4M3 Q and K with bf16 V (forward only).
-enum ElemKind : int { EL_BF16 = 0, EL_F16 = 1, EL_FP8 = 2, EL_MX8 = 3 };  // EL_MX8: MXFP8 (E4M3, E8M0 per 32)
+// EL_MX8: MXFP8 (E4M3, E8M0 scale per 32); EL_MX4: MXFP4 (E2M1 pairs per byte, E8M0 scale per 32)
+enum ElemKind : int { EL_BF16 = 0, EL_F16 = 1, EL_FP8 = 2, EL_MX8 = 3, EL_MX4 = 4 };
 // Output element types.
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 

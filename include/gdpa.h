@@ -111,7 +111,8 @@ typedef enum {
   GDPA_DTYPE_FP16 = 1,      /* IEEE binary16 */
   GDPA_DTYPE_FP8_E4M3 = 2,  /* OCP E4M3 codes, forward q/k only */
   GDPA_DTYPE_FP32 = 3,      /* outputs only */
-  GDPA_DTYPE_MXFP8_E4M3 = 4 /* OCP MXFP8: E4M3 codes + E8M0 scales; gdpa_varlen_fwd_mxfp8 only */
+  GDPA_DTYPE_MXFP8_E4M3 = 4, /* OCP MXFP8: E4M3 codes + E8M0 scales; gdpa_varlen_fwd_mxfp8 only */
+  GDPA_DTYPE_MXFP4_E2M1 = 5  /* OCP MXFP4: E2M1 pairs + E8M0 scales; gdpa_varlen_fwd_mxfp4 only */
 } gdpa_dtype_t;
 
 /* ------------------------------------------------------------------ forward
@@ -168,6 +169,27 @@ gdpa_status_t gdpa_varlen_fwd(const void* q, const void* k, const void* v, void*
  * (q_scale / k_scale NULL with work to do: GDPA_ERR_INVALID_ARG).  Both score
  * operands enter gfx950's block-scaled MFMA with their scales. */
 gdpa_status_t gdpa_varlen_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                    const void* v, void* o,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int64_t total_q, int64_t total_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                    int32_t act, float act_param, int32_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Jagged forward with MXFP4 Q and K (README "Features": "MXFP4 and MXFP8
+ * forward & backward (coming soon)"; the format is the OCP Microscaling
+ * Formats specification's MXFP4: FP4 E2M1 elements — 1 sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 — with
+ * one E8M0 scale per block of 32).  q [total_q, Hq, D / 2] and
+ * k [total_k, Hkv, D / 2] bytes each hold two elements of a row: element 2 i
+ * in the low nibble of byte i, element 2 i + 1 in the high nibble (the
+ * specification leaves the packing open).  q_scale / k_scale, v, o, the head
+ * dims (64 or 128), the other arguments, the workspace and the errors are
+ * those of gdpa_varlen_fwd_mxfp8.  Both score operands enter gfx950's
+ * block-scaled MFMA in its FP4 form with their scales. */
+gdpa_status_t gdpa_varlen_fwd_mxfp4(const void* q, const void* q_scale, const void* k, const void* k_scale,
                                     const void* v, void* o,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                     int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,

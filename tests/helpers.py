@@ -76,10 +76,11 @@ def run_forward(g, bt: gi.Batch, dev=None, out_dtype=None, poison=True):
         torch.empty((tq, H, DV), dtype=out_dtype, device="cuda")
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
               window_right=wl.window_right, q_descale=bt.q_scale, k_descale=bt.k_scale)
-    if wl.mx_qk:
+    if wl.mx_qk or wl.mx4_qk:
         kw.pop("q_descale"), kw.pop("k_descale")
-        g.gdpa_varlen_fwd_mxfp8(dev["q"], dev["q_mx"], dev["k"], dev["k_mx"], dev["v"], o, dev["cu_q"], dev["cu_k"],
-                                bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, **kw)
+        fwd_mx = g.gdpa_varlen_fwd_mxfp4 if wl.mx4_qk else g.gdpa_varlen_fwd_mxfp8
+        fwd_mx(dev["q"], dev["q_mx"], dev["k"], dev["k_mx"], dev["v"], o, dev["cu_q"], dev["cu_k"],
+               bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, **kw)
     elif wl.varlen:
         g.gdpa_varlen_fwd(dev["q"], dev["k"], dev["v"], o, dev["cu_q"], dev["cu_k"], bt.max_seqlen_q,
                           bt.max_seqlen_k, wl.scale, **kw)

@@ -83,6 +83,13 @@ def varlen_fwd(lib, **over):
     return lib.gdpa_varlen_fwd(*a.values())
 
 
+def varlen_fwd_mx(lib, name, **over):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, o=FAKE, cq=FAKE, ck=FAKE, B=2, mq=128, mk=128, tq=200, tk=200,
+             Hq=4, Hkv=4, D=128, scale=0.1, mask=0, wl=-1, wr=-1, act=3, ap=0.01, od=3, ws=None, nws=0, stream=None)
+    a.update(over)
+    return getattr(lib, name)(*a.values())
+
+
 def bwd(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=2, Lq=128, Lk=128, Hq=4, Hkv=2, D=128,
              Dv=None, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01, ind=0, gd=3, ws=None, nws=0, stream=None)
@@ -148,6 +155,27 @@ def test_fwd_validation(lib, over, expect):
 ])
 def test_varlen_fwd_validation(lib, over, expect):
     assert varlen_fwd(lib, **over) == expect
+
+
+@pytest.mark.parametrize("name", ["gdpa_varlen_fwd_mxfp8", "gdpa_varlen_fwd_mxfp4"])
+@pytest.mark.parametrize("over,expect", [
+    (dict(D=96), UNSUPPORTED),               # 32-wide blocks on the K = 64 MFMA: head dims 64 and 128
+    (dict(D=192), UNSUPPORTED),
+    (dict(qs=None), INVALID),                # the block scales are required
+    (dict(ks=None), INVALID),
+    (dict(B=0), OK),
+    (dict(od=2), INVALID),
+    (dict(tq=257), INVALID),
+])
+def test_mx_forward_validation(lib, name, over, expect):
+    assert varlen_fwd_mx(lib, name, **over) == expect
+
+
+def test_mx_dtypes_need_their_entry_points(lib):
+    # the MX dtypes through the plain entry point carry no scales
+    assert varlen_fwd(lib, qk=4) == INVALID
+    assert varlen_fwd(lib, qk=5) == INVALID
+    assert varlen_fwd(lib, qk=6) == INVALID
 
 
 @pytest.mark.parametrize("over,expect", [

@@ -45,7 +45,7 @@ def _wl(**kw):
 
 def check_forward(g, bt, tol=None):
     wl = bt.wl
-    tol = tol or (TOL_FWD_FP8 if (wl.fp8_qk or wl.mx_qk) else TOL_FWD_BF16)
+    tol = tol or (TOL_FWD_FP8 if (wl.fp8_qk or wl.mx_qk or wl.mx4_qk) else TOL_FWD_BF16)
     o = run_forward(g, bt).cpu().double().numpy()
     q, k, v, _ = oracle_inputs(bt)
     ref = oracle.gdpa_forward(q, k, v, bt.cu_seqlens_q, bt.cu_seqlens_k, wl.scale, wl.act, **mask_kw(wl))
@@ -617,6 +617,53 @@ def test_mxfp8_unsupported_head_dim_and_missing_scales(g):
     o = torch.empty(40, 4, 64, device="cuda")
     with pytest.raises(g.GDPAError) as e:
         g.gdpa_varlen_fwd_mxfp8(dev["q"], None, dev["k"], dev["k_mx"], dev["v"], o, dev["cu_q"], dev["cu_k"], 40, 40,
+                                0.1)
+    assert e.value.status == 1
+
+
+# --------------------------------------------------- MXFP4 (E2M1, E8M0 per 32)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(MX_CASES)))
+def test_mxfp4_forward(g, case, D):
+    # the MXFP8 cases with FP4 elements: per-block scales spread by a seeded
+    # offset, jagged lengths with empty, one-token and ragged sequences
+    lens = [700, 1, 0, 300, 64, 129]
+    bt = gi.make_batch(_wl(head_dim=D, batch=len(lens), mx4_qk=True, backward=False, **MX_CASES[case]),
+                       seqlens_q=lens, seqlens_k=lens)
+    rng = np.random.default_rng(97 + case)
+    bt = dataclasses.replace(bt, q_mx=(bt.q_mx.astype(np.int64) + rng.integers(-3, 4, bt.q_mx.shape)).astype(np.uint8),
+                             k_mx=(bt.k_mx.astype(np.int64) + rng.integers(-3, 4, bt.k_mx.shape)).astype(np.uint8))
+    assert len(np.unique(bt.q_mx)) >= 7 and len(np.unique(bt.k_mx)) >= 7
+    check_forward(g, bt)
+
+
+def test_mxfp4_scales_and_nibble_order_matter(g):
+    # raising the q scales by 2 multiplies the scores by 4 (checked against the
+    # oracle); swapping the two nibbles of every q byte changes the result
+    import torch
+    lens = [200, 77]
+    bt = gi.make_batch(_wl(head_dim=128, batch=2, mx4_qk=True, backward=False, act="silu"), seqlens_q=lens,
+                       seqlens_k=lens)
+    o1 = run_forward(g, bt)
+    bt2 = dataclasses.replace(bt, q_mx=(bt.q_mx + 2).astype(np.uint8))
+    check_forward(g, bt2)
+    assert not torch.equal(o1, run_forward(g, bt2))
+    bt3 = dataclasses.replace(bt, q=((bt.q >> 4) | (bt.q << 4)).astype(np.uint8))
+    check_forward(g, bt3)
+    assert not torch.equal(o1, run_forward(g, bt3))
+
+
+def test_mxfp4_unsupported_head_dim_and_missing_scales(g):
+    import torch
+    bt = gi.make_batch(_wl(head_dim=96, batch=1, mx4_qk=True, backward=False), seqlens_q=[40], seqlens_k=[40])
+    with pytest.raises(g.GDPAError) as e:
+        run_forward(g, bt)
+    assert e.value.status == 2
+    bt = gi.make_batch(_wl(head_dim=64, batch=1, mx4_qk=True, backward=False), seqlens_q=[40], seqlens_k=[40])
+    dev = device_batch(bt)
+    o = torch.empty(40, 4, 64, device="cuda")
+    with pytest.raises(g.GDPAError) as e:
+        g.gdpa_varlen_fwd_mxfp4(dev["q"], dev["q_mx"], dev["k"], None, dev["v"], o, dev["cu_q"], dev["cu_k"], 40, 40,
                                 0.1)
     assert e.value.status == 1
 
