@@ -35,7 +35,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_UNSUPPORTED",
 
 EXPORTED = (
     "gdpa_fwd", "gdpa_varlen_fwd", "gdpa_bwd", "gdpa_varlen_bwd", "gdpa_varlen_bwd_noalloc", "gdpa_varlen_fwd_mxfp8",
-    "gdpa_varlen_fwd_mxfp4",
+    "gdpa_varlen_fwd_mxfp4", "gdpa_varlen_bwd_lowp", "gdpa_varlen_bwd_lowp_workspace_size",
     "gdpa_fwd_workspace_size", "gdpa_varlen_fwd_workspace_size",
     "gdpa_bwd_workspace_size", "gdpa_varlen_bwd_workspace_size",
     "gdpa_status_string", "gdpa_abi_version",
@@ -61,6 +61,11 @@ def _load():
     lib.gdpa_varlen_fwd_mxfp8.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32, I32,
                                           I32, I32, I32, F32, I32, P, SZ, P]
     lib.gdpa_varlen_fwd_mxfp4.argtypes = lib.gdpa_varlen_fwd_mxfp8.argtypes
+    lib.gdpa_varlen_bwd_lowp.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, F32,
+                                         I32, I32, I32, I32, F32, I32, F32, F32, I32, P, SZ, P]
+    lib.gdpa_varlen_bwd_lowp.restype = ctypes.c_int
+    lib.gdpa_varlen_bwd_lowp_workspace_size.argtypes = [I32, I32, I32, I64, I64, I32, I32, I32, I32, I32]
+    lib.gdpa_varlen_bwd_lowp_workspace_size.restype = SZ
     lib.gdpa_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, I32, I32, I32, I32, F32,
                              I32, I32, P, SZ, P]
     lib.gdpa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I64, I64, I32, I32, I32, I32, F32,
@@ -294,6 +299,53 @@ def gdpa_varlen_fwd_mxfp4(q, q_scale, k, k_scale, v, o, cu_seqlens_q, cu_seqlens
                                     _stream(q.device))
     _check(st, "gdpa_varlen_fwd_mxfp4")
     return o
+
+
+LOWP = {"fp8": 2, "mxfp8": 4, "mxfp4": 5}
+
+
+def gdpa_varlen_bwd_lowp(q, q_scale, k, k_scale, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                         max_seqlen_k, scale, qk_format, q_descale=1.0, k_descale=1.0, act="fast_gelu", act_param=0.01,
+                         mask="none", window_left=-1, window_right=-1):
+    """Jagged backward from 8- or 4-bit q/k (qk_format "fp8": E4M3 codes with
+    per-tensor descales, q_scale = k_scale = None; "mxfp8": E4M3 codes with
+    E8M0 block scales; "mxfp4": bytes of E2M1 pairs [total, heads, D / 2] with
+    E8M0 block scales); v, dout bf16; dq/dk/dv as in gdpa_varlen_bwd."""
+    fmt = LOWP[qk_format]
+    D = v.shape[2]
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn) or k.dtype != q.dtype:
+        raise TypeError(f"8- and 4-bit q/k are uint8 (or float8_e4m3fn) codes, got {q.dtype} and {k.dtype}")
+    qcols = D // 2 if qk_format == "mxfp4" else D
+    dev = q.device
+    _expect("q", q, (q.shape[0], q.shape[1], qcols), dev)
+    _expect("k", k, (k.shape[0], k.shape[1], qcols), dev)
+    _expect("v", v, (k.shape[0], k.shape[1], D), dev, (torch.bfloat16,))
+    _expect("dout", dout, (q.shape[0], q.shape[1], D), dev, (torch.bfloat16,))
+    _expect("dq", dq, (q.shape[0], q.shape[1], D), dev, _OUT)
+    _expect("dk", dk, (k.shape[0], k.shape[1], D), dev, _OUT)
+    _expect("dv", dv, v.shape, dev, _OUT)
+    if (dk is None) != (dv is None):
+        raise ValueError("dk and dv are requested together (both tensors or both None)")
+    _check_cu(cu_seqlens_q, cu_seqlens_k, dev)
+    if qk_format == "fp8":
+        if q_scale is not None or k_scale is not None:
+            raise ValueError("FP8 q/k take per-tensor descales, not block scales")
+    else:
+        _SC = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+        _expect("q_scale", q_scale, (q.shape[0], q.shape[1], D // 32), dev, _SC)
+        _expect("k_scale", k_scale, (k.shape[0], k.shape[1], D // 32), dev, _SC)
+    B = cu_seqlens_q.numel() - 1
+    Hq, Hkv = q.shape[1], k.shape[1]
+    gd = _grad_dtype(dq, dk, dv)
+    ws, nws = _workspace(_lib.gdpa_varlen_bwd_lowp_workspace_size(B, max_seqlen_q, max_seqlen_k, q.shape[0],
+                                                                  k.shape[0], Hq, Hkv, D, fmt, gd), dev)
+    st = _lib.gdpa_varlen_bwd_lowp(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(v), _ptr(dout), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q),
+                                   int(max_seqlen_k), q.shape[0], k.shape[0], Hq, Hkv, D, float(scale), _mask(mask),
+                                   window_left, window_right, _act(act), float(act_param), fmt, float(q_descale),
+                                   float(k_descale), gd, _ptr(ws), nws, _stream(dev))
+    _check(st, "gdpa_varlen_bwd_lowp")
+    return dq, dk, dv
 
 
 def gdpa_bwd(q, k, v, dout, dq, dk, dv, scale, act="fast_gelu", act_param=0.01, mask="none",

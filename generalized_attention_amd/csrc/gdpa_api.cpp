@@ -402,10 +402,14 @@ int32_t spin_limit() {
   return 1 << 21;
 }
 
+// qd / kd: per-tensor scales of Q and K whose codes are passed as q / k (the
+// FP8 backward); S folds both in, dQ and dK the other operand's.  check_only:
+// return after the argument checks, before any HIP call.
 gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                       void* dv, const int32_t* cu_q, const int32_t* cu_k, const Common& c, float scale,
                       float act_param, int32_t in_dtype, int32_t grad_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, float qd = 1.0f, float kd = 1.0f,
+                      bool check_only = false) {
   if (in_dtype == GDPA_DTYPE_FP8_E4M3) return GDPA_ERR_UNSUPPORTED;  // FP8 is forward-only
   if (in_dtype != GDPA_DTYPE_BF16 && in_dtype != GDPA_DTYPE_FP16) return GDPA_ERR_INVALID_ARG;
   if (!bwd_built(in_dtype == GDPA_DTYPE_FP16 ? gdpa::EL_F16 : gdpa::EL_BF16, c.d, c.dv)) return GDPA_ERR_UNSUPPORTED;
@@ -431,6 +435,7 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   const BwdLayout lay =
       bwd_layout(c.batch, jagged, c.max_lq, c.total_q, c.hq, c.d, bwd_acc16(out_kind != gdpa::OUT_F32, c.max_lk));
   if (workspace == nullptr || workspace_bytes < lay.bytes) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  if (check_only) return GDPA_OK;
 
   BwdArgs a{};
   a.q = q;
@@ -450,7 +455,11 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   a.group = c.hq / c.hkv;
   a.mblocks = (int32_t)mblocks;
   a.nblocks = (int32_t)nblocks;
-  a.act = make_act(c.act_kind, scale, act_param);
+  a.act = make_act(c.act_kind, (double)scale * qd * kd, act_param);
+  // dQ = scale dS K and dK = scale dS^T Q: with K (Q) given as codes of
+  // per-tensor scale kd (qd), each takes scale times that scale
+  a.dq_scale = (float)((double)scale * kd);
+  a.dk_scale = (float)((double)scale * qd);
   a.wl = c.wl;
   a.wr = c.wr;
   a.out_kind = out_kind;
@@ -696,6 +705,97 @@ size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32
   return bwd_layout(batch, true, max_seqlen_q, total_q, num_heads_q, head_dim,
                     bwd_acc16(grad_dtype != GDPA_DTYPE_FP32, max_seqlen_k))
       .bytes;
+}
+
+namespace {
+// Workspace of the backward from 8- or 4-bit Q/K: the 16-bit backward's, then
+// bf16 copies of Q and K; SIZE_MAX past kMaxWorkspace.
+struct LowpLayout {
+  size_t base, qdec, kdec, bytes;
+};
+LowpLayout lowp_layout(int32_t batch, int32_t max_lq, int32_t max_lk, int64_t total_q, int64_t total_k, int32_t hq,
+                       int32_t hkv, int32_t d, int32_t grad_dtype) {
+  LowpLayout l{};
+  l.base = gdpa_varlen_bwd_workspace_size(batch, max_lq, max_lk, total_q, hq, hkv, d, grad_dtype);
+  const __int128 qb = (__int128)std::max<int64_t>(total_q, 0) * hq * d * 2;
+  const __int128 kb = (__int128)std::max<int64_t>(total_k, 0) * hkv * d * 2;
+  if (l.base == SIZE_MAX || qb > kMaxWorkspace || kb > kMaxWorkspace) {
+    l.bytes = SIZE_MAX;
+    return l;
+  }
+  l.qdec = align256(l.base);
+  l.kdec = l.qdec + align256((size_t)qb);
+  l.bytes = l.kdec + align256((size_t)kb);
+  return l;
+}
+}  // namespace
+
+size_t gdpa_varlen_bwd_lowp_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                           int64_t total_q, int64_t total_k, int32_t num_heads_q,
+                                           int32_t num_heads_kv, int32_t head_dim, int32_t qk_dtype,
+                                           int32_t grad_dtype) {
+  (void)qk_dtype;
+  if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || num_heads_q <= 0 || num_heads_kv <= 0 ||
+      head_dim <= 0)
+    return 0;
+  return lowp_layout(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv, head_dim,
+                     grad_dtype)
+      .bytes;
+}
+
+gdpa_status_t gdpa_varlen_bwd_lowp(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                   const void* v, const void* dout, void* dq, void* dk, void* dv,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t total_q, int64_t total_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float scale,
+                                   int32_t mask, int32_t window_left, int32_t window_right, int32_t act,
+                                   float act_param, int32_t qk_dtype, float q_descale, float k_descale,
+                                   int32_t grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  Common c;
+  gdpa_status_t st = check_common(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                  head_dim, head_dim, scale, mask, window_left, window_right, act, act_param, &c);
+  if (st != GDPA_OK) return st;
+  int in_kind = -1;
+  if (qk_dtype == GDPA_DTYPE_FP8_E4M3) in_kind = gdpa::EL_FP8;
+  if (qk_dtype == GDPA_DTYPE_MXFP8_E4M3) in_kind = gdpa::EL_MX8;
+  if (qk_dtype == GDPA_DTYPE_MXFP4_E2M1) in_kind = gdpa::EL_MX4;
+  if (in_kind < 0) return GDPA_ERR_INVALID_ARG;
+  // the head dims the forward of the format is built for
+  if (!fwd_built(in_kind, c.d, c.dv) || c.d % 32 != 0) return GDPA_ERR_UNSUPPORTED;
+  const bool mx = in_kind != gdpa::EL_FP8;
+  // FP8 codes carry per-tensor scales, the MX formats block scales (and only they)
+  if (!mx && (q_scale != nullptr || k_scale != nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (!mx && (!std::isfinite(q_descale) || !std::isfinite(k_descale))) return GDPA_ERR_INVALID_ARG;
+  if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return GDPA_ERR_INVALID_ARG;
+  if (mx && batch > 0 && ((total_q > 0 && q_scale == nullptr) || (total_k > 0 && k_scale == nullptr)))
+    return GDPA_ERR_INVALID_ARG;
+  const LowpLayout lay = lowp_layout(batch, max_seqlen_q, max_seqlen_k, total_q, total_k, num_heads_q, num_heads_kv,
+                                     head_dim, grad_dtype);
+  const float qd = mx ? 1.0f : q_descale, kd = mx ? 1.0f : k_descale;
+  // every check of the 16-bit backward (q and k stand in for their decoded
+  // copies), then the workspace with the copies, before any launch
+  st = run_bwd(q, k, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, GDPA_DTYPE_BF16,
+               grad_dtype, workspace, lay.base, stream, qd, kd, /*check_only=*/true);
+  const bool work = batch > 0 && (total_q > 0 || total_k > 0);
+  if (st != GDPA_OK || !work) return st;
+  if (workspace == nullptr || lay.bytes == SIZE_MAX || workspace_bytes < lay.bytes)
+    return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const void* qdec = total_q > 0 ? ws + lay.qdec : nullptr;
+  const void* kdec = total_k > 0 ? ws + lay.kdec : nullptr;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = hip_status(gdpa::launch_decode_bf16(static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(q_scale),
+                                           reinterpret_cast<uint16_t*>(ws + lay.qdec), (long)total_q * num_heads_q,
+                                           head_dim, in_kind, hs),
+                  "q decode launch");
+  if (st != GDPA_OK) return st;
+  st = hip_status(gdpa::launch_decode_bf16(static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(k_scale),
+                                           reinterpret_cast<uint16_t*>(ws + lay.kdec), (long)total_k * num_heads_kv,
+                                           head_dim, in_kind, hs),
+                  "k decode launch");
+  if (st != GDPA_OK) return st;
+  return run_bwd(qdec, kdec, v, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, c, scale, act_param, GDPA_DTYPE_BF16,
+                 grad_dtype, workspace, lay.base, stream, qd, kd);
 }
 
 const char* gdpa_status_string(gdpa_status_t s) {

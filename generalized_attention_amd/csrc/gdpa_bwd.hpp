@@ -469,14 +469,14 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     if (wave_active) {
       uint8_t* sl = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
       const int nrows = min(32, lk - k0w);
-      TileStore<NDB>::store(dkacc, a.act.gscale, sl, a.dk, ((long)(ks + k0w) * a.hkv + g) * D, (long)a.hkv * D,
+      TileStore<NDB>::store(dkacc, a.dk_scale, sl, a.dk, ((long)(ks + k0w) * a.hkv + g) * D, (long)a.hkv * D,
                             nrows, a.out_kind, lane);
       TileStore<NDBV>::store(dvacc, a.act.pscale, sl, a.dv, ((long)(ks + k0w) * a.hkv + g) * DV, (long)a.hkv * DV,
                              nrows, a.out_kind, lane);
     }
   } else if (wave_active && kj < lk) {
     const long orow = ((long)(ks + kj) * a.hkv + g) * D, vrow = ((long)(ks + kj) * a.hkv + g) * DV;
-    const float gs = a.act.gscale, ps = a.act.pscale;
+    const float gs = a.dk_scale, ps = a.act.pscale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -811,7 +811,7 @@ __global__ __launch_bounds__(256, 1) void gdpa_bwd_fused_kernel(const BwdArgs a)
       auto finish_flush = [&]() __attribute__((always_inline)) {
         if (fl_idx < 0) return;
         if (dq_owner) {
-          const float gs = a.act.gscale;
+          const float gs = a.dq_scale;
           const bool out16 = a.out_kind != OUT_F32 && (fl_single || fl_last);
 #pragma unroll
           for (int j = 0; j < DQB; ++j) {
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void gdpa_bwd_fused_kernel(const BwdArgs a)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d = db * 32 + hf * 4 + 8 * i4;
-          const float gs = a.act.gscale, ps = a.act.pscale;
+          const float gs = a.dk_scale, ps = a.act.pscale;
           store4(a.dk, orow + d, dkacc[db][4 * i4] * gs, dkacc[db][4 * i4 + 1] * gs, dkacc[db][4 * i4 + 2] * gs,
                  dkacc[db][4 * i4 + 3] * gs, a.out_kind);
           store4(a.dv, orow + d, dvacc[db][4 * i4] * ps, dvacc[db][4 * i4 + 1] * ps, dvacc[db][4 * i4 + 2] * ps,
@@ -1185,7 +1185,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
   if constexpr (TileStore<NDB>::BYTES <= TB && TileStore<NDB>::BYTES <= TBV) {
     if (wave_active) {
       uint8_t* sl = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
-      TileStore<NDB>::store(dqacc, a.act.gscale, sl, a.dq, ((long)(qs + q0w) * a.hq + h) * D, (long)a.hq * D,
+      TileStore<NDB>::store(dqacc, a.dq_scale, sl, a.dq, ((long)(qs + q0w) * a.hq + h) * D, (long)a.hq * D,
                             min(32, lq - q0w), a.out_kind, lane);
     }
   } else if (wave_active && qi < lq) {
@@ -1195,7 +1195,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + hf * 4 + 8 * i4;
-        const float gs = a.act.gscale;
+        const float gs = a.dq_scale;
         store4(a.dq, orow + d, dqacc[db][4 * i4] * gs, dqacc[db][4 * i4 + 1] * gs, dqacc[db][4 * i4 + 2] * gs,
                dqacc[db][4 * i4 + 3] * gs, a.out_kind);
       }

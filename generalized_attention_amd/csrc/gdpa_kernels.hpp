@@ -101,6 +101,11 @@ struct BwdArgs {
   int32_t* qstate;      // per queue: next item [8], owning XCD + 1 [8]; then the error flag
   int32_t mt_fixed;     // fixed-length batches: 64-row query tiles per sequence
   int32_t spin_limit;   // polls before a turn wait gives up and sets the error flag
+  // factors of the dQ and dK stores: the chain-rule factor c (act.gscale),
+  // divided by the per-tensor scale that S folds in but the other operand
+  // of the product does not carry (FP8 Q/K codes; 1 otherwise)
+  float dq_scale;
+  float dk_scale;
 };
 
 // Forward workgroup: kFwdNW waves, each owning 32 query rows.
@@ -171,6 +176,12 @@ hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, 
 // Zeroes n int32 words at p (a kernel, not a memset, so the call stays
 // capturable in a graph).
 hipError_t launch_zero(int32_t* p, long n, hipStream_t stream);
+// Decodes rows of FP8 E4M3 codes (in_kind EL_FP8), MXFP8 (EL_MX8) or MXFP4
+// (EL_MX4, two elements per byte) with their E8M0 block scales (MX kinds) to
+// bf16: rows x d values (d a multiple of 32).  FP8 codes are written as their
+// E4M3 values (the per-tensor scale stays with the caller).
+hipError_t launch_decode_bf16(const uint8_t* src, const uint8_t* scales, uint16_t* dst, long rows, int d, int in_kind,
+                              hipStream_t stream);
 
 // Fused backward: queue state layout inside BwdArgs::qstate.
 constexpr int kQNext = 0, kQOwner = kNumXcd, kQErr = 2 * kNumXcd, kQWords = 2 * kNumXcd + 1;

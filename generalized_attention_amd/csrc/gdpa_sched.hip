@@ -1,4 +1,6 @@
-// Longest-first processing order of a jagged batch.
+// Longest-first processing order of a jagged batch, and the small utility
+// kernels around the main ones (workspace clearing, decoding of 8- and 4-bit
+// Q/K to bf16 for the backward).
 //
 // GDPA's jagged batches (the GDPA README's "Features": jagged sequences with
 // load-balanced scheduling) mix short and long sequences.  The kernels take
@@ -78,6 +80,72 @@ __global__ __launch_bounds__(256) void gdpa_zero_kernel(int32_t* p, long n) {
   i32x4* q = reinterpret_cast<i32x4*>(p + h);
   for (long i = t0; i < body; i += stride) q[i] = i32x4{0, 0, 0, 0};
   for (long i = h + 4 * body + t0; i < n; i += stride) p[i] = 0;
+}
+
+// E4M3 (OCP FP8: bias 7, 3 mantissa bits, S.1111.111 NaN, no infinities)
+// and E2M1 (OCP MX FP4: bias 1, 1 mantissa bit) codes to fp32, built from
+// the bit fields; every value is exact in fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, m = c & 0x7u;
+  if ((c & 0x7Fu) == 0x7Fu) return __builtin_bit_cast(float, 0x7FC00000u | sign);
+  if (e == 0) return __builtin_bit_cast(float, sign) + (sign ? -1.0f : 1.0f) * (float)m * 0x1p-9f;
+  return __builtin_bit_cast(float, sign | ((e + 120u) << 23) | (m << 20));
+}
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x8u) << 28, e = (c >> 1) & 0x3u, m = c & 0x1u;
+  if (e == 0) return m ? __builtin_bit_cast(float, sign | 0x3F000000u) : __builtin_bit_cast(float, sign);
+  return __builtin_bit_cast(float, sign | ((e + 126u) << 23) | (m << 22));
+}
+// fp32 -> bf16 bits, round to nearest even (the decoded values are exact in
+// bf16 unless a block scale takes them outside its normal range)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One thread per 8 consecutive elements of a row (one 16-byte bf16 store).
+__global__ __launch_bounds__(256) void gdpa_decode_kernel(const uint8_t* src, const uint8_t* scales, uint16_t* dst,
+                                                          long rows, int d, int in_kind) {
+  const long groups = rows * (long)(d / 8);
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < groups; t += stride) {
+    const long row = t / (d / 8);
+    const int c0 = (int)(t % (d / 8)) * 8;  // first element of the group
+    float v[8];
+    if (in_kind == EL_MX4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + row * (d / 2) + c0 / 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = e2m1_to_f32((w >> (4 * i)) & 0xFu);  // element 2i: low nibble
+    } else {
+      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+      const u32x2v w = *reinterpret_cast<const u32x2v*>(src + row * d + c0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = e4m3_to_f32((w[i / 4] >> (8 * (i % 4))) & 0xFFu);
+    }
+    if (in_kind != EL_FP8) {
+      const uint32_t sc = scales[row * (d / 32) + c0 / 32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = sc == 255u ? __builtin_nanf("") : __builtin_ldexpf(v[i], (int)sc - 127);
+    }
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4v*>(dst + row * d + c0) = out;
+  }
+}
+
+hipError_t launch_decode_bf16(const uint8_t* src, const uint8_t* scales, uint16_t* dst, long rows, int d, int in_kind,
+                              hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d <= 0 || d % 32 != 0 || (in_kind != EL_FP8 && in_kind != EL_MX8 && in_kind != EL_MX4)) return hipErrorInvalidValue;
+  long blocks = (rows * (d / 8) + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(gdpa_decode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, scales, dst, rows, d,
+                     in_kind);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(int32_t* p, long n, hipStream_t stream) {

@@ -202,8 +202,8 @@ gdpa_status_t gdpa_varlen_fwd_mxfp4(const void* q, const void* q_scale, const vo
 /* ----------------------------------------------------------------- backward
  * Gradients of L = sum(O .* dO) for the forward above.  in_dtype (q, k, v and
  * dout) is GDPA_DTYPE_BF16 or GDPA_DTYPE_FP16; P and dS are rounded to it for
- * the products (the README lists FP8 as forward-only, so an FP8 in_dtype
- * returns GDPA_ERR_UNSUPPORTED).  dq has q's layout, dk/dv have k's layout;
+ * the products (an FP8 in_dtype returns GDPA_ERR_UNSUPPORTED here: 8- and
+ * 4-bit Q/K take gdpa_varlen_bwd_lowp).  dq has q's layout, dk/dv have k's layout;
  * all three are written in grad_dtype (GDPA_DTYPE_FP32, GDPA_DTYPE_BF16 or
  * GDPA_DTYPE_FP16).  Head dims as in the forward: (64, 64), (96, 96),
  * (128, 128) or (192, 128) (dv then has v's 128 columns; dq and dk q's and
@@ -237,6 +237,41 @@ gdpa_status_t gdpa_varlen_bwd(const void* q, const void* k, const void* v, const
                               int32_t act, float act_param,
                               int32_t in_dtype, int32_t grad_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Jagged backward from 8- or 4-bit Q and K: the gradients of the forwards
+ * above with FP8 (gdpa_varlen_fwd with GDPA_DTYPE_FP8_E4M3 q/k), MXFP8
+ * (gdpa_varlen_fwd_mxfp8) or MXFP4 (gdpa_varlen_fwd_mxfp4) inputs.  The README
+ * lists FP8 as forward-only and "MXFP4 and MXFP8 forward & backward (coming
+ * soon)"; reading: the gradients of L = sum(O .* dO) with respect to the
+ * values the codes stand for (code x per-tensor descale for FP8, code x
+ * 2^(scale - 127) per block of 32 for the MX formats).
+ *   q, q_scale, k, k_scale : as in the forward of qk_dtype (GDPA_DTYPE_FP8_E4M3
+ *                    with q_scale = k_scale = NULL and the descales; the MX
+ *                    dtypes with their scale arrays, descales ignored)
+ *   v, dout        : bf16 [total_k, Hkv, D] and [total_q, Hq, D]
+ *   dq, dk, dv     : as in gdpa_varlen_bwd (dq, dk with D columns, in
+ *                    grad_dtype; NULL to skip as there)
+ *   head_dim       : D of Q, K, V and O; the head dims of the format's
+ *                    forward (FP8 64, 96, 128; MX 64, 128), else
+ *                    GDPA_ERR_UNSUPPORTED
+ * The codes are first decoded on the device into bf16 copies in the
+ * workspace (the values are exact in bf16: E4M3 and E2M1 values, times a
+ * power of two for the MX formats, unless a block scale takes them outside
+ * bf16's normal range), then the 16-bit backward runs on them with the FP8
+ * descales folded into the scalar factors of S, dQ and dK.  Workspace:
+ * gdpa_varlen_bwd_lowp_workspace_size (the 16-bit backward's plus the two
+ * copies).  Errors as in gdpa_varlen_bwd; every check runs before the first
+ * launch. */
+gdpa_status_t gdpa_varlen_bwd_lowp(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                                   const void* v, const void* dout, void* dq, void* dk, void* dv,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int64_t total_q, int64_t total_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   float scale, int32_t mask, int32_t window_left, int32_t window_right,
+                                   int32_t act, float act_param,
+                                   int32_t qk_dtype, float q_descale, float k_descale, int32_t grad_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Allocation-free jagged backward, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
@@ -293,6 +328,14 @@ size_t gdpa_bwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k
 size_t gdpa_varlen_bwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                       int64_t total_q, int32_t num_heads_q, int32_t num_heads_kv,
                                       int32_t head_dim, int32_t grad_dtype);
+/* gdpa_varlen_bwd_lowp: the 16-bit backward's workspace (as
+ * gdpa_varlen_bwd_workspace_size), then bf16 copies of Q and K
+ * (total_q * num_heads_q + total_k * num_heads_kv rows of head_dim values),
+ * each part rounded up to 256 bytes; SIZE_MAX past 2^60. */
+size_t gdpa_varlen_bwd_lowp_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                           int64_t total_q, int64_t total_k, int32_t num_heads_q,
+                                           int32_t num_heads_kv, int32_t head_dim, int32_t qk_dtype,
+                                           int32_t grad_dtype);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* gdpa_status_string(gdpa_status_t status);

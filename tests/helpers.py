@@ -100,10 +100,18 @@ def run_backward(g, bt: gi.Batch, dev=None, grad_dtype=None, poison=True):
     grad_dtype = grad_dtype or torch.float32
     fill = (lambda s: torch.full(s, float("nan"), dtype=grad_dtype, device="cuda")) if poison else \
         (lambda s: torch.empty(s, dtype=grad_dtype, device="cuda"))
-    dq, dk, dv = fill(bt.q.shape), fill(bt.k.shape), fill(bt.v.shape)
+    D = wl.head_dim
+    dq = fill((bt.q.shape[0], bt.q.shape[1], D))
+    dk, dv = fill((bt.k.shape[0], bt.k.shape[1], D)), fill(bt.v.shape)
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
               window_right=wl.window_right)
-    if wl.varlen:
+    if wl.fp8_qk or wl.mx_qk or wl.mx4_qk:
+        # 8- and 4-bit q/k: the jagged low-precision entry point
+        fmt = "mxfp4" if wl.mx4_qk else "mxfp8" if wl.mx_qk else "fp8"
+        g.gdpa_varlen_bwd_lowp(dev["q"], dev.get("q_mx"), dev["k"], dev.get("k_mx"), dev["v"], dev["do"], dq, dk, dv,
+                               dev["cu_q"], dev["cu_k"], bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, fmt,
+                               q_descale=bt.q_scale, k_descale=bt.k_scale, **kw)
+    elif wl.varlen:
         g.gdpa_varlen_bwd(dev["q"], dev["k"], dev["v"], dev["do"], dq, dk, dv, dev["cu_q"], dev["cu_k"],
                           bt.max_seqlen_q, bt.max_seqlen_k, wl.scale, **kw)
     else:

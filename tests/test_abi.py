@@ -171,6 +171,46 @@ def test_mx_forward_validation(lib, name, over, expect):
     assert varlen_fwd_mx(lib, name, **over) == expect
 
 
+def varlen_bwd_lowp(lib, **over):
+    a = dict(q=FAKE, qs=None, k=FAKE, ks=None, v=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cq=FAKE, ck=FAKE, B=2,
+             mq=128, mk=128, tq=200, tk=200, Hq=4, Hkv=2, D=128, scale=0.1, mask=0, wl=-1, wr=-1, act=8, ap=0.01,
+             qk=2, qd=1.0, kd=1.0, gd=3, ws=None, nws=0, stream=None)
+    a.update(over)
+    return lib.gdpa_varlen_bwd_lowp(*a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(), WS_SMALL),                      # FP8 needs the workspace (decoded copies)
+    (dict(qk=0), INVALID),                    # bf16 q/k take gdpa_varlen_bwd
+    (dict(qk=3), INVALID),
+    (dict(D=192), UNSUPPORTED),
+    (dict(D=96, qk=4, qs=FAKE, ks=FAKE), UNSUPPORTED),   # MX: head dims 64 and 128
+    (dict(qs=FAKE), INVALID),                 # FP8 has no block scales
+    (dict(qk=4), INVALID),                    # MX without its block scales
+    (dict(qk=5, qs=FAKE), INVALID),
+    (dict(qd=float("nan")), INVALID),
+    (dict(dk=None), INVALID),                 # dk and dv together
+    (dict(gd=2), INVALID),
+    (dict(cq=None), INVALID),
+    (dict(B=0), OK),
+    (dict(tq=0, tk=0), OK),
+    (dict(tq=257), INVALID),
+])
+def test_lowp_backward_validation(lib, over, expect):
+    assert varlen_bwd_lowp(lib, **over) == expect
+
+
+def test_lowp_backward_workspace(lib):
+    base = lib.gdpa_varlen_bwd_workspace_size(2, 128, 128, 200, 4, 2, 128, 3)
+    need = lib.gdpa_varlen_bwd_lowp_workspace_size(2, 128, 128, 200, 150, 4, 2, 128, 2, 3)
+    # the 16-bit backward's part, then bf16 Q (200 x 4 rows) and K (150 x 2 rows)
+    assert need == (base + 255) // 256 * 256 + 200 * 4 * 128 * 2 + (150 * 2 * 128 * 2 + 255) // 256 * 256
+    assert lib.gdpa_varlen_bwd_lowp(*[FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, 128,
+                                      200, 150, 4, 2, 128, 0.1, 0, -1, -1, 8, 0.01, 2, 1.0, 1.0, 3, FAKE, need - 1,
+                                      None]) == WS_SMALL
+    assert lib.gdpa_varlen_bwd_lowp_workspace_size(2, 2 ** 30, 128, 2 ** 43, 150, 1024, 2, 128, 2, 3) == 2 ** 64 - 1
+
+
 def test_mx_dtypes_need_their_entry_points(lib):
     # the MX dtypes through the plain entry point carry no scales
     assert varlen_fwd(lib, qk=4) == INVALID

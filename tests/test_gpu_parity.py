@@ -668,6 +668,46 @@ def test_mxfp4_unsupported_head_dim_and_missing_scales(g):
     assert e.value.status == 1
 
 
+# ------------------------------- backward from 8- and 4-bit Q/K (decoded to bf16)
+def _lowp(fmt):
+    return dict(fp8_qk=fmt == "fp8", mx_qk=fmt == "mxfp8", mx4_qk=fmt == "mxfp4")
+
+
+@pytest.mark.parametrize("fmt,D", [("fp8", 64), ("fp8", 96), ("fp8", 128), ("mxfp8", 64), ("mxfp8", 128),
+                                   ("mxfp4", 64), ("mxfp4", 128)])
+def test_lowp_backward(g, fmt, D):
+    # FP8 codes carry per-tensor descales (amax / 448, not 1: S, dQ and dK
+    # fold them in differently); MX codes block scales.  Jagged lengths with
+    # empty and one-token sequences over several key blocks (separate dQ)
+    lens = [300, 1, 0, 129, 64]
+    bt = gi.make_batch(_wl(head_dim=D, batch=len(lens), act="silu", **_lowp(fmt)), seqlens_q=lens, seqlens_k=lens)
+    if fmt == "fp8":
+        assert abs(bt.q_scale - 1) > 0.5 and abs(bt.k_scale - 1) > 0.5 and bt.q_scale != bt.k_scale
+    check_backward(g, bt)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_lowp_backward_masks_gqa(g, fmt, case):
+    mask, wl_, wr_, lq, lk = MASK_CASES[case]
+    wl = _wl(act="gelu_tanh", mask=mask, window_left=wl_, window_right=wr_, batch=len(lq), heads_q=8, heads_kv=2,
+             **_lowp(fmt))
+    check_backward(g, gi.make_batch(wl, seqlens_q=lq, seqlens_k=lk))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_lowp_backward_short_kv_and_bf16_gradients(g, fmt):
+    # 64 keys per sequence: dQ comes from the fused pass (written from the
+    # single key block), with its own dQ factor; then bf16 gradients
+    import torch
+    wl = dataclasses.replace(gi.WORKLOADS["short_kv_cross"], batch=4, act="relu2", **_lowp(fmt))
+    bt = gi.make_batch(wl)
+    check_backward(g, bt)
+    dq, dk, dv = [t.cpu().double().numpy() for t in run_backward(g, bt, grad_dtype=torch.bfloat16)]
+    errs = backward_ratios(bt, dq, dk, dv)
+    assert max(errs.values()) <= TOL_BWD, errs
+
+
 # ---------------------------------------- short key/value: hi/lo-split dS and P
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("act", ["silu", "fast_gelu", "gelu", "hardswish"])
