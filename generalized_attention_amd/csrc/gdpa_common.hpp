@@ -273,7 +273,10 @@ struct Act<ACT_HARDSWISH> {
   static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
     const float x = k.k0 * s;
     d = x < -3.0f ? 0.0f : (x > 3.0f ? 1.0f : __builtin_fmaf(x, 1.0f / 3.0f, 0.5f));
-    return s * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f);
+    // k0 s + 3 as one fused multiply-add, as in f: left to the compiler, the
+    // contraction of x + 3 depends on the surrounding code, and kernels that
+    // must agree bitwise (and the forward) would round P differently
+    return s * fminf(fmaxf(__builtin_fmaf(k.k0, s, 3.0f), 0.0f), 6.0f);
   }
 };
 
