@@ -41,6 +41,30 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
   }
   int n = 1;
   while (n < batch) n <<= 1;
+  if ((int)blockDim.x >= n) {
+    // up to 1024 sequences, one per thread: the same network with partners
+    // less than 64 apart exchanged across the lanes of a wave, and only the
+    // stages of wider partners through LDS (6 of 45 stages at 512 sequences)
+    const int i = threadIdx.x;
+    uint64_t x = i < batch ? make_key(i) : ~0ull;
+    for (int k = 2; k <= (int)blockDim.x; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint64_t y;
+        if (j >= 64) {
+          key[i] = x;
+          __syncthreads();
+          y = key[i ^ j];
+          __syncthreads();
+        } else {
+          y = __shfl_xor(x, j, 64);
+        }
+        const bool take_min = ((i & j) == 0) == ((i & k) == 0);
+        x = take_min ? (x < y ? x : y) : (x < y ? y : x);
+      }
+    }
+    if (i < batch) perm[i] = (int32_t)(uint32_t)x;
+    return;
+  }
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     if (i < batch) {
       key[i] = make_key(i);
@@ -160,12 +184,14 @@ hipError_t launch_zero(int32_t* p, long n, hipStream_t stream) {
 hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
                            hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
-  // up to 64 sequences sort in registers across one wave; larger batches in
-  // LDS, one compare-exchange per thread and stage
+  // up to 64 sequences sort in registers across one wave, up to 1024 with one
+  // sequence per thread (wide partners through LDS), larger batches in LDS
+  // with one compare-exchange per thread and stage
   int threads = 64;
   if (batch > 64) {
     threads = 128;
-    while (threads < 1024 && 2 * threads < batch) threads <<= 1;
+    while (threads < batch) threads <<= 1;
+    if (threads > 1024) threads = 1024;
   }
   hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(threads), 0, stream, cu_q, cu_k, batch, perm, counters);
   return hipGetLastError();
