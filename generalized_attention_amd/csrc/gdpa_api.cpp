@@ -291,9 +291,10 @@ int device_cu_count() {
 // Builds the schedule into the workspace when this is a jagged call that has
 // one; *perm and *counters stay nullptr otherwise (index order, one workgroup
 // per item).
-gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, int32_t batch, void* workspace,
+gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, const Common& c, void* workspace,
                              size_t workspace_bytes, void* stream, const int32_t** perm, int32_t** counters,
                              int32_t* ncu) {
+  const int32_t batch = c.batch;
   *perm = nullptr;
   *counters = nullptr;
   *ncu = 0;
@@ -304,7 +305,7 @@ gdpa_status_t build_schedule(const int32_t* cu_q, const int32_t* cu_k, int32_t b
   int32_t* p = static_cast<int32_t*>(workspace);
   int32_t* cnt = p + batch;
   const gdpa_status_t st = hip_status(
-      gdpa::launch_schedule(cu_q, cu_k, batch, p, cnt, static_cast<hipStream_t>(stream)), "schedule launch");
+      gdpa::launch_schedule(cu_q, cu_k, batch, c.wl, c.wr, p, cnt, static_cast<hipStream_t>(stream)), "schedule launch");
   if (st != GDPA_OK) return st;
   *perm = p;
   const int n = device_cu_count();
@@ -381,7 +382,7 @@ gdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, cons
   int32_t ncu = 0;
   gdpa_status_t sst = debug_check_jagged(cu_q, cu_k, c, stream);
   if (sst != GDPA_OK) return sst;
-  sst = build_schedule(cu_q, cu_k, c.batch, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
+  sst = build_schedule(cu_q, cu_k, c, workspace, workspace_bytes, stream, &a.perm, &counters, &ncu);
   if (sst != GDPA_OK) return sst;
   if (debug_log())
     std::fprintf(stderr, "[gdpa] fwd B=%d maxLq=%d maxLk=%d Hq=%d Hkv=%d D=%d act=%d in=%d wl=%d wr=%d psplit=%d grid=%lld\n",
@@ -492,8 +493,8 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (jagged && c.batch <= gdpa::kSortMax) {
     // longest-first order; also zeroes the first queue words
-    sst = hip_status(gdpa::launch_schedule(cu_q, cu_k, c.batch, reinterpret_cast<int32_t*>(ws + lay.order),
-                                           a.qstate, hs),
+    sst = hip_status(gdpa::launch_schedule(cu_q, cu_k, c.batch, c.wl, c.wr,
+                                           reinterpret_cast<int32_t*>(ws + lay.order), a.qstate, hs),
                      "schedule launch");
     if (sst != GDPA_OK) return sst;
     a.perm = reinterpret_cast<const int32_t*>(ws + lay.order);

@@ -495,11 +495,13 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
   };
 
   if (a.counters == nullptr) {
-    // Block -> work item: (sequence, KV head) pair on one XCD, longest
-    // sequences first; within a pair, key blocks run last-first.
+    // Block -> work item: (sequence, KV head) pair on one XCD, costliest
+    // sequences first; within a pair, key blocks run in ascending order: a
+    // bottom-right causal mask shows a key block to no more queries than the
+    // blocks before it, and without a mask a partial last block goes last.
     WorkItem w;
     if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
-    process(w.b, w.g, a.nblocks - 1 - w.rest, nullptr);
+    process(w.b, w.g, w.rest, nullptr);
   } else {
     // Per-XCD work queue over the same pairs, longest sequence first (one
     // workgroup per CU here, so the dispatcher's in-order hand-out of one
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
               [&](int j, QueueFetch& fetch) __attribute__((always_inline)) {
                 WorkItem w;
                 xcd_item(j, a.hkv, a.nblocks, a.perm, w);
-                return process(w.b, w.g, a.nblocks - 1 - w.rest, &fetch);
+                return process(w.b, w.g, w.rest, &fetch);
               });
   }
 }

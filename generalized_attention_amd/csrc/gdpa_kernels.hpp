@@ -121,7 +121,7 @@ constexpr int kNumXcd = 8;
 // items run there back to back: each K/V (or Q/dO) tile is fetched into that
 // L2 once and re-read there by the pair's other workgroups.  Pairs are taken
 // in rank order of perm (longest sequences first, when a schedule was built),
-// so every XCD works through its share longest-first and short items fill the
+// so every XCD works through its share costliest-first and short items fill the
 // tail.  The grid is the pair count rounded up to the XCD count, times per_pair.
 inline long pair_grid(long batch, long hkv, long per_pair) {
   const long pairs = ((long)batch * hkv + kNumXcd - 1) / kNumXcd * kNumXcd;
@@ -166,13 +166,46 @@ __device__ __forceinline__ void xcd_item(int j, int hkv, int per_pair, const int
 }
 
 // Longest-first schedule of a jagged batch: perm[r] is the sequence with the
-// r-th largest lq + lk (ties by index).  Built on the device by one workgroup
-// for batches of at most kSortMax sequences, which also zeroes kNumCounters
+// r-th largest cost, the number of 64 x 64 (query, key) blocks in which the
+// window (wl, wr) (-1 = unbounded side) leaves an allowed pair (ties by
+// larger lq + lk, then by index).  Built on the device by one workgroup for
+// batches of at most kSortMax sequences, which also zeroes kNumCounters
 // work-queue counters; larger batches keep index order.
 constexpr int kSortMax = 4096;
 constexpr int kNumCounters = kNumXcd;
-hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
-                           hipStream_t stream);
+
+// Blocks of 64 queries x 64 keys that hold at least one allowed pair of a
+// sequence with lq queries and lk keys under the window (wl, wr) (-1 =
+// unbounded side; bottom-right aligned: query i sees keys i + lk - lq - wl ..
+// i + lk - lq + wr).  Each 64-query tile's allowed keys form one interval,
+// the union of its rows' intervals, which shift by one key per row.
+__host__ __device__ inline int64_t mask_blocks(int lq, int lk, int wl, int wr) {
+  if (lq <= 0 || lk <= 0) return 0;
+  const int64_t mt = (lq + 63) / 64, nt = (lk + 63) / 64;
+  if (wl < 0 && wr < 0) return mt * nt;
+  const int64_t off = (int64_t)lk - lq;
+  int64_t n = 0;
+  for (int64_t t = 0; t < mt; ++t) {
+    const int64_t r0 = 64 * t, r1 = r0 + 63 < lq - 1 ? r0 + 63 : lq - 1;
+    const int64_t lo = wl < 0 ? 0 : (r0 + off - wl > 0 ? r0 + off - wl : 0);
+    const int64_t hi = wr < 0 ? lk - 1 : (r1 + off + wr < lk - 1 ? r1 + off + wr : lk - 1);
+    if (lo <= hi) n += hi / 64 - lo / 64 + 1;
+  }
+  return n;
+}
+// Sort key of sequence i: ascending keys run the larger cost first, then the
+// larger lq + lk, then the smaller index, which the low 12 bits hold.
+static_assert(kSortMax <= 4096, "the sort key keeps the sequence index in 12 bits");
+__host__ __device__ inline uint64_t schedule_key(int lq, int lk, int wl, int wr, int i) {
+  const int64_t cost = mask_blocks(lq, lk, wl, wr);
+  const int64_t len = (int64_t)lq + lk;
+  const uint64_t icost = (uint64_t)(0xffffffffLL - (cost < 0xffffffffLL ? cost : 0xffffffffLL));
+  const uint64_t ilen = (uint64_t)(0xfffffLL - (len < 0xfffffLL ? len : 0xfffffLL));
+  return (icost << 32) | (ilen << 12) | (uint64_t)(i & 0xfff);
+}
+__host__ __device__ inline int32_t schedule_key_index(uint64_t key) { return (int32_t)(key & 0xfffu); }
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int wl, int wr, int32_t* perm,
+                           int32_t* counters, hipStream_t stream);
 // Zeroes n int32 words at p (a kernel, not a memset, so the call stays
 // capturable in a graph).
 hipError_t launch_zero(int32_t* p, long n, hipStream_t stream);

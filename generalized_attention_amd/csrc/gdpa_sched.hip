@@ -5,10 +5,13 @@
 // GDPA's jagged batches (the GDPA README's "Features": jagged sequences with
 // load-balanced scheduling) mix short and long sequences.  The kernels take
 // (sequence, KV head) pairs in the order of a permutation; processing the
-// longest sequences first is the longest-processing-time rule, which keeps
-// long work items out of the tail of the launch.  One workgroup sorts the
-// keys (lq + lk, index) with a bitonic network in LDS; keys are unique, so
-// the order is deterministic.
+// costliest sequences first is the longest-processing-time rule, which keeps
+// long work items out of the tail of the launch.  A sequence's cost is the
+// number of 64 x 64 (query, key) blocks its mask leaves any allowed pair in:
+// every kernel's work per item is proportional to the blocks it visits, and a
+// causal or windowed sequence visits far fewer than its lengths suggest.  One
+// workgroup sorts the keys (cost, lq + lk, index) with a bitonic network;
+// keys are unique, so the order is deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,14 +20,10 @@
 namespace gdpa {
 
 __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q, const int32_t* cu_k, int batch,
-                                                             int32_t* perm, int32_t* counters) {
+                                                             int wl, int wr, int32_t* perm, int32_t* counters) {
   __shared__ uint64_t key[kSortMax];
   if (threadIdx.x < kNumCounters) counters[threadIdx.x] = 0;
-  auto make_key = [&](int i) {
-    const int64_t len = (int64_t)(cu_q[i + 1] - cu_q[i]) + (cu_k[i + 1] - cu_k[i]);
-    const uint64_t inv = (uint64_t)(0xffffffffLL - (len < 0xffffffffLL ? len : 0xffffffffLL));
-    return (inv << 32) | (uint32_t)i;  // ascending key = descending length, then index
-  };
+  auto make_key = [&](int i) { return schedule_key(cu_q[i + 1] - cu_q[i], cu_k[i + 1] - cu_k[i], wl, wr, i); };
   if (blockDim.x == 64) {
     // up to 64 sequences: the same network across the lanes of one wave
     const int i = threadIdx.x;
@@ -36,7 +35,7 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
         x = take_min ? (x < y ? x : y) : (x < y ? y : x);
       }
     }
-    if (i < batch) perm[i] = (int32_t)(uint32_t)x;
+    if (i < batch) perm[i] = schedule_key_index(x);
     return;
   }
   int n = 1;
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
         x = take_min ? (x < y ? x : y) : (x < y ? y : x);
       }
     }
-    if (i < batch) perm[i] = (int32_t)(uint32_t)x;
+    if (i < batch) perm[i] = schedule_key_index(x);
     return;
   }
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(1024) void gdpa_schedule_kernel(const int32_t* cu_q
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < batch; i += blockDim.x) perm[i] = (int32_t)(uint32_t)key[i];
+  for (int i = threadIdx.x; i < batch; i += blockDim.x) perm[i] = schedule_key_index(key[i]);
 }
 
 __global__ __launch_bounds__(256) void gdpa_zero_kernel(int32_t* p, long n) {
@@ -181,8 +180,8 @@ hipError_t launch_zero(int32_t* p, long n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int32_t* perm, int32_t* counters,
-                           hipStream_t stream) {
+hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int wl, int wr, int32_t* perm,
+                           int32_t* counters, hipStream_t stream) {
   if (batch <= 0 || batch > kSortMax) return hipErrorInvalidValue;
   // up to 64 sequences sort in registers across one wave, up to 1024 with one
   // sequence per thread (wide partners through LDS), larger batches in LDS
@@ -193,7 +192,8 @@ hipError_t launch_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, 
     while (threads < batch) threads <<= 1;
     if (threads > 1024) threads = 1024;
   }
-  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(threads), 0, stream, cu_q, cu_k, batch, perm, counters);
+  hipLaunchKernelGGL(gdpa_schedule_kernel, dim3(1), dim3(threads), 0, stream, cu_q, cu_k, batch, wl, wr, perm,
+                     counters);
   return hipGetLastError();
 }
 

@@ -444,6 +444,52 @@ def test_batch_sorted_in_lds(g):
     check_backward(g, bt)
 
 
+def _mask_blocks(lq, lk, mask, wl_, wr_):
+    # 64 x 64 blocks holding an allowed pair, counted from the oracle's mask
+    if lq == 0 or lk == 0:
+        return 0
+    ok = oracle.allowed_mask(lq, lk, mask, wl_, wr_)
+    mt, nt = -(-lq // 64), -(-lk // 64)
+    pad = np.zeros((mt * 64, nt * 64), dtype=bool)
+    pad[:lq, :lk] = ok
+    return int(pad.reshape(mt, 64, nt, 64).any(axis=(1, 3)).sum())
+
+
+@pytest.mark.parametrize("batch,maxlen", [(40, 400), (300, 300), (1500, 150)])
+@pytest.mark.parametrize("case", [("none", -1, -1), ("causal", -1, 0), ("window", 100, 0), ("window", 50, 30)])
+def test_schedule_orders_by_masked_blocks(g, batch, maxlen, case):
+    # the jagged schedule (one wave, one thread per sequence, and LDS sorts)
+    # orders sequences by the 64 x 64 blocks their mask leaves work in, then
+    # by lq + lk, then by index; the order sits in the first batch words of
+    # the forward's workspace
+    import torch
+    mask, wl_, wr_ = case
+    rng = np.random.default_rng(batch + 7 * wl_ + wr_)
+    lq = rng.integers(0, maxlen + 1, size=batch)
+    lk = rng.integers(0, maxlen + 1, size=batch)
+    dev = torch.device("cuda:0")
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32, device=dev)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32, device=dev)
+    tq, tk = int(lq.sum()), int(lk.sum())
+    q = torch.randn(tq, 1, 64, device=dev).to(torch.bfloat16)
+    k = torch.randn(tk, 1, 64, device=dev).to(torch.bfloat16)
+    v = torch.randn(tk, 1, 64, device=dev).to(torch.bfloat16)
+    o = torch.empty(tq, 1, 64, device=dev)
+    nws = g._lib.gdpa_varlen_fwd_workspace_size(batch, int(lq.max()), int(lk.max()), 1, 1, 64)
+    assert nws >= 4 * batch
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    st = g._lib.gdpa_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cu_q.data_ptr(),
+                                cu_k.data_ptr(), batch, int(lq.max()), int(lk.max()), tq, tk, 1, 1, 64, 64, 0.125,
+                                g._mask(mask), wl_, wr_, g._act("relu"), 0.0, g.DTYPE_BF16, g.DTYPE_BF16,
+                                g.DTYPE_FP32, 1.0, 1.0, ws.data_ptr(), nws, g._stream(dev))
+    assert st == 0, g._lib.gdpa_status_string(st)
+    torch.cuda.synchronize()
+    perm = ws[:4 * batch].cpu().view(torch.int32).numpy()
+    cost = [_mask_blocks(int(lq[i]), int(lk[i]), mask, wl_, wr_) for i in range(batch)]
+    want = sorted(range(batch), key=lambda i: (-cost[i], -(int(lq[i]) + int(lk[i])), i))
+    assert perm.tolist() == want
+
+
 # ------------------------------------------------------ autograd and call forms
 def _oracle_check(bt, o, grads, mask="none", wl_=-1, wr_=-1):
     wl = bt.wl
