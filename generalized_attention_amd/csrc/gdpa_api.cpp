@@ -154,8 +154,29 @@ gdpa::ActConsts make_act(int kind, double c, double alpha) {
       break;
     }
     case gdpa::ACT_RELU:
-    case gdpa::ACT_RELU2:
-    case gdpa::ACT_LEAKY: k.k0 = (float)c; break;
+      k.k0 = (float)c;
+      k.pscale = (float)c;
+      k.a0 = c >= 0 ? 0.0f : -INFINITY;
+      k.a1 = c >= 0 ? INFINITY : 0.0f;
+      break;
+    case gdpa::ACT_RELU2: k.k0 = (float)c; break;
+    case gdpa::ACT_LEAKY: {
+      // leaky(c s) = A max(s, 0) + B min(s, 0)
+      const double A = c > 0 ? c : alpha * c, B = c > 0 ? alpha * c : c;
+      k.k0 = (float)c;
+      if (std::fabs(A) >= std::fabs(B)) {  // y = s + (B/A - 1) min(s, 0)
+        k.pscale = (float)A;
+        k.k1 = A != 0 ? (float)(B / A - 1.0) : 0.0f;
+        k.a0 = -INFINITY;
+        k.a1 = 0.0f;
+      } else {  // y = s + (A/B - 1) max(s, 0)
+        k.pscale = (float)B;
+        k.k1 = (float)(A / B - 1.0);
+        k.a0 = 0.0f;
+        k.a1 = INFINITY;
+      }
+      break;
+    }
     case gdpa::ACT_SILU:
       k.k0 = (float)(-log2e * c);
       k.a0 = (float)c;

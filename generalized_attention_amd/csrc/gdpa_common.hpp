@@ -178,9 +178,15 @@ __host__ __device__ constexpr int lds_dim(int d) { return d == 96 ? 128 : d == 1
 //   GELU       y = s (1 + erf(k0 s))          pscale = c/2 d = (1 + erf(k0 s))/2 + a0 s 2^(a1 s^2)
 //   GELU_TANH  r = 1/(1 + 2^(s (k0 + k1 s^2))), y = s r, pscale = c,
 //              d = r + r (1 - r) s (a0 + a1 s^2)
-//   RELU       y = max(k0 s, 0)               pscale = 1   d = [k0 s > 0]
+//   RELU       y = med3(s, a0, a1)            pscale = c   d = [k0 s > 0]
+//              ((a0, a1) = (0, +inf) for c >= 0: y = max(s, 0); (-inf, 0) for
+//              c < 0: y = min(s, 0), since relu(c s) = c min(s, 0) there)
 //   RELU2      y = max(k0 s, 0)^2             pscale = 1   d = 2 max(k0 s, 0)
-//   LEAKY      x = k0 s, y = x >= 0 ? x : alpha x, pscale = 1, d = x > 0 ? 1 : alpha
+//   LEAKY      y = s + k1 med3(s, a0, a1)     pscale = p   d = k0 s > 0 ? 1 : alpha
+//              (leaky(c s) = A max(s, 0) + B min(s, 0) with (A, B) = (c, alpha c)
+//              for c > 0 and (alpha c, c) otherwise; p is the larger of A, B in
+//              magnitude and k1 = (the other) / p - 1 on min(s, 0) = med3(s, -inf, 0)
+//              or max(s, 0) = med3(s, 0, +inf), so |y| <= |s|; p = 0 when c = 0)
 //   SILU       r = 1/(1 + 2^(k0 s)), y = s r, pscale = c, d = r + r (1 - r) a0 s
 //   HARDSWISH  y = s clamp(k0 s + 3, 0, 6)    pscale = c/6 d = x < -3 ? 0 : x > 3 ? 1 : x/3 + 1/2 (x = k0 s)
 template <int ACT>
@@ -194,11 +200,12 @@ struct Act<ACT_IDENTITY> {
 
 template <>
 struct Act<ACT_RELU> {
-  static __device__ __forceinline__ float f(float s, const ActConsts& k) { return fmaxf(k.k0 * s, 0.0f); }
+  static __device__ __forceinline__ float f(float s, const ActConsts& k) {
+    return __builtin_amdgcn_fmed3f(s, k.a0, k.a1);
+  }
   static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
-    const float x = k.k0 * s;
-    d = x > 0.0f ? 1.0f : 0.0f;
-    return fmaxf(x, 0.0f);
+    d = k.k0 * s > 0.0f ? 1.0f : 0.0f;
+    return __builtin_amdgcn_fmed3f(s, k.a0, k.a1);
   }
 };
 
@@ -218,13 +225,11 @@ struct Act<ACT_RELU2> {
 template <>
 struct Act<ACT_LEAKY> {
   static __device__ __forceinline__ float f(float s, const ActConsts& k) {
-    const float x = k.k0 * s;
-    return x >= 0.0f ? x : k.alpha * x;
+    return __builtin_fmaf(k.k1, __builtin_amdgcn_fmed3f(s, k.a0, k.a1), s);
   }
   static __device__ __forceinline__ float f_df(float s, const ActConsts& k, float& d) {
-    const float x = k.k0 * s;
-    d = x > 0.0f ? 1.0f : k.alpha;
-    return x >= 0.0f ? x : k.alpha * x;
+    d = k.k0 * s > 0.0f ? 1.0f : k.alpha;
+    return __builtin_fmaf(k.k1, __builtin_amdgcn_fmed3f(s, k.a0, k.a1), s);
   }
 };
 
@@ -287,6 +292,20 @@ struct Act<ACT_HARDSWISH> {
 __device__ __forceinline__ bool in_range(int r, int lo, int hi) {
   const int c = 8 * (r >> 2) + (r & 3);
   return c >= lo && c <= hi;
+}
+// The same mask as a bit set, built once per block: bit c of range_bits(lo,
+// hi) is set iff lo <= c <= hi (c in 0..31).  keep_bits clears a masked
+// element with one sign-extending bit-field extract (0 or all ones) and one
+// AND of its bits, which leaves +0 where the element is masked.
+__device__ __forceinline__ uint32_t range_bits(int lo, int hi) {
+  const int l = min(max(lo, 0), 32), h = min(max(hi, -1), 31) + 1;  // bits [l, h)
+  const uint32_t below_h = h >= 32 ? ~0u : (1u << h) - 1u;
+  const uint32_t below_l = l >= 32 ? ~0u : (1u << l) - 1u;
+  return below_h & ~below_l;
+}
+__device__ __forceinline__ float keep_bits(float v, uint32_t bits, int r) {
+  const int c = 8 * (r >> 2) + (r & 3);
+  return __uint_as_float(__float_as_uint(v) & (uint32_t)__builtin_amdgcn_sbfe((int)bits, c, 1));
 }
 
 // ------------------------------------------------------------- global loads

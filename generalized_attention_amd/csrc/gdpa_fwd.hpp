@@ -81,14 +81,14 @@ struct FwdKernel {
 
   // One pair of accumulator elements (key rows 8t+2w, +1) -> packed P words.
   template <bool MASK>
-  static __device__ __forceinline__ void pair(const f32x16& s, int t, int w, int lo, int hi, u32x4 (*p)[2],
+  static __device__ __forceinline__ void pair(const f32x16& s, int t, int w, uint32_t mbits, u32x4 (*p)[2],
                                               const ActConsts& k) {
     float y[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int r = 8 * t + 2 * w + u;
       float v = Act<ACT>::f(s[r], k);
-      if constexpr (MASK) v = in_range(r, lo, hi) ? v : 0.0f;
+      if constexpr (MASK) v = keep_bits(v, mbits, r);
       y[u] = v;
     }
     const uint32_t h2 = pack2<EL>(y[0], y[1]);
@@ -144,6 +144,11 @@ struct FwdKernel {
                                                     const uint32_t* ksc = nullptr, uint32_t qsc = 0) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     u32x4 p[2][NP][2];
+    uint32_t mbits[2] = {0u, 0u};
+    if constexpr (MASK) {
+      mbits[0] = range_bits(mlo[0], mhi[0]);
+      mbits[1] = range_bits(mlo[1], mhi[1]);
+    }
     u32x4 ring[PREF + 1], ring_hi[PREF + 1];  // ring_hi: second 16 bytes of K = 64 FP8 units
 #pragma unroll
     for (int u = 0; u < PREF; ++u) ring[u] = load_unit(u, kb0, kl, vl, lo, vo, lane, ring_hi[u]);
@@ -189,7 +194,7 @@ struct FwdKernel {
         const int span = u < 2 * NA ? NA : NB;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (pair_at(q, v, span)) pair<MASK>(sacc[j], q >> 2, q & 3, mlo[j], mhi[j], p[j], k);
+          if (pair_at(q, v, span)) pair<MASK>(sacc[j], q >> 2, q & 3, mbits[j], p[j], k);
       }
     }
     __builtin_amdgcn_sched_barrier(0);

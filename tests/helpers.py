@@ -207,15 +207,15 @@ def kink_allowance(bt, q, k, v, do):
             g = h // group
             Q, K, V, dO = q[sq, h], k[sk, g], v[sk, g], do[sq, h]
             s = wl.scale * (Q @ K.T)
-            bound = 2.0 * wl.scale * gamma * (np.abs(Q) @ np.abs(K).T) + 2.0 * U32 * np.abs(s) + 1e-30
+            bound = 2.0 * abs(wl.scale) * gamma * (np.abs(Q) @ np.abs(K).T) + 2.0 * U32 * np.abs(s) + 1e-30
             near = np.zeros_like(s)
             for kink, jump in jumps:
                 near += np.where(np.abs(s - kink) <= bound, jump, 0.0)
             w = np.where(allowed, near * np.abs(dO @ V.T), 0.0)   # |jump * dP| per ambiguous pair
             if not w.any():
                 continue
-            aq[sq, h] += wl.scale * (w @ np.abs(K))
-            ak[sk, g] += wl.scale * (w.T @ np.abs(Q))
+            aq[sq, h] += abs(wl.scale) * (w @ np.abs(K))
+            ak[sk, g] += abs(wl.scale) * (w.T @ np.abs(Q))
     return aq, ak
 
 

@@ -101,6 +101,30 @@ def test_backward_every_activation(g, act, D):
     check_backward(g, bt)
 
 
+@dataclasses.dataclass(frozen=True)
+class _ScaledWorkload(gi.Workload):
+    scale_value: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return self.scale_value
+
+
+# the activations whose score scale the kernels fold into the output factor
+# (ReLU, LeakyReLU at slopes below, at and above 1, identity) and two that keep
+# it inside, at a negative and a zero scale, with a window mask
+@pytest.mark.parametrize("act,alpha", [("relu", 0.0), ("leaky_relu", 0.05), ("leaky_relu", 0.0),
+                                       ("leaky_relu", 2.5), ("leaky_relu", -0.5), ("identity", 0.0),
+                                       ("relu2", 0.0), ("gelu_tanh", 0.0)])
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_negative_and_zero_scale(g, act, alpha, scale):
+    base = dict(name="t", batch=3, heads_q=4, heads_kv=2, head_dim=64, lq_range=(1, 300), lk_range=None, act=act,
+                act_param=alpha, mask="window", window_left=70, window_right=5, backward=True, seed=13)
+    bt = gi.make_batch(_ScaledWorkload(**base, scale_value=scale), seqlens_q=[37, 130, 1], seqlens_k=[50, 130, 9])
+    check_forward(g, bt)
+    check_backward(g, bt)
+
+
 # ---------------------------------------------------------------------- masks
 MASK_CASES = [
     ("causal", -1, -1, [200, 77, 256], [200, 77, 256]),
