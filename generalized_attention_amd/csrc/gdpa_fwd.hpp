@@ -75,7 +75,9 @@ struct FwdKernel {
   static constexpr int NA = NARROW ? NK64 + NK16 : KS;  // S units per key block (1 MFMA each)
   static constexpr int NB = 2 * NDB;         // P V units per key block (NP MFMAs each)
   static constexpr int NU = 2 * NA + 2 * NB;
-  static constexpr int PREF = 2;             // units of operand prefetch
+  // units of operand prefetch (8- and 4-bit Q K^T: one MFMA per key block,
+  // so a deeper ring covers more of the LDS latency; measured 2 % faster)
+  static constexpr int PREF = NARROW ? 3 : 2;
   using KOffs = TileOffs<NARROW ? VROWB : KROWB>;  // row reads of 16-bit K (unused for 8- and 4-bit K)
   using VOffs = TileOffs<VROWB>;                 // transposed reads of V
 
@@ -158,9 +160,11 @@ struct FwdKernel {
       // the units with no activation work (S of block 0, P V of block 1) run
       // at raised priority, so the other wave on the SIMD fills the vector
       // ALU with its activation while these keep the matrix core busy
-      // (measured: 2-4 % shorter forwards at two waves per SIMD)
-      if (u == 0 || u == 2 * NA + NB) __builtin_amdgcn_s_setprio(3);
-      if (u == NA) __builtin_amdgcn_s_setprio(0);
+      // (measured: 2-4 % shorter 16-bit forwards at two waves per SIMD; the
+      // 8- and 4-bit forwards, at three waves per SIMD and one S MFMA per
+      // key block, ran 1-4 % faster without it)
+      if (!NARROW && (u == 0 || u == 2 * NA + NB)) __builtin_amdgcn_s_setprio(3);
+      if (!NARROW && u == NA) __builtin_amdgcn_s_setprio(0);
       if (u + PREF < NU)
         ring[(u + PREF) % (PREF + 1)] =
             load_unit(u + PREF, kb0, kl, vl, lo, vo, lane, ring_hi[(u + PREF) % (PREF + 1)]);
