@@ -197,7 +197,7 @@ gdpa_status_t hip_status(hipError_t e, const char* what) {
   return GDPA_ERR_HIP;
 }
 
-// Workspace of a jagged call: the longest-first sequence order (int32 per
+// Workspace of a jagged call: the costliest-first sequence order (int32 per
 // sequence) and the work-queue counters, built on the device before the main
 // kernels.  Batches beyond kSortMax keep index order and need no workspace.
 size_t schedule_bytes(int64_t batch) {
@@ -206,7 +206,7 @@ size_t schedule_bytes(int64_t batch) {
 }
 
 // Backward workspace, each part 256-byte aligned:
-//   order  int32 [batch]        longest-first sequence order (jagged calls of up
+//   order  int32 [batch]        costliest-first sequence order (jagged calls of up
 //                                to kSortMax sequences; index order otherwise)
 //   queues int32 [kQWords]      per-XCD queue heads and owners, then the flag a
 //                                dQ turn wait sets when it gives up
@@ -513,7 +513,7 @@ gdpa_status_t run_bwd(const void* q, const void* k, const void* v, const void* d
   if (sst != GDPA_OK) return sst;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (jagged && c.batch <= gdpa::kSortMax) {
-    // longest-first order; also zeroes the first queue words
+    // costliest-first order; also zeroes the first queue words
     sst = hip_status(gdpa::launch_schedule(cu_q, cu_k, c.batch, c.wl, c.wr,
                                            reinterpret_cast<int32_t*>(ws + lay.order), a.qstate, hs),
                      "schedule launch");

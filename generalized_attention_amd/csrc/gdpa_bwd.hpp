@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256, (dkdv_occupancy<D, ACT, SPLIT>())) void gdpa_b
     if (!map_work(blockIdx.x, a.batch, a.hkv, a.nblocks, a.perm, w)) return;
     process(w.b, w.g, w.rest, nullptr);
   } else {
-    // Per-XCD work queue over the same pairs, longest sequence first (one
+    // Per-XCD work queue over the same pairs, costliest sequence first (one
     // workgroup per CU here, so the dispatcher's in-order hand-out of one
     // item per workgroup would leave CUs idle between items).
     run_queue(a.counters + (blockIdx.x & (kNumXcd - 1)), xcd_items(a.batch, a.hkv, a.nblocks),
@@ -1205,7 +1205,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<D, ACT, SPLIT>())) void gdpa_bwd
   }
   };
 
-  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // Block -> work item: (sequence, KV head) pair on one XCD, costliest
   // sequences first; within a pair, query blocks run last-first.
   WorkItem w;
   if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;

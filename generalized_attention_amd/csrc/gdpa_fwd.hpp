@@ -24,7 +24,7 @@
 // Two 32-key blocks are issued as one interleaved stream so the activation
 // of one block runs on the vector ALU under the other block's MFMAs.
 // Work items are taken (sequence, KV head) pair by pair, each pair's blocks on
-// one XCD, longest sequences first, query blocks last-first (the README's
+// one XCD, costliest sequences first, query blocks last-first (the README's
 // "Features" names load-balanced tile scheduling for jagged inputs).
 #pragma once
 
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
   }
   };
 
-  // Block -> work item: (sequence, KV head) pair on one XCD, longest
+  // Block -> work item: (sequence, KV head) pair on one XCD, costliest
   // sequences first; within a pair, query blocks run last-first.
   WorkItem w;
   if (!map_work(blockIdx.x, a.batch, a.hkv, a.group * a.mblocks, a.perm, w)) return;

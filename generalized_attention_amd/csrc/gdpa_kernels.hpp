@@ -61,7 +61,7 @@ struct FwdArgs {
   int32_t wr;         // window right (-1: unbounded)
   int32_t out_kind;   // OUT_F32, OUT_BF16 or OUT_F16
   int32_t psplit;     // 1: P carried as a 16-bit hi/lo pair (two MFMAs for P V)
-  const int32_t* perm;  // sequences in processing order (longest first), or nullptr
+  const int32_t* perm;  // sequences in processing order (costliest first), or nullptr
   const uint8_t* q_mx;  // MXFP8: E8M0 scales of q [total_q, Hq, D / 32] (else nullptr)
   const uint8_t* k_mx;  //        and of k [total_k, Hkv, D / 32]
 };
@@ -91,7 +91,7 @@ struct BwdArgs {
   int32_t out_kind;   // OUT_F32, OUT_BF16 or OUT_F16 (dQ, dK, dV)
   int32_t dsplit;     // 1: dS carried as a 16-bit hi/lo pair in dQ = dS K
   int32_t kvsplit;    // 1: P and dS carried as 16-bit hi/lo pairs in dV, dK
-  const int32_t* perm;  // sequences in processing order (longest first), or nullptr
+  const int32_t* perm;  // sequences in processing order (costliest first), or nullptr
   int32_t* counters;    // per-XCD dK/dV work-queue counters (zeroed by the schedule), or nullptr
   int32_t ncu;          // compute units of the device (sizes the work-queue launches)
   // Fused backward (dQ accumulated inside the dK/dV kernel), all zeroed by
@@ -120,7 +120,7 @@ constexpr int kNumXcd = 8;
 // turn and each XCD has its own L2, so pair p goes to XCD p % 8 and all its
 // items run there back to back: each K/V (or Q/dO) tile is fetched into that
 // L2 once and re-read there by the pair's other workgroups.  Pairs are taken
-// in rank order of perm (longest sequences first, when a schedule was built),
+// in rank order of perm (costliest sequences first, when a schedule was built),
 // so every XCD works through its share costliest-first and short items fill the
 // tail.  The grid is the pair count rounded up to the XCD count, times per_pair.
 inline long pair_grid(long batch, long hkv, long per_pair) {
@@ -228,14 +228,14 @@ constexpr int kDqTile = 64;
 // KV head) pair with pair p on XCD p % 8 (L2 reuse of the pair's tiles), but
 // the workgroups of an XCD take the next item of that XCD's list from an
 // atomic counter instead of being handed one item each by the dispatcher.
-// The lists run longest sequence first, so a free workgroup always picks the
+// The lists run costliest sequence first, so a free workgroup always picks the
 // heaviest remaining item of its XCD (list scheduling).  The next index is
 // taken as the current item enters its last step (the body calls
 // fetch.issue() there; the counter's reply arrives while the step computes):
 // an index taken any earlier would reserve the heaviest remaining item for a
 // workgroup that stays busy for longer, while workgroups that free up in the
 // meantime take lighter ones, and the tail of the launch would lose the
-// longest-first order.  Workgroup ids are dealt to the XCDs in turn, so
+// costliest-first order.  Workgroup ids are dealt to the XCDs in turn, so
 // blockIdx % 8 names the XCD (only locality depends on that).
 struct QueueFetch {
   int32_t* counter;

@@ -302,7 +302,8 @@ gdpa_status_t gdpa_varlen_bwd_noalloc(const void* q, const void* k, const void* 
  * mirror the shape arguments of the matching entry point.
  * Forward: jagged calls of 1..4096 sequences need 4 bytes per sequence plus
  * 32, rounded up to 256: the call first builds there, on the device, the
- * order in which sequences are processed (longest first) and the counters of
+ * order in which sequences are processed (costliest first: the most 64 x 64
+ * (query, key) blocks holding a pair the mask allows) and the counters of
  * the work queues its kernels draw items from (see the README's load-balanced
  * scheduling of jagged batches).  Fixed-length calls and larger batches need
  * none.
