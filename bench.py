@@ -68,8 +68,8 @@ TOL_FP8 = 6e-2
 
 
 def pool_size():
-    """Host cores for the oracle leg: this process's CPU affinity, capped at the
-    16-core share a one-GPU machine gives its GPU."""
+    """Host cores for the oracle leg: this process's CPU affinity, capped at 16
+    (the host-core share of one GPU on an 8-GPU MI355X node)."""
     return max(1, min(len(os.sched_getaffinity(0)), 16))
 
 
