@@ -1,5 +1,6 @@
 """Full-size parity: the four large reference workloads at their real sizes (and
-the jagged one with fp16 inputs, with head dim 96 and with head dims (192, 128)), in
+the jagged one with fp16 inputs, with head dim 96 and with head dims (192, 128);
+the windowed one with FP8, MXFP8 and MXFP4 Q/K forward and backward), in
 the launch configuration the benchmark uses (same C entry points, same
 shapes).  Every output element is checked to have been written (outputs are
 NaN-poisoned before the call); sampled rows are recomputed one by one by the
@@ -31,7 +32,11 @@ def _decode16(bt, arr):
     return oracle.decode_f16(arr) if bt.wl.fp16 else oracle.decode_bf16(arr)
 
 
-def _decode_qk(bt, arr, scale):
+def _decode_qk(bt, arr, scale, blocks=None):
+    if bt.wl.mx4_qk:
+        return oracle.decode_mxfp4(arr, blocks)
+    if bt.wl.mx_qk:
+        return oracle.decode_mxfp8(arr, blocks)
     return oracle.decode_e4m3(arr, scale) if bt.wl.fp8_qk else _decode16(bt, arr)
 
 
@@ -39,8 +44,9 @@ def _seq(bt, b):
     """fp64 views of sequence b: q [Lq,Hq,D], k/v [Lk,Hkv,D], do [Lq,Hq,D] (or None)."""
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
     sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
-    q = _decode_qk(bt, bt.q[sq], bt.q_scale)
-    k = _decode_qk(bt, bt.k[sk], bt.k_scale)
+    mx = bt.wl.mx_qk or bt.wl.mx4_qk
+    q = _decode_qk(bt, bt.q[sq], bt.q_scale, bt.q_mx[sq] if mx else None)
+    k = _decode_qk(bt, bt.k[sk], bt.k_scale, bt.k_mx[sk] if mx else None)
     v = _decode16(bt, bt.v[sk])
     do = _decode16(bt, bt.do[sq]) if bt.do is not None else None
     return q, k, v, do
@@ -102,7 +108,7 @@ def _check_workload(g, wl, seed, n_rows, out_dtype=None):
         q, k, v, _ = _seq(bt, b)
         ref[r] = oracle.gdpa_forward_rows(q, k, v, [0, q.shape[0]], [0, k.shape[0]], wl.scale, wl.act,
                                           [(t - cq[b], h)], **_kw(wl))[0]
-    tol = TOL_FWD_FP8 if wl.fp8_qk else TOL_FWD_BF16
+    tol = TOL_FWD_FP8 if (wl.fp8_qk or wl.mx_qk or wl.mx4_qk) else TOL_FWD_BF16
     ratio = err_ratio(got, ref)
     print(f"[fullsize] {name}: forward err/rms {ratio:.3e} over {len(rows)} rows", flush=True)
     assert ratio <= tol
@@ -138,6 +144,19 @@ def _check_workload(g, wl, seed, n_rows, out_dtype=None):
     errs = dict(dq=err_ratio(got_q, ref_q), dk=err_ratio(got_k, ref_k), dv=err_ratio(got_v, ref_v))
     print(f"[fullsize] {name}: backward err/rms {errs}", flush=True)
     assert max(errs.values()) <= TOL_BWD, errs
+
+
+# The windowed GQA workload's real shape (16 sequences of 1024-4096 tokens,
+# Hq = 16, Hkv = 4, D = 64, LeakyReLU, causal window 512) with Q/K in each 8-
+# and 4-bit format, forward and backward (the backward through the
+# low-precision entry point)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
+def test_full_size_low_precision_formats(g, fmt):
+    import dataclasses
+    wl = dataclasses.replace(gi.WORKLOADS["window_gqa_fp8"], name=f"window_gqa_{fmt}", fp8_qk=fmt == "fp8",
+                             mx_qk=fmt == "mxfp8", mx4_qk=fmt == "mxfp4", backward=True)
+    _check_workload(g, wl, None, 48)
 
 
 @pytest.mark.timeout(600)
