@@ -120,9 +120,13 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None, workers=None):
     workers = workers or pool_size()
     pairs = workload_pairs(bt) // max(wl.heads_q, 1)  # per sequence and head
     DV = wl.head_dim_v or wl.head_dim
-    with_bwd = not wl.fp8_qk and bt.do is not None
+    with_bwd = bt.do is not None
     dec = oracle.decode_f16 if wl.fp16 else oracle.decode_bf16
-    if wl.fp8_qk:
+    if wl.mx4_qk:
+        q, k = oracle.decode_mxfp4(bt.q, bt.q_mx), oracle.decode_mxfp4(bt.k, bt.k_mx)
+    elif wl.mx_qk:
+        q, k = oracle.decode_mxfp8(bt.q, bt.q_mx), oracle.decode_mxfp8(bt.k, bt.k_mx)
+    elif wl.fp8_qk:
         q, k = oracle.decode_e4m3(bt.q, bt.q_scale), oracle.decode_e4m3(bt.k, bt.k_scale)
     else:
         q, k = dec(bt.q), dec(bt.k)
@@ -152,19 +156,31 @@ def cpu_baseline(bt: gi.Batch, budget_s: float, gpu=None, workers=None):
                 t_bwd += tb
             results += res
     _ORACLE_INPUTS.clear()
+    decoded = {"q": q, "k": k, "v": dec(bt.v), "do": dec(bt.do) if with_bwd else None}
     base = {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
             "sample": f"fp64 NumPy oracle, {'forward+backward' if with_bwd else 'forward'} of the first {nseq} "
                       f"of {wl.batch} sequences ({flops / 1e9:.1f} GFLOP algorithmic), one task per "
                       f"(sequence, head) on {workers} single-threaded processes: {wall:.1f} s wall "
                       f"(task time forward {t_fwd:.1f} s, backward {t_bwd:.1f} s)"}
-    return base, {"nseq": nseq, "results": results}
+    return base, {"nseq": nseq, "results": results, "decoded": decoded}
 
 
 def parity_record(bt: gi.Batch, sample, gpu):
     """max |gpu - oracle| / rms(oracle) per output over the oracle leg's
-    sequences (all elements); gpu holds host copies of o (and dq, dk, dv)."""
+    sequences (all elements); gpu holds host copies of o (and dq, dk, dv).
+    For activations whose derivative jumps (ReLU, LeakyReLU, HardSwish), dQ
+    and dK errors get the per-element allowance the GPU parity tests give
+    scores within rounding of a kink, where the kernel's fp32 score and the
+    oracle's fp64 score may fall on different sides."""
     wl = bt.wl
     cq, ck = bt.cu_seqlens_q, bt.cu_seqlens_k
+    allow = {}
+    if "dq" in gpu:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from helpers import kink_allowance, kink_jumps
+        if kink_jumps(wl.act, wl.act_param):
+            d = sample["decoded"]
+            allow["dq"], allow["dk"] = kink_allowance(bt, d["q"], d["k"], d["v"], d["do"])
     group = wl.heads_q // wl.heads_kv
     refs = {}
     for b, h, _, _, out in sample["results"]:
@@ -182,12 +198,17 @@ def parity_record(bt: gi.Batch, sample, gpu):
             rows = slice(cq[b], cq[b + 1]) if name in ("o", "dq") else slice(ck[b], ck[b + 1])
             got = gpu[name][rows, j].astype(np.float64)
             if ref.size:
-                mx = max(mx, float(np.abs(got - ref).max()))
+                err = np.abs(got - ref)
+                if name in allow:
+                    err = np.maximum(err - allow[name][rows, j], 0.0)
+                mx = max(mx, float(err.max()))
                 ss += float((ref * ref).sum())
                 n += ref.size
         err_rms[name] = mx / np.sqrt(ss / n) if n and ss > 0 else 0.0
-    tol = {n: (TOL_FP8 if wl.fp8_qk else t) for n, t in TOL.items()}
-    return {"sample": f"the first {sample['nseq']} of {wl.batch} sequences against the fp64 oracle, all elements",
+    # 8- and 4-bit Q/K: the forward's bar is the FP8 one; the gradients keep theirs
+    tol = {n: (TOL_FP8 if n == "o" and lowp_format(wl) else t) for n, t in TOL.items()}
+    return {"sample": f"the first {sample['nseq']} of {wl.batch} sequences against the fp64 oracle, all elements"
+                      + (" (dQ, dK: kink allowance)" if allow else ""),
             "err_rms": {n: float(f"{x:.3g}") for n, x in err_rms.items()},
             "tol": {n: tol[n] for n in err_rms},
             "pass": bool(all(err_rms[n] <= tol[n] for n in err_rms))}
@@ -254,6 +275,11 @@ def calibrate_copy(mib: int, reps: int):
                       "GBps_read_plus_write": 2 * n / ms / 1e6}))
 
 
+def lowp_format(wl):
+    """The 8- or 4-bit format of Q/K ("fp8", "mxfp8", "mxfp4"), or None."""
+    return "mxfp4" if wl.mx4_qk else "mxfp8" if wl.mx_qk else "fp8" if wl.fp8_qk else None
+
+
 def bwd_dq_path(max_seqlen_k):
     """The backward kernels a call takes (the library's default choice, or
     GDPA_BWD_DQ): dQ inside the dK/dV pass when every sequence's keys fit one
@@ -287,9 +313,11 @@ def main():
 
     wl = gi.WORKLOADS[args.workload]
     DV = wl.head_dim_v or wl.head_dim
-    # FP8 Q/K is a forward-only path (the README's FP8 support is inference);
-    # every other workload is timed forward + backward
-    with_bwd = not wl.fp8_qk
+    # 16-bit workloads are timed forward + backward; 8- and 4-bit Q/K ones
+    # forward + backward when the workload asks for it (the FP8 workload of the
+    # windowed shape is the README's inference case, forward only)
+    fmt = lowp_format(wl)
+    with_bwd = wl.backward or fmt is None
     if with_bwd and not wl.backward:
         wl = gi.dataclasses.replace(wl, backward=True)
     if not args.calibrate_copy:
@@ -321,18 +349,23 @@ def main():
     def dev(a, kind):
         t = torch.from_numpy(np.ascontiguousarray(a))
         views = {"bf16": torch.bfloat16, "fp16": torch.float16}
-        t = t.view(torch.int16).view(views[kind]) if kind in views else t.view(torch.float8_e4m3fn)
-        return t.cuda()
+        if kind in views:
+            t = t.view(torch.int16).view(views[kind])
+        elif kind == "fp8":
+            t = t.view(torch.float8_e4m3fn)
+        return t.cuda()  # "u8": bytes as they are (MXFP4 pairs, E8M0 scales)
 
     e16 = "fp16" if wl.fp16 else "bf16"
-    qk = "fp8" if wl.fp8_qk else e16
+    qk = {None: e16, "fp8": "fp8", "mxfp8": "fp8", "mxfp4": "u8"}[fmt]
     q, k, v = dev(bt.q, qk), dev(bt.k, qk), dev(bt.v, e16)
+    q_mx = dev(bt.q_mx, "u8") if fmt in ("mxfp8", "mxfp4") else None
+    k_mx = dev(bt.k_mx, "u8") if fmt in ("mxfp8", "mxfp4") else None
     do = dev(bt.do, e16) if with_bwd else None
     cu_q, cu_k = torch.from_numpy(bt.cu_seqlens_q).cuda(), torch.from_numpy(bt.cu_seqlens_k).cuda()
     odt = torch.float32 if args.out_dtype == "fp32" else torch.bfloat16
     o = torch.empty(q.shape[0], wl.heads_q, DV, dtype=odt, device="cuda")
-    dq = torch.empty(q.shape, dtype=odt, device="cuda")
-    dk = torch.empty(k.shape, dtype=odt, device="cuda")
+    dq = torch.empty(q.shape[0], wl.heads_q, D, dtype=odt, device="cuda")
+    dk = torch.empty(k.shape[0], wl.heads_kv, D, dtype=odt, device="cuda")
     dv = torch.empty(v.shape, dtype=odt, device="cuda")
     mq, mk = bt.max_seqlen_q, bt.max_seqlen_k
     kw = dict(act=wl.act, act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left,
@@ -340,12 +373,22 @@ def main():
     path = bwd_dq_path(mk) if with_bwd else None
 
     def fwd():
-        g.gdpa_varlen_fwd(q, k, v, o, cu_q, cu_k, mq, mk, wl.scale, q_descale=bt.q_scale, k_descale=bt.k_scale,
-                          **kw)
+        if fmt == "mxfp4":
+            g.gdpa_varlen_fwd_mxfp4(q, q_mx, k, k_mx, v, o, cu_q, cu_k, mq, mk, wl.scale, **kw)
+        elif fmt == "mxfp8":
+            g.gdpa_varlen_fwd_mxfp8(q, q_mx, k, k_mx, v, o, cu_q, cu_k, mq, mk, wl.scale, **kw)
+        else:
+            g.gdpa_varlen_fwd(q, k, v, o, cu_q, cu_k, mq, mk, wl.scale, q_descale=bt.q_scale,
+                              k_descale=bt.k_scale, **kw)
 
     def bwd(want_dq=True, want_dkv=True):
-        g.gdpa_varlen_bwd(q, k, v, do, dq if want_dq else None, dk if want_dkv else None,
-                          dv if want_dkv else None, cu_q, cu_k, mq, mk, wl.scale, **kw)
+        grads = (dq if want_dq else None, dk if want_dkv else None, dv if want_dkv else None)
+        if fmt is not None:
+            # decodes Q/K to bf16 in the workspace (inside the timing), then the 16-bit kernels
+            g.gdpa_varlen_bwd_lowp(q, q_mx, k, k_mx, v, do, *grads, cu_q, cu_k, mq, mk, wl.scale, fmt,
+                                   q_descale=bt.q_scale, k_descale=bt.k_scale, **kw)
+        else:
+            g.gdpa_varlen_bwd(q, k, v, do, *grads, cu_q, cu_k, mq, mk, wl.scale, **kw)
 
     def step():
         fwd()
@@ -409,7 +452,9 @@ def main():
     # recomputed S and dP are not counted) and the bytes each kernel must move
     # at least (every input read once, every output written once)
     osz = 4 if args.out_dtype == "fp32" else 2
-    isz = {"q": q.element_size(), "k": k.element_size(), "v": 2, "do": 2, "out": osz}
+    # bytes per Q/K element: 16-bit, FP8 codes, MX codes plus one E8M0 scale per 32
+    qk_b = {None: 2, "fp8": 1, "mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}[fmt]
+    isz = {"q": qk_b, "k": qk_b, "v": 2, "do": 2, "out": osz}
     tq, tk = q.shape[0], k.shape[0]
     nq, nkv = tq * wl.heads_q * D, tk * wl.heads_kv * D
     nqv, nkvv = tq * wl.heads_q * DV, tk * wl.heads_kv * DV  # V- and O-shaped tensors
@@ -467,11 +512,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f8" if wl.fp8_qk else e16,
+        "dtype": {None: e16, "fp8": "f8", "mxfp8": "mxfp8", "mxfp4": "mxfp4"}[fmt],
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.batch} sequences, lengths U[{wl.lq_range[0]},{wl.lq_range[1]}] "
                                f"(drawn total {int(bt.seqlens_q.sum())} tokens), Hq={wl.heads_q}, "
-                               f"Hkv={wl.heads_kv}, D={D}, act={wl.act}, mask={wl.mask}, "
+                               f"Hkv={wl.heads_kv}, D={D}, Q/K {fmt or e16}, act={wl.act}, mask={wl.mask}, "
                                f"{'fwd+bwd' if with_bwd else 'fwd'}, {args.out_dtype} outputs",
                    "global_batch": wl.batch, "seq_len": int(bt.max_seqlen_q), "parallelism": "none (1 GPU)"},
         "timing": ("ms_per_step is the median over the timed steps, each after a 512 MiB write outside the "

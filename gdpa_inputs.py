@@ -80,6 +80,21 @@ WORKLOADS = {
                                None, "leaky_relu", act_param=0.01,
                                mask="window", window_left=511, window_right=0,
                                fp8_qk=True, seed=5),
+    # the same shape with the 8- and 4-bit Q/K formats forward and backward
+    # (the README lists MXFP8 and MXFP4 forward and backward as coming; the
+    # backward from FP8 Q/K is read the same way)
+    "window_gqa_fp8_bwd": Workload("window_gqa_fp8_bwd", 16, 16, 4, 64, (1024, 4096),
+                                   None, "leaky_relu", act_param=0.01,
+                                   mask="window", window_left=511, window_right=0,
+                                   fp8_qk=True, backward=True, seed=5),
+    "window_gqa_mxfp8": Workload("window_gqa_mxfp8", 16, 16, 4, 64, (1024, 4096),
+                                 None, "leaky_relu", act_param=0.01,
+                                 mask="window", window_left=511, window_right=0,
+                                 mx_qk=True, backward=True, seed=5),
+    "window_gqa_mxfp4": Workload("window_gqa_mxfp4", 16, 16, 4, 64, (1024, 4096),
+                                 None, "leaky_relu", act_param=0.01,
+                                 mask="window", window_left=511, window_right=0,
+                                 mx4_qk=True, backward=True, seed=5),
 }
 
 

@@ -8,6 +8,7 @@ import pytest
 import bench
 import gdpa_inputs as gi
 import oracle
+from helpers import oracle_inputs
 
 
 @pytest.mark.parametrize("lq,lk,wl,wr", [(7, 7, -1, -1), (7, 7, -1, 0), (5, 9, -1, 0), (9, 5, -1, 0),
@@ -54,3 +55,40 @@ def test_cpu_baseline_pool_size_and_gqa_sums():
     assert base["unit"] == "TFLOP/s" and base["cores"] == 3
     assert bench.parity_record(bt, sample, out)["pass"]
     assert 1 <= bench.pool_size() <= 16
+
+
+def test_cpu_baseline_decodes_the_low_precision_formats():
+    # the oracle leg of the 8- and 4-bit workloads consumes the decoded codes
+    # (codes x per-tensor or block scale); the forward takes the FP8 bar, the
+    # gradients their own
+    for fmt in ("fp8", "mxfp8", "mxfp4"):
+        wl = dataclasses.replace(gi.WORKLOADS["tiny"], backward=True, fp8_qk=fmt == "fp8", mx_qk=fmt == "mxfp8",
+                                 mx4_qk=fmt == "mxfp4")
+        assert bench.lowp_format(wl) == fmt
+        bt = gi.make_batch(wl)
+        q, k, v, do = oracle_inputs(bt)
+        kw = dict(act_param=wl.act_param, mask=wl.mask, window_left=wl.window_left, window_right=wl.window_right)
+        cu = (bt.cu_seqlens_q, bt.cu_seqlens_k)
+        o = oracle.gdpa_forward(q, k, v, *cu, wl.scale, wl.act, **kw)
+        dq, dk, dv = oracle.gdpa_backward(q, k, v, do, *cu, wl.scale, wl.act, **kw)
+        out = {n: x.astype(np.float32) for n, x in dict(o=o, dq=dq, dk=dk, dv=dv).items()}
+        base, sample = bench.cpu_baseline(bt, 0.5, workers=2)
+        parity = bench.parity_record(bt, sample, out)
+        assert parity["pass"] and max(parity["err_rms"].values()) < 1e-6, (fmt, parity)
+        assert parity["tol"]["o"] == bench.TOL_FP8 and parity["tol"]["dq"] == bench.TOL["dq"]
+    assert bench.lowp_format(gi.WORKLOADS["jagged_self"]) is None
+
+
+def test_parity_record_kink_allowance_for_piecewise_linear_activations():
+    # LeakyReLU gradients: the record subtracts the tests' per-element kink
+    # allowance from dQ/dK errors (zero away from the kink, so oracle outputs
+    # still pass exactly and a gross error still fails)
+    wl = dataclasses.replace(gi.WORKLOADS["tiny"], act="leaky_relu", act_param=0.01, backward=True)
+    bt = gi.make_batch(wl)
+    out = _oracle_outputs(bt)
+    base, sample = bench.cpu_baseline(bt, 0.5, workers=2)
+    parity = bench.parity_record(bt, sample, out)
+    assert parity["pass"] and "kink allowance" in parity["sample"]
+    assert max(parity["err_rms"].values()) < 1e-6
+    out["dq"] = out["dq"] * 1.5
+    assert not bench.parity_record(bt, sample, out)["pass"]
