@@ -339,7 +339,10 @@ __device__ __forceinline__ int chunk_swz(int row) {
   if constexpr (ROWB >= 256) return ((row & 3) << 2) | ((row >> 2) & 3);
   else if constexpr (ROWB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   else if constexpr (ROWB == 64) return (row >> 2) & 3;
-  else return (row >> 2) & 1;  // 32-byte rows (MXFP4 K at head dim 64): two chunks
+  // 32-byte rows (MXFP4 K at head dim 64): two chunks; eight rows fill one
+  // 256-byte bank sweep, so rows r and r + 8 (read in the same 16-lane pass)
+  // take different chunks
+  else return (row >> 3) & 1;
 }
 template <int ROWB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {  // byte offset of a 16-byte chunk

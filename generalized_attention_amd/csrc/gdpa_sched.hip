@@ -127,14 +127,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// One thread per 8 consecutive elements of a row (one 16-byte bf16 store).
+// One thread per 8 consecutive elements of a row (one 16-byte bf16 store): a
+// block covers rpb = 256 / (d / 8) whole rows per pass, so each thread splits
+// its index into (row, column) once and the loop over rows has no division.
 __global__ __launch_bounds__(256) void gdpa_decode_kernel(const uint8_t* src, const uint8_t* scales, uint16_t* dst,
                                                           long rows, int d, int in_kind) {
-  const long groups = rows * (long)(d / 8);
-  const long stride = (long)gridDim.x * blockDim.x;
-  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < groups; t += stride) {
-    const long row = t / (d / 8);
-    const int c0 = (int)(t % (d / 8)) * 8;  // first element of the group
+  const int groups = d / 8, rpb = 256 / groups;
+  const int tr = (int)threadIdx.x / groups;
+  const int c0 = ((int)threadIdx.x - tr * groups) * 8;  // first element of the thread's group
+  if (tr >= rpb) return;                                // 256 % groups spare threads
+  for (long row = (long)blockIdx.x * rpb + tr; row < rows; row += (long)gridDim.x * rpb) {
     float v[8];
     if (in_kind == EL_MX4) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(src + row * (d / 2) + c0 / 2);
@@ -163,9 +165,12 @@ __global__ __launch_bounds__(256) void gdpa_decode_kernel(const uint8_t* src, co
 hipError_t launch_decode_bf16(const uint8_t* src, const uint8_t* scales, uint16_t* dst, long rows, int d, int in_kind,
                               hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (d <= 0 || d % 32 != 0 || (in_kind != EL_FP8 && in_kind != EL_MX8 && in_kind != EL_MX4)) return hipErrorInvalidValue;
-  long blocks = (rows * (d / 8) + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  // d / 8 groups of a row must fit one block of 256 threads
+  if (d <= 0 || d % 32 != 0 || d > 2048 || (in_kind != EL_FP8 && in_kind != EL_MX8 && in_kind != EL_MX4))
+    return hipErrorInvalidValue;
+  const long rpb = 256 / (d / 8);
+  long blocks = (rows + rpb - 1) / rpb;
+  if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(gdpa_decode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, scales, dst, rows, d,
                      in_kind);
   return hipGetLastError();
