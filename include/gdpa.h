@@ -33,9 +33,12 @@
  *    have the layouts of q/k/v.
  *    cu_seqlens_{q,k}: device int32 [B+1], cu[0] = 0, non-decreasing,
  *    cu[B] = total.  Zero-length sequences are allowed.
- *  - Element types: inputs bf16 or fp16 (or, forward only, FP8 E4M3 codes
- *    for q/k with fp32 per-tensor descales and bf16 v); outputs fp32, bf16
- *    or fp16 (fp32 is the mode whose accuracy the tests bound most tightly).
+ *  - Element types: inputs bf16 or fp16; or 8- and 4-bit q/k with bf16 v
+ *    (and dO): FP8 E4M3 codes with fp32 per-tensor descales (gdpa_fwd,
+ *    gdpa_varlen_fwd), MXFP8 or MXFP4 codes with E8M0 block scales
+ *    (gdpa_varlen_fwd_mxfp8, gdpa_varlen_fwd_mxfp4), and for the backward of
+ *    all three gdpa_varlen_bwd_lowp.  Outputs fp32, bf16 or fp16 (fp32 is the
+ *    mode whose accuracy the tests bound most tightly).
  *  - Outputs are overwritten, never accumulated into.  Query rows with no
  *    allowed key get O = 0 and dQ = 0; keys no query attends get dK = dV = 0.
  *    dK/dV are summed over the query heads of each KV group.
