@@ -92,3 +92,16 @@ def test_parity_record_kink_allowance_for_piecewise_linear_activations():
     assert max(parity["err_rms"].values()) < 1e-6
     out["dq"] = out["dq"] * 1.5
     assert not bench.parity_record(bt, sample, out)["pass"]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    # the path runs on one GPU; a multi-GPU request is refused before any
+    # GPU or oracle work, with exit status 2 and a message saying so
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2 and r.stdout == ""
+    assert "one GPU" in r.stderr or "1 GPU" in r.stderr, r.stderr
