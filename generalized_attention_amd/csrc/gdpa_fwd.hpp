@@ -309,10 +309,26 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
                                                    lk - n0, kl, wave, lane);
     stage_tile_buf<BN, K::VROWB, NW, DV / 8>(vrs, n0 * (int)v_ld * 2, (int)v_ld * 2, lk - n0, vl, wave, lane);
   };
+  // MX formats: the E8M0 scales of this lane's key in each 32-key block of a
+  // tile, loaded with the tile's copy (one tile ahead), so the wait before the
+  // tile's math covers them instead of a load inside it
+  constexpr int NKS = K::MX ? NKB : 1;
+  uint32_t ks_a[NKS], ks_b[NKS];
+  auto load_ks = [&](int nb, uint32_t* kss) __attribute__((always_inline)) {
+    if constexpr (K::MX) {
+      const int n0 = nb * BN;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int key = min(n0 + kb * 32 + (lane & 31), lk - 1);
+        kss[kb] = load_scales<D / 32>(a.k_mx + ((long)(ks + key) * a.hkv + g) * (D / 32));
+      }
+    }
+  };
   // One tile of math for this wave, two 32-key blocks at a time; the mask is
   // applied only where the window cuts a block (K and V rows past the last key
   // are staged as zeros and add nothing).
-  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl) __attribute__((always_inline)) {
+  auto compute = [&](int nb, const uint8_t* kl, const uint8_t* vl, const uint32_t* kss)
+                     __attribute__((always_inline)) {
     if (!wave_active) return;
     const int n0 = nb * BN;
 #pragma unroll
@@ -338,14 +354,11 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
         mhi[j] = jhi - (b_lo + hf * 4);
       }
       if (!any) continue;
-      // MXFP8: the E8M0 scales of this lane's key in each of the two blocks
+      // MX formats: the E8M0 scales of this lane's key in each of the two blocks
       uint32_t ksc[2] = {0u, 0u};
       if constexpr (K::MX) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int key = min(n0 + (kb0 + j) * 32 + (lane & 31), lk - 1);
-          ksc[j] = load_scales<D / 32>(a.k_mx + ((long)(ks + key) * a.hkv + g) * (D / 32));
-        }
+        ksc[0] = kss[kb0];
+        ksc[1] = kss[kb0 + 1];
       }
       if (all_full)
         K::template block_pair<false>(kl, vl, kb0, loffs, voffs, lane, qreg, qreg8, oacc, mlo, mhi, a.act, ksc, qsc);
@@ -354,17 +367,26 @@ __global__ __launch_bounds__(64 * NW) void gdpa_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  if (nb_begin < nb_end) stage(nb_begin, k_lds0, v_lds0);
+  if (nb_begin < nb_end) {
+    stage(nb_begin, k_lds0, v_lds0);
+    load_ks(nb_begin, ks_a);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): tile copy landed
   __syncthreads();
   for (int nb = nb_begin; nb < nb_end; nb += 2) {
-    if (nb + 1 < nb_end) stage(nb + 1, k_lds1, v_lds1);
-    compute(nb, k_lds0, v_lds0);
+    if (nb + 1 < nb_end) {
+      stage(nb + 1, k_lds1, v_lds1);
+      load_ks(nb + 1, ks_b);
+    }
+    compute(nb, k_lds0, v_lds0, ks_a);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (nb + 1 >= nb_end) break;
-    if (nb + 2 < nb_end) stage(nb + 2, k_lds0, v_lds0);
-    compute(nb + 1, k_lds1, v_lds1);
+    if (nb + 2 < nb_end) {
+      stage(nb + 2, k_lds0, v_lds0);
+      load_ks(nb + 2, ks_a);
+    }
+    compute(nb + 1, k_lds1, v_lds1, ks_b);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
